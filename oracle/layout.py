@@ -1,0 +1,116 @@
+"""Independent reader of the packed weight blob (test infrastructure only).
+
+Written from the blob specification (the "Packed blob layout" section of the
+library's public header), not from the packer's code.  It turns a blob back
+into the logical quantized form so that the packer can be checked by a round
+trip and the GEMV parity can start from what the device actually reads.
+
+Specification (all little-endian):
+  header, 256 bytes: u32 magic 0x51544942, u32 version 1, u32 format,
+      u32 N, u32 K, u32 P (planes), u32 group, u32 Np, u32 Kp, u32 reserved,
+      u64 off_planes, u64 off_c0, u64 off_c1, u64 total_bytes.
+  Np = N rounded up to 64 (row tile), Kp = K rounded up to 128 (k block).
+  planes section: 1024-byte tiles ordered [row tile t][k block b][plane p];
+      inside a tile, row r (= n - 64 t) owns 16 bytes = 4 uint32 words,
+      word w covering k = 128 b + 32 w .. +31 with bit i <-> k = 128b+32w+i.
+      Rows >= N and k >= K are zero bits.
+  coefficient sections by format:
+      1 sign    c0 = alpha  f32 [Np]
+      2 rabit   c0 = g      f16 [P][Np],  c1 = h f16 [P][Kp]
+      3 ternary c0 = gamma  f32 [1]          (plane 0: T=+1, plane 1: T=-1)
+      4 w2a8    c0 = dz     u32 [Np/64][Kp/128][64], low half = delta (f16),
+                high half = zero point (f16)  (plane i = bit i of q)
+      5 bvsr    c0 = idx    u8  [Np/64][Kp/128][64][4] (byte j = group 4b+j),
+                c1 = cache  f32 [256][5]      (plane k = bitvector beta_k)
+  Every section starts at a multiple of 256 bytes.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import bitserial
+
+MAGIC = 0x51544942
+HEADER_BYTES = 256
+ROW_TILE = 64
+K_BLOCK = 128
+FORMATS = {1: "sign", 2: "rabit", 3: "ternary", 4: "w2a8", 5: "bvsr"}
+
+
+def parse_header(blob: np.ndarray) -> dict:
+    b = np.ascontiguousarray(blob, dtype=np.uint8)
+    u32 = b[:40].view(np.uint32)
+    u64 = b[40:72].view(np.uint64)
+    h = dict(magic=int(u32[0]), version=int(u32[1]), fmt=int(u32[2]), N=int(u32[3]),
+             K=int(u32[4]), P=int(u32[5]), group=int(u32[6]), Np=int(u32[7]),
+             Kp=int(u32[8]), off_planes=int(u64[0]), off_c0=int(u64[1]),
+             off_c1=int(u64[2]), total=int(u64[3]))
+    if h["magic"] != MAGIC:
+        raise ValueError("bad magic")
+    return h
+
+
+def _section(b, off, nbytes, dtype):
+    return b[off:off + nbytes].view(dtype)
+
+
+def plane_bits(blob: np.ndarray, h: dict) -> np.ndarray:
+    """All plane bits as uint8 [P, Np, Kp]."""
+    b = np.ascontiguousarray(blob, dtype=np.uint8)
+    P, Np, Kp = h["P"], h["Np"], h["Kp"]
+    Tn, Tb = Np // ROW_TILE, Kp // K_BLOCK
+    words = _section(b, h["off_planes"], Tn * Tb * P * 1024, np.uint32)
+    words = words.reshape(Tn, Tb, P, ROW_TILE, 4)
+    words = words.transpose(2, 0, 3, 1, 4).reshape(P, Np, Kp // 32)
+    return bitserial.unpack_bits(words)
+
+
+def unpack(blob: np.ndarray) -> dict:
+    """Blob -> logical form (plus 'pad_ok': padded rows/columns are zero)."""
+    b = np.ascontiguousarray(blob, dtype=np.uint8)
+    h = parse_header(b)
+    fmt, N, K, P, Np, Kp = h["fmt"], h["N"], h["K"], h["P"], h["Np"], h["Kp"]
+    bits = plane_bits(b, h)
+    pad_ok = bool(bits[:, N:, :].sum() == 0 and bits[:, :, K:].sum() == 0)
+    bits = bits[:, :N, :K]
+    Tn, Tb = Np // ROW_TILE, Kp // K_BLOCK
+    out = dict(header=h, format=FORMATS[fmt])
+    if fmt == 1:
+        out["B"] = (2 * bits[0].astype(np.int8) - 1)
+        alpha = _section(b, h["off_c0"], 4 * Np, np.float32)
+        out["alpha"] = alpha[:N].copy()
+        pad_ok &= bool(np.all(alpha[N:] == 0))
+    elif fmt == 2:
+        out["B"] = (2 * bits.astype(np.int8) - 1)
+        g = _section(b, h["off_c0"], 2 * P * Np, np.float16).reshape(P, Np)
+        hh = _section(b, h["off_c1"], 2 * P * Kp, np.float16).reshape(P, Kp)
+        out["g"], out["h"] = g[:, :N].copy(), hh[:, :K].copy()
+        pad_ok &= bool(np.all(g[:, N:] == 0) and np.all(hh[:, K:] == 0))
+    elif fmt == 3:
+        plus, minus = bits[0].astype(np.int8), bits[1].astype(np.int8)
+        out["both_set"] = bool(np.any(plus & minus))
+        out["T"] = plus - minus
+        out["gamma"] = np.float32(_section(b, h["off_c0"], 4, np.float32)[0])
+    elif fmt == 4:
+        out["q"] = (bits[0] + 2 * bits[1]).astype(np.uint8)
+        dz = _section(b, h["off_c0"], 4 * Np * (Kp // K_BLOCK), np.uint32)
+        dz = dz.reshape(Tn, Tb, ROW_TILE).transpose(0, 2, 1).reshape(Np, Tb)
+        delta = (dz & 0xFFFF).astype(np.uint16).view(np.float16)
+        zero = (dz >> 16).astype(np.uint16).view(np.float16)
+        G = K // h["group"]
+        out["delta"], out["zero"] = delta[:N, :G].copy(), zero[:N, :G].copy()
+        pad_ok &= bool(np.all(dz[N:] == 0))
+    elif fmt == 5:
+        code = np.zeros((N, K), dtype=np.uint8)
+        for k in range(P):
+            code |= (bits[k] << k).astype(np.uint8)
+        out["code"] = code
+        idx = _section(b, h["off_c0"], Np * (Kp // 32), np.uint8)
+        idx = idx.reshape(Tn, Tb, ROW_TILE, 4).transpose(0, 2, 1, 3).reshape(Np, Kp // 32)
+        out["idx"] = idx[:N, :K // 32].copy()
+        out["cache"] = _section(b, h["off_c1"], 256 * 5 * 4, np.float32).reshape(256, 5).copy()
+        pad_ok &= bool(np.all(idx[N:] == 0) and np.all(idx[:, K // 32:] == 0))
+    else:
+        raise ValueError(f"unknown format {fmt}")
+    out["pad_ok"] = pad_ok
+    return out
