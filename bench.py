@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Benchmark of the bit-plane GEMV hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one batch-1 GEMV y = W^ x over one Llama-2-7B gate/up layer
+(11008 x 4096): the RaBiT 2-path residual-binary layer by default (the
+workload the headline metric is quoted on), or the W2A8 bit-plane layer
+(activation quantizer + AND+popcount GEMV) with --workload w2a8.
+
+Measurement:
+  * The packed layer is replicated into >= 1 GiB of distinct device copies and
+    step i reads copy i mod C, so every step streams its weights from HBM
+    (the 256 MB Infinity Cache and the L2s cannot hold the rotation).
+  * Inputs are resident in HBM before timing starts.  The K timed steps are
+    captured once into a HIP graph and replayed, so host launch overhead is
+    not part of the measurement; HIP events recorded on the launch stream
+    bracket the replay.
+  * value = packed weight bytes x K / elapsed (GB/s); roofline.achieved is the
+    same algorithmic byte count divided by the per-launch time of the GEMV
+    kernel measured the same way (equal to ms_per_step when the step is that
+    single kernel).
+  * cpu_baseline: the CPU oracle (explicit fp64 dequantization + dot product)
+    on the same layer, timed on the host for a bounded number of repetitions.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+ROTATE_BYTES = 1 << 30
+
+# Algorithmic packed bytes of one layer (planes + coefficients), by format.
+def packed_bytes(fmt: str, N: int, K: int) -> int:
+    if fmt == "rabit":
+        return 2 * N * K // 8 + 2 * 2 * N + 2 * 2 * K
+    if fmt == "w2a8":
+        return 2 * N * K // 8 + 4 * N * (K // 128)
+    if fmt == "ternary":
+        return 2 * N * K // 8 + 4
+    if fmt == "bvsr":
+        return 4 * N * K // 8 + N * K // 32 + 256 * 5 * 4
+    if fmt == "sign":
+        return N * K // 8 + 4 * N
+    raise ValueError(fmt)
+
+
+WORKLOADS = {
+    "rabit": dict(fmt="rabit", shape_idx=1, N=11008, K=4096),
+    "w2a8": dict(fmt="w2a8", shape_idx=1, N=11008, K=4096),
+    "rabit_down": dict(fmt="rabit", shape_idx=2, N=4096, K=11008),
+    "w2a8_down": dict(fmt="w2a8", shape_idx=2, N=4096, K=11008),
+    "bvsr": dict(fmt="bvsr", shape_idx=1, N=28672, K=8192),
+    "ternary": dict(fmt="ternary", shape_idx=3, N=4096, K=4096),
+}
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(wl: dict, budget_s: float = 12.0) -> dict:
+    """The oracle as it stands, timed on the host: explicit fp64 dequantization
+    and dot product for one GEMV of the workload layer, repeated until about
+    `budget_s` seconds of CPU work (at least once)."""
+    from oracle import act as oact, gemv as og, weights as ow
+    import synth
+    fmt, N, K, si = wl["fmt"], wl["N"], wl["K"], wl["shape_idx"]
+    W = synth.weights(fmt, si, N, K)
+    xs, xf = synth.activations(fmt, si, 1, K)
+    if fmt == "rabit":
+        # the GEMV step only: the logical form is built once, outside the timing
+        B, g, h = ow.quantize_rabit(W)
+        run = lambda: og.gemv_rabit(B, g, h, xf)
+        what = "oracle gemv_rabit (fp64 dequant + dot)"
+    elif fmt == "w2a8":
+        qw, delta, zero = ow.quantize_w2a8(W)
+        def run():
+            q, d = oact.quantize(xf)
+            return og.gemv_w2a8(qw, delta, zero, q, d)
+        what = "oracle act quantize + gemv_w2a8 (fp64 dequant + dot)"
+    else:
+        raise ValueError(fmt)
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    times = []
+    t_all = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        run()
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_all > budget_s or len(times) >= 50:
+            break
+    med = float(np.median(times))
+    return {"value": packed_bytes(fmt, N, K) / med / 1e9, "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{what}, {fmt} {N}x{K} M=1, {len(times)} runs, median {med * 1e3:.1f} ms "
+                      f"per GEMV; host has {os.cpu_count()} cpus"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default="rabit", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch every step from the host")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_plane_gemv_amd as bq
+    import synth
+
+    wl = WORKLOADS[args.workload]
+    fmt, N, K, si = wl["fmt"], wl["N"], wl["K"], wl["shape_idx"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- weights: library quantizer + packer (offline, untimed)
+    t0 = time.perf_counter()
+    W = synth.weights(fmt, si, N, K)
+    desc = bq.wdesc(fmt, N, K)
+    blob = bq.quantize_weights(desc, W)
+    log(f"quantized+packed {fmt} {N}x{K} in {time.perf_counter() - t0:.1f}s, blob {blob.nbytes} B")
+    alg_bytes = packed_bytes(fmt, N, K)
+    copies = max(2, math.ceil(ROTATE_BYTES / blob.nbytes))
+    base = torch.empty(blob.nbytes, dtype=torch.uint8, device=dev)
+    base.copy_(torch.from_numpy(blob))
+    stride = (blob.nbytes + 4095) // 4096 * 4096
+    pool = torch.empty(copies * stride, dtype=torch.uint8, device=dev)
+    for c in range(copies):
+        pool[c * stride:c * stride + blob.nbytes].copy_(base)
+    del base
+    blobs = [pool[c * stride:c * stride + blob.nbytes] for c in range(copies)]
+
+    # ---- activations / outputs / workspace
+    xs, xf = synth.activations(fmt, si, 1, K)
+    x = torch.from_numpy(np.ascontiguousarray(xs).view(np.int16)).to(dev)
+    y = torch.empty(N, dtype=torch.float32, device=dev)
+    ws = torch.zeros(bq.workspace_size(desc, 1), dtype=torch.uint8, device=dev)
+    integer = fmt in ("ternary", "w2a8", "bvsr")
+    act = torch.zeros(bq.act_size(1, K), dtype=torch.uint8, device=dev) if integer else None
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        w = blobs[i % copies]
+        if integer:
+            bq.quantize_act(x, bq.DT_BF16, 1, K, act, stream=stream)
+            bq.gemv(desc, w, act, bq.DT_ACT, y, ws, stream=stream)
+        else:
+            bq.gemv(desc, w, x, bq.DT_BF16, y, ws, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K_steps = args.steps
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(graph, stream=s):
+                stream = torch.cuda.current_stream()
+                for i in range(K_steps):
+                    step(i)
+        torch.cuda.current_stream().wait_stream(s)
+        stream = torch.cuda.current_stream()
+        graph.replay()                      # one untimed replay
+        torch.cuda.synchronize()
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    ev0.record(stream)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(K_steps):
+            step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / K_steps
+    value = alg_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # per-launch time of the GEMV kernel alone (integer workloads also run the
+    # activation quantizer in each step): a graph of GEMV launches only
+    gemv_ms = ms_per_step
+    if integer and graph is not None:
+        g2 = torch.cuda.CUDAGraph()
+        s2 = torch.cuda.Stream()
+        s2.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s2):
+            with torch.cuda.graph(g2, stream=s2):
+                st2 = torch.cuda.current_stream()
+                for i in range(K_steps):
+                    bq.gemv(desc, blobs[i % copies], act, bq.DT_ACT, y, ws, stream=st2)
+        torch.cuda.current_stream().wait_stream(s2)
+        g2.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(torch.cuda.current_stream())
+        g2.replay()
+        e1.record(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        gemv_ms = e0.elapsed_time(e1) / K_steps
+    achieved = alg_bytes / (gemv_ms * 1e-3) / 1e9
+
+    out = {
+        "metric": "packed-weight GB/s & % HBM peak, bit-plane GEMV 11008x4096 M=1; us/layer",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "us_per_layer": round(ms_per_step * 1e3, 3),
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if fmt in ("rabit", "sign") else "int32",
+        "data": "synthetic",
+        "config": {"workload": f"{fmt} {N}x{K} M=1 ({'RaBiT 2-path residual binary, bf16 x' if fmt == 'rabit' else fmt})",
+                   "N": N, "K": K, "M": 1, "format": fmt, "packed_bytes": alg_bytes,
+                   "rotating_copies": copies, "rotating_bytes": copies * stride,
+                   "graph_replay": graph is not None, "host_wall_s": round(wall, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "gemv_sign_kernel" if fmt in ("rabit", "sign") else "gemv_bits_kernel",
+                     "kernel_us": round(gemv_ms * 1e3, 3)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        try:
+            out["cpu_baseline"] = cpu_baseline(wl)
+        except Exception as e:  # reported, never fatal for the GPU figure
+            out["cpu_baseline"] = {"error": repr(e)}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

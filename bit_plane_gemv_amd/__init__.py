@@ -1,0 +1,227 @@
+"""Python binding of libbitq (argument marshalling only).
+
+Every function here forwards to the C ABI of the same name in
+bit_plane_gemv_amd/libbitq.so (declared in include/bitq.h); all computation
+happens in that library.  Device buffers are passed as torch tensors (their
+data_ptr()) or raw integer addresses; PyTorch is used only to own device
+memory and to name the current HIP stream.
+
+Importing this package fails loudly if libbitq.so has not been built
+(python -m bit_plane_gemv_amd.build); there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbitq.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libbitq.so not found at {LIB_PATH}; build it with "
+                      "`python -m bit_plane_gemv_amd.build`")
+
+# One HIP runtime per process: torch wheels bundle their own libamdhip64, and
+# loading libbitq.so first would bind it to the system runtime while torch
+# later loads a second one (device pointers and streams are then not shared).
+# Importing torch first makes libbitq.so bind to the runtime torch uses.
+try:
+    import torch as _torch  # noqa: F401
+except ImportError:
+    _torch = None
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+def _hip_runtimes() -> list:
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+    except OSError:
+        return []
+
+
+if len(_hip_runtimes()) > 1:
+    raise ImportError("two HIP runtimes are loaded in this process: " + ", ".join(_hip_runtimes()))
+
+# ------------------------------------------------------------------ enums
+OK, E_ARG, E_SHAPE, E_ALIGN, E_UNSUPPORTED, E_CAPACITY, E_DEVICE = 0, -1, -2, -3, -4, -5, -6
+SIGN1, RABIT, TERNARY, W2A8, BVSR4 = 1, 2, 3, 4, 5
+DT_F32, DT_BF16, DT_ACT = 0, 1, 2
+F_ACC_INT32 = 1
+
+FORMAT_NAMES = {SIGN1: "sign", RABIT: "rabit", TERNARY: "ternary", W2A8: "w2a8", BVSR4: "bvsr"}
+FORMATS = {v: k for k, v in FORMAT_NAMES.items()}
+DEFAULT_PLANES = {SIGN1: 1, RABIT: 2, TERNARY: 2, W2A8: 2, BVSR4: 4}
+DEFAULT_GROUP = {SIGN1: 0, RABIT: 0, TERNARY: 0, W2A8: 128, BVSR4: 32}
+
+
+class BitqError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"bitq status {status}: {message}")
+        self.status = status
+
+
+class WDesc(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
+                ("planes", ctypes.c_int32), ("group", ctypes.c_int32)]
+
+
+class Logical(ctypes.Structure):
+    _fields_ = [("sign", ctypes.c_void_p), ("tern", ctypes.c_void_p), ("code", ctypes.c_void_p),
+                ("alpha", ctypes.c_void_p), ("g", ctypes.c_void_p), ("h", ctypes.c_void_p),
+                ("gamma", ctypes.c_float), ("delta", ctypes.c_void_p), ("zero", ctypes.c_void_p),
+                ("idx", ctypes.c_void_p), ("cache", ctypes.c_void_p)]
+
+
+_P = ctypes.c_void_p
+_SZ = ctypes.c_size_t
+_I32 = ctypes.c_int32
+_U32 = ctypes.c_uint32
+_sigs = {
+    "bitq_version": ([], _I32),
+    "bitq_last_error": ([], ctypes.c_char_p),
+    "bitq_packed_size": ([ctypes.POINTER(WDesc), ctypes.POINTER(_SZ)], _I32),
+    "bitq_pack_weights": ([ctypes.POINTER(WDesc), ctypes.POINTER(Logical), _P, _SZ], _I32),
+    "bitq_quantize_weights": ([ctypes.POINTER(WDesc), _P, _P, _SZ, _I32], _I32),
+    "bitq_act_size": ([_I32, _I32, ctypes.POINTER(_SZ)], _I32),
+    "bitq_quantize_act": ([_P, _I32, _I32, _I32, _P, _SZ, _P], _I32),
+    "bitq_workspace_size": ([ctypes.POINTER(WDesc), _I32, ctypes.POINTER(_SZ)], _I32),
+    "bitq_gemv": ([ctypes.POINTER(WDesc), _P, _P, _I32, _P, _P, _SZ, _U32, _P], _I32),
+    "bitq_gemm_smallM": ([ctypes.POINTER(WDesc), _P, _P, _I32, _P, _P, _SZ, _U32, _P], _I32),
+}
+for _name, (_args, _ret) in _sigs.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = _ret
+
+EXPORTED = tuple(_sigs)
+
+
+def _check(status: int):
+    if status != OK:
+        raise BitqError(status, _lib.bitq_last_error().decode())
+
+
+def _ptr(x) -> int | None:
+    """Device/host address of a tensor, numpy array or raw int (None -> NULL)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    if isinstance(x, np.ndarray):
+        return x.ctypes.data
+    raise TypeError(f"cannot take the address of {type(x)}")
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if hasattr(stream, "cuda_stream"):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def wdesc(fmt, N: int, K: int, planes: int | None = None, group: int | None = None) -> WDesc:
+    if isinstance(fmt, str):
+        fmt = FORMATS[fmt]
+    return WDesc(fmt, N, K, DEFAULT_PLANES[fmt] if planes is None else planes,
+                 DEFAULT_GROUP[fmt] if group is None else group)
+
+
+# -------------------------------------------------------------- host calls
+def version() -> int:
+    return _lib.bitq_version()
+
+
+def last_error() -> str:
+    return _lib.bitq_last_error().decode()
+
+
+def packed_size(desc: WDesc) -> int:
+    n = _SZ(0)
+    _check(_lib.bitq_packed_size(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def pack_weights(desc: WDesc, **fields) -> np.ndarray:
+    """Pack a logical form (numpy arrays named as in bitq_logical) into a blob."""
+    keep = []
+    lg = Logical()
+    conv = {"sign": np.int8, "tern": np.int8, "code": np.uint8, "alpha": np.float32,
+            "g": np.uint16, "h": np.uint16, "delta": np.uint16, "zero": np.uint16,
+            "idx": np.uint8, "cache": np.float32}
+    for name, val in fields.items():
+        if name == "gamma":
+            lg.gamma = float(val)
+            continue
+        arr = np.asarray(val)
+        if arr.dtype == np.float16:
+            arr = arr.view(np.uint16)
+        arr = np.ascontiguousarray(arr, dtype=conv[name])
+        keep.append(arr)
+        setattr(lg, name, arr.ctypes.data)
+    blob = np.zeros(packed_size(desc), dtype=np.uint8)
+    _check(_lib.bitq_pack_weights(ctypes.byref(desc), ctypes.byref(lg), blob.ctypes.data, blob.nbytes))
+    return blob
+
+
+def quantize_weights(desc: WDesc, W: np.ndarray, nthreads: int = 0) -> np.ndarray:
+    """fp32 W [N, K] -> packed blob with the library's own offline quantizer."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    if W.shape != (desc.N, desc.K):
+        raise ValueError(f"W has shape {W.shape}, descriptor says {(desc.N, desc.K)}")
+    blob = np.zeros(packed_size(desc), dtype=np.uint8)
+    _check(_lib.bitq_quantize_weights(ctypes.byref(desc), W.ctypes.data, blob.ctypes.data,
+                                      blob.nbytes, nthreads))
+    return blob
+
+
+def act_size(M: int, K: int) -> int:
+    n = _SZ(0)
+    _check(_lib.bitq_act_size(M, K, ctypes.byref(n)))
+    return n.value
+
+
+def workspace_size(desc: WDesc, M: int = 1) -> int:
+    n = _SZ(0)
+    _check(_lib.bitq_workspace_size(ctypes.byref(desc), M, ctypes.byref(n)))
+    return n.value
+
+
+# ------------------------------------------------------------ device calls
+def quantize_act(x, x_dtype: int, M: int, K: int, act, act_bytes: int | None = None, stream=None):
+    nbytes = act.numel() * act.element_size() if act_bytes is None else act_bytes
+    _check(_lib.bitq_quantize_act(_ptr(x), x_dtype, M, K, _ptr(act), nbytes, _stream(stream)))
+
+
+def gemv(desc: WDesc, w, x, x_dtype: int, y, ws, ws_bytes: int | None = None, flags: int = 0,
+         stream=None):
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check(_lib.bitq_gemv(ctypes.byref(desc), _ptr(w), _ptr(x), x_dtype, _ptr(y), _ptr(ws),
+                          nbytes, flags, _stream(stream)))
+
+
+def gemm_smallM(desc: WDesc, w, act, M: int, y, ws, ws_bytes: int | None = None, flags: int = 0,
+                stream=None):
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check(_lib.bitq_gemm_smallM(ctypes.byref(desc), _ptr(w), _ptr(act), M, _ptr(y), _ptr(ws),
+                                 nbytes, flags, _stream(stream)))
+
+
+def act_layout(M: int, K: int) -> dict:
+    """Section offsets of an activation buffer (mirrors bitq_act_size)."""
+    Kp = (K + 127) // 128 * 128
+    Kw = Kp // 32
+
+    def a256(v):
+        return (v + 255) // 256 * 256
+    off_S = a256(M * Kw * 32)
+    off_q = a256(off_S + M * Kw * 4)
+    off_d = a256(off_q + M * Kp)
+    return dict(Kp=Kp, Kw=Kw, off_planes=0, off_S=off_S, off_q=off_q, off_d=off_d,
+                total=a256(off_d + 4 * M))

@@ -1,0 +1,62 @@
+// Internal declarations shared by the host side (bitq_host.cpp) and the HIP
+// kernels (bitq_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/bitq.h"
+
+namespace bitq {
+
+constexpr int kRowTile = 64;      // rows per tile = lanes per wave
+constexpr int kKBlock = 128;      // inputs per k block = 4 words per row
+constexpr int kHeaderBytes = 256;
+constexpr uint32_t kMagic = 0x51544942u;
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Byte layout of a packed blob (see include/bitq.h, "Packed blob layout").
+struct BlobLayout {
+    int64_t Np, Kp, P, Tn, Tb;
+    size_t off_planes, planes_bytes;
+    size_t off_c0, c0_bytes;
+    size_t off_c1, c1_bytes;
+    size_t total;
+};
+BlobLayout blob_layout(const bitq_wdesc& d);
+
+// Byte layout of an activation buffer (see bitq_quantize_act).
+struct ActLayout {
+    int64_t M, K, Kp, Kw;
+    size_t off_planes, off_S, off_q, off_d, total;
+};
+ActLayout act_layout(int M, int K);
+
+// How a GEMV/GEMM call is split over workgroups, and its workspace.
+struct Plan {
+    int waves_per_wg;      // 64-row waves per workgroup
+    int rows_per_wg;       // 64 * waves_per_wg
+    int row_groups;        // ceil(Np / rows_per_wg)
+    int blocks_per_split;  // k blocks (128 inputs) per workgroup
+    int splits;            // ceil((Kp/128) / blocks_per_split)
+    int M;
+    size_t off_partials;   // f32 [splits][M][Np]
+    size_t off_counters;   // u32 [row_groups]
+    size_t ws_bytes;
+};
+Plan make_plan(const bitq_wdesc& d, int M);
+
+// Kernel launchers (bitq_kernels.hip).  Arguments are already validated.
+// Each returns hipSuccess or the HIP error code of the launch.
+int launch_quantize_act(const void* x, int x_dtype, int M, int K, void* act, void* stream);
+int launch_gemv_float(const bitq_wdesc& d, const Plan& plan, const void* w, const void* x,
+                      int x_dtype, float* y, void* ws, void* stream);
+int launch_gemv_int(const bitq_wdesc& d, const Plan& plan, const void* w, const void* act,
+                    int M, float* y, void* ws, uint32_t flags, void* stream);
+
+// Device checks (bitq_kernels.hip): is the current device a gfx950?
+int current_device_is_gfx950(int* is_gfx950);
+
+}  // namespace bitq

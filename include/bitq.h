@@ -1,0 +1,268 @@
+/*
+ * bitq.h -- C ABI of libbitq: decode-time linear layers y = W x on AMD MI355X
+ * (gfx950) with W stored as packed binary bit-planes and small float
+ * coefficients.
+ *
+ * Sources (cited below by the short name in brackets):
+ *   [RaBiT]  "RaBiT框架：突破2比特量化性能瓶颈的LLM部署方案"
+ *            (2-path residual binarization W^ = g1.B1.h1 + g2.B2.h2)
+ *   [HGF]    "1.58位LLM混合门控流优化技术解析"
+ *            (ternary weights with absmean gamma, int8 activations)
+ *   [ABQ]    "ABQ-LLM：用于大語言模型的任意比特量化推理加速"
+ *            (arbitrary-bit weight/activation planes, binary-TensorCore-
+ *             equivalent integer GEMV)
+ *   [BVSR]   "BVSR：面向分布感知的大语言模型权重量化的比特向量求和表示"
+ *            (bitvector-sum representation, AND+popcount GEMV)
+ *   [BitNet] "1-bit LLM的端侧推理革命" (sign() binarization, scale alpha,
+ *            XNOR+popcount, the weight-parameter struct of §3.2)
+ *
+ * Conventions for every entry point
+ *   - Shapes: W is [N, K] (N outputs, K inputs); activations are [M, K]
+ *     row-major; outputs y are [M, N] row-major fp32.
+ *   - Ownership: the caller owns every buffer.  The library allocates no
+ *     memory (host or device) and keeps no state between calls other than a
+ *     per-thread error string and a per-device "is gfx950" check.
+ *   - Validation: every argument is checked before anything is enqueued or
+ *     written.  On error nothing is written, a negative bitq_status is
+ *     returned and bitq_last_error() describes it.  No C++ exception crosses
+ *     the ABI; the library never aborts or exits.
+ *   - Device calls are asynchronous on the given stream (a hipStream_t passed
+ *     as void*, NULL = the null stream) and never synchronize.  A launch
+ *     failure reported by the HIP runtime maps to BITQ_E_DEVICE.
+ *   - Device pointers must satisfy the alignments stated per call
+ *     (BITQ_E_ALIGN otherwise); host pointers need natural alignment only.
+ */
+#ifndef BITQ_H
+#define BITQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BITQ_VERSION 1
+
+typedef enum {
+    BITQ_OK = 0,
+    BITQ_E_ARG = -1,          /* null pointer, bad enum, bad value in a logical form */
+    BITQ_E_SHAPE = -2,        /* N, K, M or planes/group out of range or misaligned */
+    BITQ_E_ALIGN = -3,        /* device pointer alignment */
+    BITQ_E_UNSUPPORTED = -4,  /* format/flag combination not implemented, non-gfx950 device */
+    BITQ_E_CAPACITY = -5,     /* destination or workspace smaller than required */
+    BITQ_E_DEVICE = -6        /* error reported by the HIP runtime */
+} bitq_status;
+
+/* Weight formats. */
+typedef enum {
+    BITQ_SIGN1 = 1,    /* [BitNet] §2.1-2.2: W^ = alpha_n * B, B = sign(W) in {-1,+1},
+                          one fp32 alpha per output row. planes = 1, group = 0. */
+    BITQ_RABIT = 2,    /* [RaBiT] §2.1-2.2: W^ = sum_p g_p (.) B_p (.) h_p with B_p in
+                          {-1,+1}, g_p fp16 per row, h_p fp16 per column.
+                          planes = number of paths (1..3), group = 0. */
+    BITQ_TERNARY = 3,  /* [HGF] §1.2: W^ = gamma * T, T in {-1,0,1} stored as a
+                          plus plane and a minus plane (2 bits/weight), one fp32
+                          gamma per tensor. planes = 2, group = 0. */
+    BITQ_W2A8 = 4,     /* [ABQ] §3.2 Eq. (3): 2-bit asymmetric codes q in 0..3,
+                          W^ = delta * (q - z) per group of 128 consecutive inputs,
+                          delta and z fp16; the two bits are two binary planes.
+                          planes = 2, group = 128. */
+    BITQ_BVSR4 = 5     /* [BVSR] introduction: per group of 32 consecutive inputs,
+                          W^ = b + sum_k c_k beta_k with 4 {0,1} bitvectors
+                          beta_0..3 and a coefficient set (c_0..c_3, b) picked by
+                          a u8 index from a shared 256-entry cache of fp32 sets.
+                          planes = 4, group = 32. */
+} bitq_format;
+
+/* Activation dtypes accepted by bitq_quantize_act / bitq_gemv. */
+typedef enum {
+    BITQ_DT_F32 = 0,   /* raw fp32 activations [M, K] */
+    BITQ_DT_BF16 = 1,  /* raw bf16 activations [M, K] (uint16 bit patterns) */
+    BITQ_DT_ACT = 2    /* an activation buffer written by bitq_quantize_act */
+} bitq_dtype;
+
+/* Flags of bitq_gemv / bitq_gemm_smallM. */
+#define BITQ_F_ACC_INT32 1u  /* integer formats only: the production main loop
+                                writes its exact int32 partial sums to y instead
+                                of the fp32 output (see bitq_gemv). */
+
+/* Shape/format descriptor of one weight matrix. */
+typedef struct {
+    int32_t fmt;      /* bitq_format */
+    int32_t N;        /* outputs, 1 .. 2^24 */
+    int32_t K;        /* inputs, multiple of 32 (of 128 for BITQ_W2A8), <= 2^20 */
+    int32_t planes;   /* see bitq_format */
+    int32_t group;    /* see bitq_format */
+} bitq_wdesc;
+
+/*
+ * Logical (unpacked) quantized form of one weight matrix, host memory,
+ * row-major.  Only the fields of the descriptor's format are read; the rest
+ * may be NULL.  fp16 values are passed as their IEEE binary16 bit patterns.
+ *
+ *   BITQ_SIGN1   sign [N][K] (+1/-1), alpha [N]
+ *   BITQ_RABIT   sign [P][N][K] (+1/-1), g [P][N], h [P][K]
+ *   BITQ_TERNARY tern [N][K] (-1/0/+1), gamma
+ *   BITQ_W2A8    code [N][K] (0..3), delta [N][K/128], zero [N][K/128]
+ *                (zero must hold an integer 0..3)
+ *   BITQ_BVSR4   code [N][K] (0..15, bit k = bitvector beta_k), idx [N][K/32],
+ *                cache [256][5] as (c0, c1, c2, c3, b)
+ *
+ * This mirrors the weight-parameter struct of [BitNet] §3.2 (binary weights,
+ * scales, optional zero points) generalized to the five formats.
+ */
+typedef struct {
+    const int8_t*   sign;
+    const int8_t*   tern;
+    const uint8_t*  code;
+    const float*    alpha;
+    const uint16_t* g;
+    const uint16_t* h;
+    float           gamma;
+    const uint16_t* delta;
+    const uint16_t* zero;
+    const uint8_t*  idx;
+    const float*    cache;
+} bitq_logical;
+
+/*
+ * Packed blob layout (what bitq_pack_weights writes and the kernels read).
+ * Little-endian.  Np = N rounded up to 64, Kp = K rounded up to 128.
+ *
+ *   header, 256 bytes: u32 magic 0x51544942 ("BITQ"), u32 version (1),
+ *     u32 fmt, u32 N, u32 K, u32 P (planes), u32 group, u32 Np, u32 Kp,
+ *     u32 reserved (0), u64 off_planes, u64 off_c0, u64 off_c1,
+ *     u64 total_bytes; the rest is zero.
+ *   planes section: tiles of 64 rows x 128 inputs x 1 plane = 1024 bytes,
+ *     ordered [row tile t][k block b][plane p].  Inside a tile, row
+ *     r = n - 64t owns 16 contiguous bytes = 4 uint32 words; word w holds
+ *     inputs k = 128b + 32w + i at bit i (LSB first).  So the 64 rows of a
+ *     tile are adjacent: one 16-byte load per lane, 1 KB per 64-lane wave,
+ *     is fully coalesced ([BVSR] introduction: bitvectors of consecutive
+ *     output rows stored next to each other).  Rows >= N and inputs >= K are
+ *     zero bits.
+ *   plane meaning: SIGN1/RABIT bit 1 <-> +1, 0 <-> -1 (one plane per path);
+ *     TERNARY plane 0 = [T == +1], plane 1 = [T == -1]; W2A8 plane i = bit i
+ *     of q; BVSR4 plane k = beta_k.
+ *   coefficient sections (zero-padded):
+ *     SIGN1   c0 = alpha f32 [Np]
+ *     RABIT   c0 = g f16 [P][Np];  c1 = h f16 [P][Kp]
+ *     TERNARY c0 = gamma f32 [1]
+ *     W2A8    c0 = u32 [Np/64][Kp/128][64]: low 16 bits delta, high 16 bits z
+ *     BVSR4   c0 = idx u8 [Np/64][Kp/128][64][4] (byte j: group 4b + j);
+ *             c1 = cache f32 [256][5]
+ *   Every section starts at a multiple of 256 bytes; off_c1 = total_bytes
+ *   when a format has no c1 section.
+ */
+
+/* Bytes of the packed blob for a descriptor. */
+bitq_status bitq_packed_size(const bitq_wdesc* desc, size_t* bytes);
+
+/*
+ * Host packer: logical form -> packed blob (host memory, dst_bytes >=
+ * bitq_packed_size).  Rejects codes outside their range (BITQ_E_ARG).
+ * The blob is then copied to device memory by the caller (256-byte aligned).
+ */
+bitq_status bitq_pack_weights(const bitq_wdesc* desc, const bitq_logical* src,
+                              void* dst, size_t dst_bytes);
+
+/*
+ * Host quantizer + packer: fp32 W [N][K] (host) -> packed blob, using the
+ * library's own offline quantizer for the format:
+ *   SIGN1   B = sign(W) (sign(0) = +1, [BitNet] §2.1), alpha_n = mean_k |W|
+ *   RABIT   per path ([RaBiT] §2.2): B_p = sign(R_p), (g_p, h_p) = leading
+ *           singular pair of |R_p| by 30 power iterations (fp64, sigma split
+ *           evenly), stored fp16; R_{p+1} = R_p - g_p.B_p.h_p from the stored
+ *           fp16 values; R_0 = W
+ *   TERNARY gamma = mean|W| (fp32), T = clamp(rint(W/gamma), -1, 1) ([HGF] §1.2)
+ *   W2A8    per 128-group min/max RTN ([ABQ] Eq. 3, no compensation)
+ *   BVSR4   256-set cache from the group-range quantiles, exhaustive
+ *           nearest-point / least-SSE search per 32-group ([BVSR] intro)
+ * nthreads <= 0 uses all hardware threads.  W must be finite.
+ */
+bitq_status bitq_quantize_weights(const bitq_wdesc* desc, const float* W, void* dst,
+                                  size_t dst_bytes, int32_t nthreads);
+
+/*
+ * Activation buffer (written by bitq_quantize_act, read by the integer
+ * formats).  Kp = K rounded up to 128, Kw = Kp / 32.  Sections, each at a
+ * multiple of 256 bytes, in this order:
+ *   planes u32 [M][Kw][8]  plane j of word w = bit j of the two's-complement
+ *                          byte of q[m][32w + i] at bit i
+ *   S      i32 [M][Kw]     sum of q over each run of 32 inputs
+ *   q      i8  [M][Kp]     quantized activations (0 beyond K)
+ *   d      f32 [M]         dequantization step amax/127
+ */
+bitq_status bitq_act_size(int32_t M, int32_t K, size_t* bytes);
+
+/*
+ * Per-token int8 quantization ([HGF] §1.2: int8 activations rescaled by
+ * gamma_x/127; [BVSR] intro: online conversion of activations to bit-planes).
+ * For each token m: amax = max_k |x|; if amax = 0 then q = 0 and d = 0, else
+ * s = fl32(127/amax) (correctly rounded), q = clamp(rint(fl32(x*s)), -127,
+ * 127) (round half to even), d = fl32(amax/127).  Bit-exact.
+ *   x_dev   device [M][K] fp32 or bf16 (x_dtype BITQ_DT_F32/BF16), 16-byte
+ *           aligned, finite values
+ *   act_dev device buffer of bitq_act_size bytes, 256-byte aligned
+ * 1 <= M <= 64.
+ */
+bitq_status bitq_quantize_act(const void* x_dev, int32_t x_dtype, int32_t M, int32_t K,
+                              void* act_dev, size_t act_bytes, void* stream);
+
+/*
+ * Workspace for one bitq_gemv / bitq_gemm_smallM call (device memory, 256-byte
+ * aligned).  It holds per-split partial outputs and per-row-tile arrival
+ * counters.  The caller zero-fills it once before its first use; every
+ * completed call leaves the counters at zero again, so the same workspace is
+ * reused without clearing.  Calls that share a workspace must be ordered
+ * (same stream); concurrent calls need distinct workspaces.
+ */
+bitq_status bitq_workspace_size(const bitq_wdesc* desc, int32_t M, size_t* bytes);
+
+/*
+ * Batch-1 GEMV y[N] = W^ x.
+ *   w_dev  packed blob in device memory (256-byte aligned)
+ *   x_dev  SIGN1/RABIT: raw activations, BITQ_DT_F32 or BITQ_DT_BF16, 16-byte
+ *          aligned.  TERNARY/W2A8/BVSR4: an activation buffer from
+ *          bitq_quantize_act with M = 1 (x_dtype = BITQ_DT_ACT).
+ *   y_dev  fp32 [N], 4-byte aligned.
+ * Float formats ([RaBiT] §3.2 sign-apply instead of multiplies): y_n =
+ *   sum_p g_p[n] sum_k B_p[n,k] h_p[k] x_k (SIGN1: alpha_n sum_k B[n,k] x_k).
+ * Integer formats (AND+popcount of weight planes with activation planes,
+ *   [ABQ] abstract/§1, [BVSR] intro; exact int32 partial sums):
+ *   TERNARY y_n = gamma d Y_n, Y_n = sum_k T[n,k] q_k
+ *   W2A8    y_n = d sum_g delta[n,g] (A[n,g] - z[n,g] S128[g]),
+ *           A[n,g] = sum_{k in g} q[n,k] q_k
+ *   BVSR4   y_n = d sum_g (b S32[g] + sum_j c_j P[n,g,j]),
+ *           P[n,g,j] = sum_{k in g} beta_j[n,k] q_k, (c, b) = cache[idx[n,g]]
+ * flags & BITQ_F_ACC_INT32 (integer formats): y_dev receives, as int32,
+ *   TERNARY Y [N]; W2A8 A [N][K/128]; BVSR4 P [N][K/32][4]; the buffer must
+ *   hold that many int32 values.
+ */
+bitq_status bitq_gemv(const bitq_wdesc* desc, const void* w_dev, const void* x_dev,
+                      int32_t x_dtype, float* y_dev, void* ws_dev, size_t ws_bytes,
+                      uint32_t flags, void* stream);
+
+/*
+ * Small-batch GEMM y[M][N] = x W^T for 2 <= M <= 64, integer formats
+ * (TERNARY, W2A8, BVSR4), reading every weight once for all M tokens.
+ *   act_dev activation buffer from bitq_quantize_act with this M.
+ *   y_dev   fp32 [M][N].  BITQ_F_ACC_INT32 writes [M][...] int32 partials
+ *           laid out as in bitq_gemv, one block per token.
+ */
+bitq_status bitq_gemm_smallM(const bitq_wdesc* desc, const void* w_dev, const void* act_dev,
+                             int32_t M, float* y_dev, void* ws_dev, size_t ws_bytes,
+                             uint32_t flags, void* stream);
+
+/* Text of the last error on the calling thread ("" if none). */
+const char* bitq_last_error(void);
+
+/* BITQ_VERSION of the built library. */
+int32_t bitq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITQ_H */

@@ -1,0 +1,148 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bit_plane_gemv_amd as bq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    text = open(os.path.join(ROOT, "include", "bitq.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:bitq_status|const char\*|int32_t)\s+(bitq_\w+)\s*\(",
+                                 text, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    syms = _declared_symbols()
+    assert len(syms) >= 10
+    lib = ctypes.CDLL(bq.LIB_PATH)
+    for s in syms:
+        assert hasattr(lib, s), s
+    assert set(syms) == set(bq.EXPORTED)
+
+
+def test_version_and_error_string():
+    assert bq.version() == 1
+    with pytest.raises(bq.BitqError):
+        bq.packed_size(bq.wdesc(bq.SIGN1, 4, 33))
+    assert "multiple of 32" in bq.last_error()
+
+
+@pytest.mark.parametrize("desc,status", [
+    (bq.WDesc(9, 64, 128, 1, 0), bq.E_ARG),
+    (bq.WDesc(bq.SIGN1, 0, 128, 1, 0), bq.E_SHAPE),
+    (bq.WDesc(bq.SIGN1, 64, 48, 1, 0), bq.E_SHAPE),
+    (bq.WDesc(bq.SIGN1, 64, 16, 1, 0), bq.E_SHAPE),
+    (bq.WDesc(bq.SIGN1, 64, 128, 2, 0), bq.E_SHAPE),
+    (bq.WDesc(bq.RABIT, 64, 128, 4, 0), bq.E_SHAPE),
+    (bq.WDesc(bq.TERNARY, 64, 128, 2, 32), bq.E_SHAPE),
+    (bq.WDesc(bq.W2A8, 64, 96, 2, 128), bq.E_SHAPE),
+    (bq.WDesc(bq.W2A8, 64, 128, 2, 64), bq.E_SHAPE),
+    (bq.WDesc(bq.BVSR4, 64, 128, 3, 32), bq.E_SHAPE),
+])
+def test_descriptor_validation(desc, status):
+    with pytest.raises(bq.BitqError) as e:
+        bq.packed_size(desc)
+    assert e.value.status == status
+
+
+def test_packed_size_formula():
+    # planes + coefficients, each section 256-aligned, plus the 256-byte header
+    def a(v):
+        return (v + 255) // 256 * 256
+    for fmt, N, K, c0, c1 in [
+        (bq.SIGN1, 256, 256, 4 * 256, 0),
+        (bq.RABIT, 11008, 4096, 2 * 2 * 11008, 2 * 2 * 4096),
+        (bq.TERNARY, 512, 2048, 4, 0),
+        (bq.W2A8, 4096, 11008, 4 * 4096 * 86, 0),
+        (bq.BVSR4, 100, 96, 128 * 4, 5120),
+    ]:
+        d = bq.wdesc(fmt, N, K)
+        Np, Kp = (N + 63) // 64 * 64, (K + 127) // 128 * 128
+        planes = Np * Kp * d.planes // 8
+        off_c0 = a(256 + planes)
+        off_c1 = a(off_c0 + c0)
+        assert bq.packed_size(d) == a(off_c1 + c1)
+
+
+def test_pack_rejects_bad_codes_and_capacity():
+    d = bq.wdesc(bq.TERNARY, 2, 32)
+    T = np.zeros((2, 32), np.int8)
+    T[1, 3] = 2
+    with pytest.raises(bq.BitqError) as e:
+        bq.pack_weights(d, tern=T, gamma=1.0)
+    assert e.value.status == bq.E_ARG
+    d = bq.wdesc(bq.W2A8, 1, 128)
+    with pytest.raises(bq.BitqError) as e:
+        bq.pack_weights(d, code=np.full((1, 128), 4, np.uint8), delta=np.ones((1, 1), np.float16),
+                        zero=np.zeros((1, 1), np.float16))
+    assert e.value.status == bq.E_ARG
+    with pytest.raises(bq.BitqError) as e:          # zero point must be an integer 0..3
+        bq.pack_weights(d, code=np.zeros((1, 128), np.uint8), delta=np.ones((1, 1), np.float16),
+                        zero=np.full((1, 1), 0.5, np.float16))
+    assert e.value.status == bq.E_ARG
+    d = bq.wdesc(bq.SIGN1, 1, 32)
+    lg = bq.Logical()
+    B = np.ones((1, 32), np.int8)
+    al = np.ones(1, np.float32)
+    lg.sign, lg.alpha = B.ctypes.data, al.ctypes.data
+    small = np.zeros(16, np.uint8)
+    st = bq._lib.bitq_pack_weights(ctypes.byref(d), ctypes.byref(lg), small.ctypes.data, 16)
+    assert st == bq.E_CAPACITY
+    lg.alpha = None
+    big = np.zeros(bq.packed_size(d), np.uint8)
+    assert bq._lib.bitq_pack_weights(ctypes.byref(d), ctypes.byref(lg), big.ctypes.data,
+                                     big.nbytes) == bq.E_ARG
+
+
+def test_device_entry_points_validate_before_any_device_call():
+    d = bq.wdesc(bq.W2A8, 128, 256)
+    ws_need = bq.workspace_size(d, 1)
+    good = 1 << 20                              # fake, 256-aligned addresses: never dereferenced
+    # null pointer
+    assert bq._lib.bitq_gemv(ctypes.byref(d), None, good, bq.DT_ACT, good, good, ws_need, 0, None) == bq.E_ARG
+    # raw activations for an integer format
+    assert bq._lib.bitq_gemv(ctypes.byref(d), good, good, bq.DT_BF16, good, good, ws_need, 0, None) == bq.E_ARG
+    # misaligned blob / activation buffer / workspace
+    assert bq._lib.bitq_gemv(ctypes.byref(d), good + 16, good, bq.DT_ACT, good, good, ws_need, 0,
+                             None) == bq.E_ALIGN
+    assert bq._lib.bitq_gemv(ctypes.byref(d), good, good + 64, bq.DT_ACT, good, good, ws_need, 0,
+                             None) == bq.E_ALIGN
+    assert bq._lib.bitq_gemv(ctypes.byref(d), good, good, bq.DT_ACT, good, good + 8, ws_need, 0,
+                             None) == bq.E_ALIGN
+    # workspace too small, unknown flag
+    assert bq._lib.bitq_gemv(ctypes.byref(d), good, good, bq.DT_ACT, good, good, ws_need - 1, 0,
+                             None) == bq.E_CAPACITY
+    assert bq._lib.bitq_gemv(ctypes.byref(d), good, good, bq.DT_ACT, good, good, ws_need, 8,
+                             None) == bq.E_ARG
+    # float formats: M = 1 only, raw activations, no integer flag
+    ds = bq.wdesc(bq.RABIT, 128, 256)
+    wsn = bq.workspace_size(ds, 1)
+    assert bq._lib.bitq_gemv(ctypes.byref(ds), good, good, bq.DT_ACT, good, good, wsn, 0, None) == bq.E_ARG
+    assert bq._lib.bitq_gemv(ctypes.byref(ds), good, good + 4, bq.DT_BF16, good, good, wsn, 0,
+                             None) == bq.E_ALIGN
+    assert bq._lib.bitq_gemv(ctypes.byref(ds), good, good, bq.DT_BF16, good, good, wsn, 1,
+                             None) == bq.E_UNSUPPORTED
+    # small-M range and formats
+    assert bq._lib.bitq_gemm_smallM(ctypes.byref(d), good, good, 1, good, good, 1 << 30, 0, None) == bq.E_SHAPE
+    assert bq._lib.bitq_gemm_smallM(ctypes.byref(d), good, good, 65, good, good, 1 << 30, 0, None) == bq.E_SHAPE
+    assert bq._lib.bitq_gemm_smallM(ctypes.byref(ds), good, good, 4, good, good, 1 << 30, 0,
+                                    None) == bq.E_UNSUPPORTED
+    # activation quantizer
+    n = bq.act_size(4, 256)
+    assert bq._lib.bitq_quantize_act(good, bq.DT_BF16, 0, 256, good, n, None) == bq.E_SHAPE
+    assert bq._lib.bitq_quantize_act(good, bq.DT_BF16, 4, 100, good, n, None) == bq.E_SHAPE
+    assert bq._lib.bitq_quantize_act(good, 7, 4, 256, good, n, None) == bq.E_ARG
+    assert bq._lib.bitq_quantize_act(good + 2, bq.DT_BF16, 4, 256, good, n, None) == bq.E_ALIGN
+    assert bq._lib.bitq_quantize_act(good, bq.DT_BF16, 4, 256, good, n - 1, None) == bq.E_CAPACITY
+
+
+def test_act_size_matches_documented_layout():
+    for M, K in [(1, 4096), (16, 512), (64, 11008), (3, 96)]:
+        assert bq.act_size(M, K) == bq.act_layout(M, K)["total"]
