@@ -7,7 +7,7 @@ data_ptr()) or raw integer addresses; PyTorch is used only to own device
 memory and to name the current HIP stream.
 
 Importing this package fails loudly if libbitq.so has not been built
-(python -m bit_plane_gemv_amd.build); there is no fallback path.
+(python bit_plane_gemv_amd/build.py); there is no fallback path.
 """
 from __future__ import annotations
 
@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libbitq.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"libbitq.so not found at {LIB_PATH}; build it with "
-                      "`python -m bit_plane_gemv_amd.build`")
+                      "`python bit_plane_gemv_amd/build.py`")
 
 # One HIP runtime per process: torch wheels bundle their own libamdhip64, and
 # loading libbitq.so first would bind it to the system runtime while torch

@@ -1,7 +1,10 @@
 """Build libbitq.so in-tree with hipcc for gfx950.
 
-    python -m bit_plane_gemv_amd.build          # build (always recompiles)
-    python -m bit_plane_gemv_amd.build --asm    # also dump the gfx950 assembly
+    python bit_plane_gemv_amd/build.py          # build (always recompiles)
+    python bit_plane_gemv_amd/build.py --asm    # also dump the gfx950 assembly
+
+This file is loaded by path (not as part of the package), so it works before
+libbitq.so exists; importing the package itself requires the built library.
 
 The shared library holds the host code (validation, packer, quantizers) and
 the HIP kernels.  Host code is compiled without floating-point contraction so

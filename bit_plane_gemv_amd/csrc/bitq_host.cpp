@@ -582,23 +582,39 @@ Plan make_plan(const bitq_wdesc& d, int M) {
     const int64_t Np = round_up(d.N, kRowTile);
     const int64_t NB = round_up(d.K, kKBlock) / kKBlock;
     p.M = M;
+    if (!lut) {
+        // Integer formats: one workgroup per 16 rows covers the whole k range
+        // (16 k-groups x blocks_per_split blocks per round); no workspace.
+        const int64_t need = (NB + 15) / 16;
+        const int sizes[6] = {1, 2, 3, 4, 6, 8};
+        p.blocks_per_split = 8;
+        for (int sz : sizes)
+            if (sz >= need) {
+                p.blocks_per_split = sz;
+                break;
+            }
+        p.waves_per_wg = 4;
+        p.rows_per_wg = 16;
+        p.row_groups = static_cast<int>((d.N + 15) / 16);
+        p.splits = 1;
+        p.off_partials = p.off_counters = 0;
+        p.ws_bytes = 0;
+        return p;
+    }
     p.waves_per_wg = lut ? 4 : 1;
     p.rows_per_wg = kRowTile * p.waves_per_wg;
     p.row_groups = static_cast<int>((Np + p.rows_per_wg - 1) / p.rows_per_wg);
-    const int64_t target = lut ? 512 : 1024;  // workgroups wanted in the grid
-    if (lut) {
-        // blocks per split is a compile-time variant of the kernel: 1, 2 or 4
-        int kb = 4;
-        while (kb > 1 && p.row_groups * ((NB + kb - 1) / kb) < target) kb >>= 1;
-        p.blocks_per_split = kb;
-    } else {
-        int64_t kb = (NB * p.row_groups + target - 1) / target;
-        p.blocks_per_split = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(kb, NB)));
-    }
+    // Blocks per split are compile-time variants of the kernels (1, 2, 4, and
+    // 8 for the integer kernels): take the largest that still gives at least
+    // `target` workgroups.
+    const int64_t target = lut ? 512 : 1024;
+    int kb = lut ? 4 : 8;
+    while (kb > 1 && p.row_groups * ((NB + kb - 1) / kb) < target) kb >>= 1;
+    p.blocks_per_split = kb;
     p.splits = static_cast<int>((NB + p.blocks_per_split - 1) / p.blocks_per_split);
     p.off_partials = 0;
     p.off_counters = align256(static_cast<size_t>(p.splits) * M * Np * 4);
-    p.ws_bytes = align256(p.off_counters + static_cast<size_t>(p.row_groups) * 4);
+    p.ws_bytes = align256(p.off_counters + static_cast<size_t>(Np) * 4);  // one counter per row
     return p;
 }
 
@@ -756,7 +772,7 @@ static bitq_status gemv_common(const bitq_wdesc* desc, const void* w_dev, const 
     bitq_status s = check_desc(desc);
     if (s) return s;
     const bitq_wdesc d = *desc;
-    if (!w_dev || !x_dev || !y_dev || !ws_dev) return fail(BITQ_E_ARG, "a device pointer is NULL");
+    if (!w_dev || !x_dev || !y_dev) return fail(BITQ_E_ARG, "a device pointer is NULL");
     if (flags & ~BITQ_F_ACC_INT32) return fail(BITQ_E_ARG, "unknown flags 0x%x", flags);
     const bool float_fmt = (d.fmt == BITQ_SIGN1 || d.fmt == BITQ_RABIT);
     if (float_fmt) {
@@ -772,10 +788,13 @@ static bitq_status gemv_common(const bitq_wdesc* desc, const void* w_dev, const 
     }
     if (!aligned(w_dev, 256)) return fail(BITQ_E_ALIGN, "w_dev must be 256-byte aligned");
     if (!aligned(y_dev, 4)) return fail(BITQ_E_ALIGN, "y_dev must be 4-byte aligned");
-    if (!aligned(ws_dev, 256)) return fail(BITQ_E_ALIGN, "workspace must be 256-byte aligned");
     Plan plan = make_plan(d, M);
-    if (ws_bytes < plan.ws_bytes)
-        return fail(BITQ_E_CAPACITY, "workspace has %zu bytes, needs %zu", ws_bytes, plan.ws_bytes);
+    if (plan.ws_bytes > 0) {
+        if (!ws_dev) return fail(BITQ_E_ARG, "workspace is NULL");
+        if (!aligned(ws_dev, 256)) return fail(BITQ_E_ALIGN, "workspace must be 256-byte aligned");
+        if (ws_bytes < plan.ws_bytes)
+            return fail(BITQ_E_CAPACITY, "workspace has %zu bytes, needs %zu", ws_bytes, plan.ws_bytes);
+    }
     int is950 = 0;
     int e = current_device_is_gfx950(&is950);
     if (e) return fail(BITQ_E_DEVICE, "HIP error %d while querying the device", e);

@@ -43,7 +43,7 @@ struct Plan {
     int splits;            // ceil((Kp/128) / blocks_per_split)
     int M;
     size_t off_partials;   // f32 [splits][M][Np]
-    size_t off_counters;   // u32 [row_groups]
+    size_t off_counters;   // u32 [Np]: per-row arrival counters
     size_t ws_bytes;
 };
 Plan make_plan(const bitq_wdesc& d, int M);

@@ -48,23 +48,60 @@ __device__ __forceinline__ float wave_max(float v) {
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // ------------------------------------------------- split-k reduction helper
-// Called by every thread of the workgroup after it computed `part` (the
-// partial output of row n, split s, token m).  Returns true in the workgroup
-// that must finish the row group (the last to arrive); that workgroup then
-// reads the partials back from the workspace.
-__device__ __forceinline__ bool arrive_last(uint32_t* counter, int splits, int* s_flag) {
-    __threadfence();  // make this workgroup's partial stores visible device-wide
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t prev = atomicAdd(counter, 1u);
-        int last = (prev == static_cast<uint32_t>(splits - 1));
-        if (last) *counter = 0u;  // reset for the next call on this workspace
-        *s_flag = last;
+// When a row's k range is split over several workgroups, each split stores
+// its partial output with a device-scope atomic store (written through to
+// the device-coherent level, not left in one XCD's L2), waits until the store
+// is acknowledged, then increments the row's arrival counter with a
+// device-scope atomic.  The lane that sees the counter at splits - 1 is the
+// last one for that row: it resets the counter for the next call and adds
+// the row's partials in split order (deterministic), reading them with
+// device-scope atomic loads.  Rows hand off independently: no workgroup
+// barrier and no cache-wide write-back or invalidate is involved.
+__device__ __forceinline__ void store_partial(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_partial(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_partial_i(int32_t* p, int32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t load_partial_i(const int32_t* p) {
+    return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Sum of the partials p[0], p[stride], ..., p[(count-1)*stride] in index
+// order.  Loads are issued 32 at a time (indices clamped in bounds, the
+// surplus ignored), so a batch costs one memory round trip, not 32.
+template <typename T>
+__device__ __forceinline__ T sum_partials(const T* p, size_t stride, int count) {
+    constexpr int kBatch = 32;
+    T s = 0;
+    for (int s0 = 0; s0 < count; s0 += kBatch) {
+        T v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int i = min(s0 + u, count - 1);
+            if constexpr (sizeof(T) == 4 && static_cast<T>(0.5f) != 0)
+                v[u] = load_partial(reinterpret_cast<const float*>(p) + i * stride);
+            else
+                v[u] = load_partial_i(reinterpret_cast<const int32_t*>(p) + i * stride);
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            if (s0 + u < count) s += v[u];
     }
-    __syncthreads();
-    const bool last = *s_flag != 0;
-    if (last) __threadfence();  // acquire: see the other workgroups' partials
-    return last;
+    return s;
+}
+
+// Per-lane arrival after this lane's partial stores: true for the last split
+// of the lane's row (whose counter is then reset to zero).
+__device__ __forceinline__ bool arrive_last_row(uint32_t* row_counter, int splits) {
+    __builtin_amdgcn_s_waitcnt(0);  // this lane's partial stores are complete
+    const uint32_t prev = __hip_atomic_fetch_add(row_counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev != static_cast<uint32_t>(splits - 1)) return false;
+    __hip_atomic_store(row_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
 }
 
 // ======================================================= activation quantizer
@@ -72,14 +109,67 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, int splits, int* 
 // per-token absmax scale, dequantized with amax/127; [BVSR] intro: online
 // conversion of activations to the bit format.  Arithmetic order fixed for
 // bit-exactness: s = fl32(127/amax) correctly rounded, q = rint(fl32(x*s)).
-__global__ __launch_bounds__(256) void quant_act_kernel(const void* __restrict__ x, int dt, int K, int Kw,
+// Thread t owns the 32-input words t, t+256, ...: it reads each word's 32
+// activations with 16-byte loads, keeps them for the second pass, and writes
+// the word's 8 planes, its sum and its 32 codes.
+template <int DT>
+__device__ __forceinline__ void load_word(const void* x, size_t row, int K, int w, float (&v)[32]) {
+    const int k0 = 32 * w;
+    if (k0 + 32 <= K) {
+        if (DT == BITQ_DT_F32) {
+            const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(x) + row + k0);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint4 u = p[i];
+                v[4 * i] = __uint_as_float(u.x);
+                v[4 * i + 1] = __uint_as_float(u.y);
+                v[4 * i + 2] = __uint_as_float(u.z);
+                v[4 * i + 3] = __uint_as_float(u.w);
+            }
+        } else {
+            const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + row + k0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint4 u = p[i];
+                const uint32_t a[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    v[8 * i + 2 * j] = __uint_as_float(a[j] << 16);
+                    v[8 * i + 2 * j + 1] = __uint_as_float(a[j] & 0xFFFF0000u);
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) v[i] = 0.0f;  // word entirely beyond K (K is a multiple of 32)
+    }
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void quant_act_kernel(const void* __restrict__ x, int K, int Kw,
                                                         uint32_t* __restrict__ planes, int32_t* __restrict__ S,
                                                         int8_t* __restrict__ q, float* __restrict__ dq) {
     __shared__ float s_red[4];
     const int m = blockIdx.x;
     const size_t xrow = static_cast<size_t>(m) * K;
+    constexpr int kHold = 2;  // words kept in registers between the passes
+    float v[kHold][32];
     float amax = 0.0f;
-    for (int k = threadIdx.x; k < K; k += 256) amax = fmaxf(amax, fabsf(load_act(x, dt, xrow + k)));
+#pragma unroll
+    for (int h = 0; h < kHold; ++h) {
+        const int w = threadIdx.x + 256 * h;
+        if (w < Kw) {
+            load_word<DT>(x, xrow, K, w, v[h]);
+#pragma unroll
+            for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[h][i]));
+        }
+    }
+    for (int w = threadIdx.x + 256 * kHold; w < Kw; w += 256) {
+        float t[32];
+        load_word<DT>(x, xrow, K, w, t);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(t[i]));
+    }
     amax = wave_max(amax);
     if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = amax;
     __syncthreads();
@@ -89,18 +179,23 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const void* __restrict__
         s = __fdiv_rn(127.0f, amax);
         d = __fdiv_rn(amax, 127.0f);
     }
-    for (int w = threadIdx.x; w < Kw; w += 256) {
+    for (int w = threadIdx.x, h = 0; w < Kw; w += 256, ++h) {
+        float t[32];
+        if (h < kHold) {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) t[i] = (h == 0) ? v[0][i] : v[1][i];
+        } else {
+            load_word<DT>(x, xrow, K, w, t);
+        }
         uint32_t pl[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         uint32_t qb[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         int sum = 0;
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
-            const int k = 32 * w + i;
             int qi = 0;
-            if (k < K && amax > 0.0f) {
-                float v = __fmul_rn(load_act(x, dt, xrow + k), s);
-                v = fminf(fmaxf(rintf(v), -127.0f), 127.0f);
-                qi = static_cast<int>(v);
+            if (amax > 0.0f) {
+                float r = rintf(__fmul_rn(t[i], s));
+                qi = static_cast<int>(fminf(fmaxf(r, -127.0f), 127.0f));
             }
             sum += qi;
             const uint32_t byte = static_cast<uint32_t>(qi) & 0xFFu;
@@ -129,64 +224,132 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const void* __restrict__
 // the sign-apply sum, with one table read and one add per 4 weights.
 // Every lane of a wave reads the same table (one k position), so the 16
 // entries are broadcast without bank conflicts.
-template <int P, int KB>
+
+// Byte offset 4*nibble of the nibble held in bits 2..5 of byte B of w: one
+// SDWA instruction (byte select + AND with the inline constant 60).
+#define BITQ_NIB_ADDR(NAME, B)                                                                     \
+    __device__ __forceinline__ uint32_t NAME(uint32_t w) {                                          \
+        uint32_t r;                                                                                \
+        asm("v_and_b32_sdwa %0, 60, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD "        \
+            "src1_sel:BYTE_" #B                                                                    \
+            : "=v"(r)                                                                              \
+            : "v"(w));                                                                             \
+        return r;                                                                                  \
+    }
+BITQ_NIB_ADDR(nib_addr0, 0)
+BITQ_NIB_ADDR(nib_addr1, 1)
+BITQ_NIB_ADDR(nib_addr2, 2)
+BITQ_NIB_ADDR(nib_addr3, 3)
+#undef BITQ_NIB_ADDR
+
+__device__ __forceinline__ uint32_t nib_addr(uint32_t w, int byte) {
+    switch (byte) {
+        case 0: return nib_addr0(w);
+        case 1: return nib_addr1(w);
+        case 2: return nib_addr2(w);
+        default: return nib_addr3(w);
+    }
+}
+
+template <int P, int KB, bool RABIT, int DT>
 __global__ __launch_bounds__(256) void gemv_sign_kernel(const uint8_t* __restrict__ blob, size_t off_c0,
-                                                        size_t off_c1, const void* __restrict__ x, int dt,
-                                                        int fmt, int N, int K, int Np, int Tn, int Tb, int splits,
-                                                        float* __restrict__ y, float* __restrict__ ws_part,
-                                                        uint32_t* __restrict__ ws_cnt) {
-    constexpr int CH = KB * 32;        // 4-input chunks in the k slice
-    __shared__ float4 lut4[CH * P * 4];  // [chunk][plane][16 floats]
-    __shared__ int s_flag;
+                                                        size_t off_c1, const void* __restrict__ x, int N, int K,
+                                                        int Np, int Tn, int Tb, int splits, float* __restrict__ y,
+                                                        float* __restrict__ ws_part, uint32_t* __restrict__ ws_cnt) {
+    constexpr int CH = KB * 32;          // 4-input chunks in the k slice
+    constexpr int NT = CH * P;           // tables in the k slice
+    constexpr int TPT = (NT + 255) / 256;  // tables per thread
+    __shared__ float4 lut4[NT * 4];      // [chunk][plane][16 floats]
     const int split = blockIdx.y;
     const int k0 = split * KB * kKBlock;
-
-    // ---- build the tables for this k slice
-    const uint16_t* hbits = reinterpret_cast<const uint16_t*>(blob + off_c1);
-    for (int tbl = threadIdx.x; tbl < CH * P; tbl += 256) {
-        const int c = tbl / P, p = tbl % P;
-        float xv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int k = k0 + 4 * c + i;
-            float v = 0.0f;
-            if (k < K) {
-                v = load_act(x, dt, k);
-                if (fmt == BITQ_RABIT) v = v * f16_bits_to_f32(hbits[static_cast<size_t>(p) * (Tb * kKBlock) + k]);
-            }
-            xv[i] = v;
-        }
-        const float a = xv[0], b = xv[1], cc = xv[2], dd = xv[3];
-        const float lo[4] = {-a - b, a - b, -a + b, a + b};
-        const float hi[4] = {-cc - dd, cc - dd, -cc + dd, cc + dd};
-        float4* dst = &lut4[tbl * 4];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-            dst[q4] = make_float4(lo[0] + hi[q4], lo[1] + hi[q4], lo[2] + hi[q4], lo[3] + hi[q4]);
-    }
-    __syncthreads();
-
-    // ---- main loop: one row per lane
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + wave;
     const int n = t * kRowTile + lane;
-    float part = 0.0f;
-    if (t < Tn) {
-        const uint8_t* lut_bytes = reinterpret_cast<const uint8_t*>(lut4);
-        uint4 wv[KB][P];
+    const uint16_t* hbits = reinterpret_cast<const uint16_t*>(blob + off_c1);
+
+    // ---- 1. weight words and row scales (raw bits, converted at the end),
+    //         all in flight before anything waits.
+    //         Loads are unconditional (no branch, so nothing waits on
+    //         them early): a wave beyond the last row tile re-reads the last
+    //         tile and stores nothing; a block beyond K re-reads the last
+    //         block, whose chunks here have all-zero tables (zero
+    //         activations), so it adds nothing.
+    const int tl = min(t, Tn - 1);
+    const int nl = tl * kRowTile + lane;
+    uint4 wv[KB][P];
+    uint32_t graw[P];
 #pragma unroll
-        for (int bb = 0; bb < KB; ++bb) {
-            const int b = split * KB + bb;
+    for (int bb = 0; bb < KB; ++bb) {
+        const int b = min(split * KB + bb, Tb - 1);
 #pragma unroll
-            for (int p = 0; p < P; ++p) {
-                if (b < Tb) {
-                    const size_t off = (static_cast<size_t>(t) * Tb + b) * P + p;
-                    wv[bb][p] = *reinterpret_cast<const uint4*>(blob + kHeaderBytes + off * 1024 + lane * 16);
-                } else {
-                    wv[bb][p] = make_uint4(0, 0, 0, 0);
-                }
+        for (int p = 0; p < P; ++p) {
+            const size_t off = (static_cast<size_t>(tl) * Tb + b) * P + p;
+            wv[bb][p] = *reinterpret_cast<const uint4*>(blob + kHeaderBytes + off * 1024 + lane * 16);
+        }
+    }
+    if (RABIT) {
+        const uint16_t* g = reinterpret_cast<const uint16_t*>(blob + off_c0);
+#pragma unroll
+        for (int p = 0; p < P; ++p) graw[p] = g[static_cast<size_t>(p) * Np + nl];
+    } else {
+        graw[0] = reinterpret_cast<const uint32_t*>(blob + off_c0)[nl];  // alpha, fp32 bits
+    }
+
+    // ---- 2. activations (and column scales) of this thread's tables: small
+    //         and shared by all workgroups (L2 hits).  They are issued after
+    //         the weight loads; since loads complete in order, the short table
+    //         build then runs once the weights have arrived instead of holding
+    //         the weight loads back by an L2 round trip.  K is a multiple of
+    //         32: a chunk of 4 inputs is entirely in or out.
+    float xv[TPT][4], hv[TPT][4];
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+        const int tbl = threadIdx.x + 256 * i;
+        const int c = tbl / P, p = tbl % P;
+        const int k = k0 + 4 * c;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            xv[i][e] = 0.0f;
+            hv[i][e] = 1.0f;
+        }
+        if (tbl < NT && k < K) {
+            if (DT == BITQ_DT_F32) {
+                const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(x) + k);
+                xv[i][0] = v.x; xv[i][1] = v.y; xv[i][2] = v.z; xv[i][3] = v.w;
+            } else {
+                const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(x) + k);
+                xv[i][0] = __uint_as_float(v.x << 16); xv[i][1] = __uint_as_float(v.x & 0xFFFF0000u);
+                xv[i][2] = __uint_as_float(v.y << 16); xv[i][3] = __uint_as_float(v.y & 0xFFFF0000u);
+            }
+            if (RABIT) {
+                const uint2 h2 = *reinterpret_cast<const uint2*>(hbits + static_cast<size_t>(p) * (Tb * kKBlock) + k);
+                hv[i][0] = f16_bits_to_f32(h2.x); hv[i][1] = f16_bits_to_f32(h2.x >> 16);
+                hv[i][2] = f16_bits_to_f32(h2.y); hv[i][3] = f16_bits_to_f32(h2.y >> 16);
             }
         }
+    }
+
+    // ---- 3. tables: x~ = h x, then the 16 signed sums of each chunk
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+        const int tbl = threadIdx.x + 256 * i;
+        if (tbl < NT) {
+            const float a = xv[i][0] * hv[i][0], b = xv[i][1] * hv[i][1];
+            const float cc = xv[i][2] * hv[i][2], dd = xv[i][3] * hv[i][3];
+            const float lo[4] = {-a - b, a - b, -a + b, a + b};
+            const float hi[4] = {-cc - dd, cc - dd, -cc + dd, cc + dd};
+            float4* dst = &lut4[tbl * 4];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+                dst[q4] = make_float4(lo[0] + hi[q4], lo[1] + hi[q4], lo[2] + hi[q4], lo[3] + hi[q4]);
+        }
+    }
+    __syncthreads();
+
+    // ---- 4. table lookups: one row per lane
+    float part = 0.0f;
+    {
+        const uint8_t* lut_bytes = reinterpret_cast<const uint8_t*>(lut4);
         float acc[P];
 #pragma unroll
         for (int p = 0; p < P; ++p) acc[p] = 0.0f;
@@ -197,35 +360,33 @@ __global__ __launch_bounds__(256) void gemv_sign_kernel(const uint8_t* __restric
                 const uint32_t words[4] = {wv[bb][p].x, wv[bb][p].y, wv[bb][p].z, wv[bb][p].w};
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
-                    const uint32_t w4 = words[w] << 2;   // nibble 2j at byte j, scaled by 4
-                    const uint32_t w2 = words[w] >> 2;   // nibble 2j+1 at byte j, scaled by 4
+                    const uint32_t w4 = words[w] << 2;   // nibble 2j in bits 2..5 of byte j
+                    const uint32_t w2 = words[w] >> 2;   // nibble 2j+1 in bits 2..5 of byte j
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int c = bb * 32 + w * 8 + 2 * j;
-                        const uint32_t a0 = (w4 >> (8 * j)) & 0x3Cu;
-                        const uint32_t a1 = (w2 >> (8 * j)) & 0x3Cu;
+                        const uint32_t a0 = nib_addr(w4, j);
+                        const uint32_t a1 = nib_addr(w2, j);
                         acc[p] += *reinterpret_cast<const float*>(lut_bytes + a0 + ((c * P + p) * 64));
                         acc[p] += *reinterpret_cast<const float*>(lut_bytes + a1 + (((c + 1) * P + p) * 64));
                     }
                 }
             }
-        if (fmt == BITQ_RABIT) {
-            const uint16_t* g = reinterpret_cast<const uint16_t*>(blob + off_c0);
+        if (RABIT) {
 #pragma unroll
-            for (int p = 0; p < P; ++p) part += f16_bits_to_f32(g[static_cast<size_t>(p) * Np + n]) * acc[p];
+            for (int p = 0; p < P; ++p) part += f16_bits_to_f32(graw[p]) * acc[p];
         } else {
-            part = reinterpret_cast<const float*>(blob + off_c0)[n] * acc[0];
+            part = __uint_as_float(graw[0]) * acc[0];
         }
     }
     if (splits == 1) {
         if (t < Tn && n < N) y[n] = part;
         return;
     }
-    if (t < Tn) ws_part[static_cast<size_t>(split) * Np + n] = part;
-    if (arrive_last(&ws_cnt[blockIdx.x], splits, &s_flag) && t < Tn && n < N) {
-        float s = 0.0f;
-        for (int sp = 0; sp < splits; ++sp) s += ws_part[static_cast<size_t>(sp) * Np + n];
-        y[n] = s;
+    if (t < Tn) {
+        store_partial(&ws_part[static_cast<size_t>(split) * Np + n], part);
+        if (arrive_last_row(&ws_cnt[n], splits) && n < N)
+            y[n] = sum_partials<float>(ws_part + n, static_cast<size_t>(Np), splits);
     }
 }
 
@@ -239,6 +400,7 @@ __global__ __launch_bounds__(256) void gemv_sign_kernel(const uint8_t* __restric
 // plane words are the same for all 64 rows of a wave, so they are read with
 // scalar loads and enter the AND as scalar operands; each weight word costs
 // one AND and one popcount-accumulate (v_bcnt_u32_b32) per activation plane.
+// All weight loads of the workgroup's k slice are issued before any compute.
 //
 // Per-token epilogues (y before the per-token factor d, applied at the end):
 //   TERNARY ([HGF] §1.2): Y = sum_j c_j (popc(P & X_j) - popc(M & X_j)),
@@ -264,28 +426,44 @@ __device__ __forceinline__ int combine_planes(const int (&a)[8]) {
     return r;
 }
 
-template <int FMT, bool ACC>
+template <int FMT, bool ACC, int KB>
 __global__ __launch_bounds__(64) void gemv_bits_kernel(const uint8_t* __restrict__ blob, size_t off_c0,
                                                        size_t off_c1, const uint8_t* __restrict__ act,
                                                        size_t act_off_S, size_t act_off_d, int M, int N,
-                                                       int K, int Np, int Tn, int Tb, int KB, int splits,
+                                                       int K, int Np, int Tn, int Tb, int splits,
                                                        float* __restrict__ y, float* __restrict__ ws_part,
                                                        uint32_t* __restrict__ ws_cnt) {
     constexpr int P = IntCfg<FMT>::P;
     __shared__ float4 s_cache[FMT == BITQ_BVSR4 ? 256 * 2 : 1];
-    __shared__ int s_flag;
     const int lane = threadIdx.x;
     const int t = blockIdx.x;
     const int n = t * kRowTile + lane;
     const int split = blockIdx.y;
     const int b0 = split * KB;
-    const int b1 = min(Tb, b0 + KB);
     const int Kw = Tb * 4;
     const uint32_t* __restrict__ aplanes = reinterpret_cast<const uint32_t*>(act);
     const int32_t* __restrict__ aS = reinterpret_cast<const int32_t*>(act + act_off_S);
     const float* __restrict__ ad = reinterpret_cast<const float*>(act + act_off_d);
 
-    if (FMT == BITQ_BVSR4) {
+    // ---- all weight words and coefficients of the k slice, issued up front
+    //      and unconditionally (a block beyond K re-reads the last block and
+    //      is skipped below)
+    uint4 wv[KB][P];
+    uint32_t coef[KB];
+#pragma unroll
+    for (int bb = 0; bb < KB; ++bb) {
+        const int b = min(b0 + bb, Tb - 1);
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const size_t off = (static_cast<size_t>(t) * Tb + b) * P + p;
+            wv[bb][p] = *reinterpret_cast<const uint4*>(blob + kHeaderBytes + off * 1024 + lane * 16);
+        }
+        coef[bb] = 0;
+        if (FMT == BITQ_W2A8 || FMT == BITQ_BVSR4)
+            coef[bb] = reinterpret_cast<const uint32_t*>(blob + off_c0)[(static_cast<size_t>(t) * Tb + b) * 64 + lane];
+    }
+
+    if (FMT == BITQ_BVSR4 && !ACC) {
         const float* cache = reinterpret_cast<const float*>(blob + off_c1);
         for (int e = lane; e < 256; e += 64) {
             const float* c = cache + 5 * e;
@@ -305,23 +483,15 @@ __global__ __launch_bounds__(64) void gemv_bits_kernel(const uint8_t* __restrict
 #pragma unroll
             for (int j = 0; j < 8; ++j) tacc[i][j] = 0;
 
-        for (int b = b0; b < b1; ++b) {
-            const int bu = uniform(b);
-            uint4 wv[P];
 #pragma unroll
-            for (int p = 0; p < P; ++p) {
-                const size_t off = (static_cast<size_t>(t) * Tb + bu) * P + p;
-                wv[p] = *reinterpret_cast<const uint4*>(blob + kHeaderBytes + off * 1024 + lane * 16);
-            }
-            uint32_t coef = 0;
-            if (FMT == BITQ_W2A8 || FMT == BITQ_BVSR4)
-                coef = reinterpret_cast<const uint32_t*>(blob + off_c0)[(static_cast<size_t>(t) * Tb + bu) * 64 + lane];
-
+        for (int bb = 0; bb < KB; ++bb) {
+            const int bu = uniform(b0 + bb);
+            if (bu >= Tb) break;
             if (FMT == BITQ_TERNARY) {
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
                     const uint32_t* xw = xp + static_cast<size_t>(bu * 4 + w) * 8;
-                    const uint32_t wp = (&wv[0].x)[w], wm = (&wv[1].x)[w];
+                    const uint32_t wp = (&wv[bb][0].x)[w], wm = (&wv[bb][1].x)[w];
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
                         const uint32_t xj = xw[j];
@@ -338,7 +508,7 @@ __global__ __launch_bounds__(64) void gemv_bits_kernel(const uint8_t* __restrict
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
                     const uint32_t* xw = xp + static_cast<size_t>(bu * 4 + w) * 8;
-                    const uint32_t w0 = (&wv[0].x)[w], w1 = (&wv[1].x)[w];
+                    const uint32_t w0 = (&wv[bb][0].x)[w], w1 = (&wv[bb][1].x)[w];
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
                         const uint32_t xj = xw[j];
@@ -355,8 +525,8 @@ __global__ __launch_bounds__(64) void gemv_bits_kernel(const uint8_t* __restrict
                     if (n < N) reinterpret_cast<int32_t*>(y)[(static_cast<size_t>(m) * N + n) * G + bu] = A;
                 } else {
                     const int S128 = xS[bu * 4] + xS[bu * 4 + 1] + xS[bu * 4 + 2] + xS[bu * 4 + 3];
-                    const float delta = f16_bits_to_f32(coef);
-                    const float z = f16_bits_to_f32(coef >> 16);
+                    const float delta = f16_bits_to_f32(coef[bb]);
+                    const float z = f16_bits_to_f32(coef[bb] >> 16);
                     yacc += delta * (static_cast<float>(A) - z * static_cast<float>(S128));
                 }
             } else {  // BVSR4
@@ -366,7 +536,7 @@ __global__ __launch_bounds__(64) void gemv_bits_kernel(const uint8_t* __restrict
                     int a[4][8];
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
-                        const uint32_t bk = (&wv[k].x)[w];
+                        const uint32_t bk = (&wv[bb][k].x)[w];
 #pragma unroll
                         for (int j = 0; j < 8; ++j) a[k][j] = __builtin_popcount(bk & xw[j]);
                     }
@@ -379,11 +549,11 @@ __global__ __launch_bounds__(64) void gemv_bits_kernel(const uint8_t* __restrict
                         int4* dst = reinterpret_cast<int4*>(y) + (static_cast<size_t>(m) * N + n) * G + g;
                         if (n < N && g < G) *dst = make_int4(Pk[0], Pk[1], Pk[2], Pk[3]);
                     } else {
-                        const int id = (coef >> (8 * w)) & 0xFF;
+                        const int id = (coef[bb] >> (8 * w)) & 0xFF;
                         const float4 c = s_cache[2 * id];
-                        const float bb = s_cache[2 * id + 1].x;
+                        const float bb5 = s_cache[2 * id + 1].x;
                         const float S32 = static_cast<float>(xS[bu * 4 + w]);
-                        yacc += bb * S32 + c.x * static_cast<float>(Pk[0]) + c.y * static_cast<float>(Pk[1]) +
+                        yacc += bb5 * S32 + c.x * static_cast<float>(Pk[0]) + c.y * static_cast<float>(Pk[1]) +
                                 c.z * static_cast<float>(Pk[2]) + c.w * static_cast<float>(Pk[3]);
                     }
                 }
@@ -417,24 +587,234 @@ __global__ __launch_bounds__(64) void gemv_bits_kernel(const uint8_t* __restrict
         }
         float* slot = ws_part + (static_cast<size_t>(split) * M + m) * Np + n;
         if (int_out)
-            *reinterpret_cast<int32_t*>(slot) = ipart;
+            store_partial_i(reinterpret_cast<int32_t*>(slot), ipart);
         else
-            *slot = part;
-        if (m == M - 1) {
-            // all tokens of this split are stored: arrive once
-            if (arrive_last(&ws_cnt[t], splits, &s_flag) && n < N) {
-                for (int mm = 0; mm < M; ++mm) {
-                    if (int_out) {
-                        int s = 0;
-                        for (int sp = 0; sp < splits; ++sp)
-                            s += reinterpret_cast<const int32_t*>(ws_part)[(static_cast<size_t>(sp) * M + mm) * Np + n];
-                        reinterpret_cast<int32_t*>(y)[static_cast<size_t>(mm) * N + n] = s;
+            store_partial(slot, part);
+    }
+    if (ACC && FMT != BITQ_TERNARY) return;
+    if (splits == 1) return;
+    // ---- all tokens of this split are stored: arrive once, the last sums
+    if (arrive_last_row(&ws_cnt[n], splits) && n < N) {
+        const size_t stride = static_cast<size_t>(M) * Np;
+        for (int mm = 0; mm < M; ++mm) {
+            const size_t off = static_cast<size_t>(mm) * Np + n;
+            if (ACC)
+                reinterpret_cast<int32_t*>(y)[static_cast<size_t>(mm) * N + n] =
+                    sum_partials<int32_t>(reinterpret_cast<const int32_t*>(ws_part) + off, stride, splits);
+            else
+                y[static_cast<size_t>(mm) * N + n] = sum_partials<float>(ws_part + off, stride, splits);
+        }
+    }
+}
+
+// ================================= AND+popcount GEMV, whole k per workgroup
+// Same arithmetic as gemv_bits_kernel, with a decomposition that needs no
+// hand-off between workgroups: a workgroup (256 threads) owns 16 rows and the
+// whole k range.  Thread (g, r) = (tid / 16, tid % 16) takes row r of the
+// group and the k blocks b = g + 16 j (j < BPL) of each round of 16 BPL
+// blocks; the 16 lanes of a k-group read 16 adjacent rows of a tile (256
+// contiguous bytes per load).  Activation planes and group sums of the round
+// are staged once in LDS; the 16 k-groups' results for a row are added in a
+// fixed order (two lane exchanges, then four waves through LDS).
+template <int FMT, bool ACC, int BPL>
+__global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __restrict__ blob, size_t off_c0,
+                                                           size_t off_c1, const uint8_t* __restrict__ act,
+                                                           size_t act_off_S, size_t act_off_d, int M, int N, int K,
+                                                           int Tb, float* __restrict__ y) {
+    constexpr int P = IntCfg<FMT>::P;
+    constexpr int NBW = 16 * BPL;  // k blocks per round
+    constexpr int BSTR = 36;       // LDS words per block: 32 + 4 padding, so the
+                                   // 4 k-groups of a wave hit disjoint banks
+    __shared__ __attribute__((aligned(16))) uint32_t s_act[NBW * BSTR];
+    __shared__ __attribute__((aligned(16))) int32_t s_S[NBW * 4];
+    __shared__ float4 s_cache[FMT == BITQ_BVSR4 ? 512 : 1];
+    __shared__ float s_red[4][16];
+    __shared__ int32_t s_redi[4][16];
+
+    const int tid = threadIdx.x, r = tid & 15, g = tid >> 4, wave = tid >> 6;
+    const int rg = blockIdx.x;
+    const int t = rg >> 2;                   // 64-row tile
+    const int rowin = 16 * (rg & 3) + r;     // row inside the tile
+    const int n = 64 * t + rowin;
+    const int NB = Tb;
+    const int Kw = Tb * 4;
+    const int rounds = (NB + NBW - 1) / NBW;
+    const uint32_t* __restrict__ aplanes = reinterpret_cast<const uint32_t*>(act);
+    const int32_t* __restrict__ aS = reinterpret_cast<const int32_t*>(act + act_off_S);
+    const float* __restrict__ ad = reinterpret_cast<const float*>(act + act_off_d);
+
+    uint4 wv[BPL][P];
+    uint32_t coef[BPL];
+    auto load_weights = [&](int b_base) {
+#pragma unroll
+        for (int j = 0; j < BPL; ++j) {
+            const int b = min(b_base + g + 16 * j, NB - 1);  // in bounds; surplus skipped below
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                const size_t off = (static_cast<size_t>(t) * Tb + b) * P + p;
+                wv[j][p] = *reinterpret_cast<const uint4*>(blob + kHeaderBytes + off * 1024 + rowin * 16);
+            }
+            coef[j] = 0;
+            if (FMT == BITQ_W2A8 || FMT == BITQ_BVSR4)
+                coef[j] = reinterpret_cast<const uint32_t*>(blob + off_c0)[(static_cast<size_t>(t) * Tb + b) * 64 + rowin];
+        }
+    };
+    // stage the activation planes and sums of blocks [b_base, b_base + NBW)
+    auto stage = [&](int m, int b_base) {
+        const uint4* src = reinterpret_cast<const uint4*>(aplanes + (static_cast<size_t>(m) * Kw + 4 * b_base) * 8);
+        for (int i = tid; i < NBW * 8; i += 256) {  // 8 uint4 per block
+            const int blk = i >> 3, part = i & 7;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (b_base + blk < NB) v = src[i];
+            *reinterpret_cast<uint4*>(&s_act[blk * BSTR + 4 * part]) = v;
+        }
+        for (int i = tid; i < NBW; i += 256) {
+            int4 v = make_int4(0, 0, 0, 0);
+            if (b_base + i < NB) v = *reinterpret_cast<const int4*>(aS + static_cast<size_t>(m) * Kw + 4 * (b_base + i));
+            *reinterpret_cast<int4*>(&s_S[4 * i]) = v;
+        }
+    };
+
+    if (rounds == 1) load_weights(0);
+    if (FMT == BITQ_BVSR4 && !ACC) {
+        const float* cache = reinterpret_cast<const float*>(blob + off_c1);
+        for (int e = tid; e < 256; e += 256) {
+            const float* c = cache + 5 * e;
+            s_cache[2 * e] = make_float4(c[0], c[1], c[2], c[3]);
+            s_cache[2 * e + 1] = make_float4(c[4], 0.0f, 0.0f, 0.0f);
+        }
+    }
+
+    for (int m = 0; m < M; ++m) {
+        float yacc = 0.0f;
+        int tacc[2][8];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) tacc[i][j] = 0;
+
+        for (int rd = 0; rd < rounds; ++rd) {
+            const int b_base = rd * NBW;
+            if (rounds > 1) load_weights(b_base);
+            __syncthreads();  // previous readers of s_act are done
+            stage(m, b_base);
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < BPL; ++j) {
+                const int bl = g + 16 * j;  // block inside the round
+                const int b = b_base + bl;
+                if (b >= NB) continue;
+                const uint32_t* xa = &s_act[bl * BSTR];
+                if (FMT == BITQ_TERNARY) {
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const uint4 x0 = *reinterpret_cast<const uint4*>(xa + 8 * w);
+                        const uint4 x1 = *reinterpret_cast<const uint4*>(xa + 8 * w + 4);
+                        const uint32_t xj[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+                        const uint32_t wp = (&wv[j][0].x)[w], wm = (&wv[j][1].x)[w];
+#pragma unroll
+                        for (int jj = 0; jj < 8; ++jj) {
+                            tacc[0][jj] += __builtin_popcount(wp & xj[jj]);
+                            tacc[1][jj] += __builtin_popcount(wm & xj[jj]);
+                        }
+                    }
+                } else if (FMT == BITQ_W2A8) {
+                    int a[2][8];
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+#pragma unroll
+                        for (int jj = 0; jj < 8; ++jj) a[i][jj] = 0;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const uint4 x0 = *reinterpret_cast<const uint4*>(xa + 8 * w);
+                        const uint4 x1 = *reinterpret_cast<const uint4*>(xa + 8 * w + 4);
+                        const uint32_t xj[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+                        const uint32_t w0 = (&wv[j][0].x)[w], w1 = (&wv[j][1].x)[w];
+#pragma unroll
+                        for (int jj = 0; jj < 8; ++jj) {
+                            a[0][jj] += __builtin_popcount(w0 & xj[jj]);
+                            a[1][jj] += __builtin_popcount(w1 & xj[jj]);
+                        }
+                    }
+                    int t8[8];
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj) t8[jj] = a[0][jj] + 2 * a[1][jj];
+                    const int A = combine_planes(t8);
+                    if (ACC) {
+                        if (n < N) reinterpret_cast<int32_t*>(y)[(static_cast<size_t>(m) * N + n) * NB + b] = A;
                     } else {
-                        float s = 0.0f;
-                        for (int sp = 0; sp < splits; ++sp) s += ws_part[(static_cast<size_t>(sp) * M + mm) * Np + n];
-                        y[static_cast<size_t>(mm) * N + n] = s;
+                        const int4 S4 = *reinterpret_cast<const int4*>(&s_S[4 * bl]);
+                        const int S128 = S4.x + S4.y + S4.z + S4.w;
+                        const float delta = f16_bits_to_f32(coef[j]);
+                        const float z = f16_bits_to_f32(coef[j] >> 16);
+                        yacc += delta * (static_cast<float>(A) - z * static_cast<float>(S128));
+                    }
+                } else {  // BVSR4
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const uint4 x0 = *reinterpret_cast<const uint4*>(xa + 8 * w);
+                        const uint4 x1 = *reinterpret_cast<const uint4*>(xa + 8 * w + 4);
+                        const uint32_t xj[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+                        int Pk[4];
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            const uint32_t bk = (&wv[j][k].x)[w];
+                            int a8[8];
+#pragma unroll
+                            for (int jj = 0; jj < 8; ++jj) a8[jj] = __builtin_popcount(bk & xj[jj]);
+                            Pk[k] = combine_planes(a8);
+                        }
+                        const int gi = 4 * b + w;
+                        if (ACC) {
+                            const int G = K / 32;  // groups of the real (unpadded) K
+                            int4* dst = reinterpret_cast<int4*>(y) + (static_cast<size_t>(m) * N + n) * G + gi;
+                            if (n < N && gi < G) *dst = make_int4(Pk[0], Pk[1], Pk[2], Pk[3]);
+                        } else {
+                            const int id = (coef[j] >> (8 * w)) & 0xFF;
+                            const float4 c = s_cache[2 * id];
+                            const float bo = s_cache[2 * id + 1].x;
+                            const float S32 = static_cast<float>(s_S[4 * bl + w]);
+                            yacc += bo * S32 + c.x * static_cast<float>(Pk[0]) + c.y * static_cast<float>(Pk[1]) +
+                                    c.z * static_cast<float>(Pk[2]) + c.w * static_cast<float>(Pk[3]);
+                        }
                     }
                 }
+            }
+        }
+        if (ACC && FMT != BITQ_TERNARY) continue;  // partials already written per group
+
+        // ---- add the 16 k-groups of each row in a fixed order
+        if (FMT == BITQ_TERNARY && ACC) {
+            int Y[8];
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) Y[jj] = tacc[0][jj] - tacc[1][jj];
+            int v = combine_planes(Y);
+            v += __shfl_xor(v, 16, 64);
+            v += __shfl_xor(v, 32, 64);
+            if ((tid & 63) < 16) s_redi[wave][r] = v;
+            __syncthreads();
+            if (tid < 16 && n < N)
+                reinterpret_cast<int32_t*>(y)[static_cast<size_t>(m) * N + n] =
+                    (s_redi[0][r] + s_redi[1][r]) + (s_redi[2][r] + s_redi[3][r]);
+        } else {
+            float v;
+            if (FMT == BITQ_TERNARY) {
+                int Y[8];
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) Y[jj] = tacc[0][jj] - tacc[1][jj];
+                v = static_cast<float>(combine_planes(Y));  // exact while |Y| < 2^24 (K <= 2^17)
+            } else {
+                v = yacc;
+            }
+            v += __shfl_xor(v, 16, 64);
+            v += __shfl_xor(v, 32, 64);
+            if ((tid & 63) < 16) s_red[wave][r] = v;
+            __syncthreads();
+            if (tid < 16 && n < N) {
+                float tot = (s_red[0][r] + s_red[1][r]) + (s_red[2][r] + s_red[3][r]);
+                if (FMT == BITQ_TERNARY) tot = *reinterpret_cast<const float*>(blob + off_c0) * ad[m] * tot;
+                else tot = ad[m] * tot;
+                y[static_cast<size_t>(m) * N + n] = tot;
             }
         }
     }
@@ -468,31 +848,52 @@ int current_device_is_gfx950(int* is_gfx950) {
 int launch_quantize_act(const void* x, int x_dtype, int M, int K, void* act, void* stream) {
     ActLayout A = act_layout(M, K);
     uint8_t* base = static_cast<uint8_t*>(act);
-    hipLaunchKernelGGL(quant_act_kernel, dim3(M), dim3(256), 0, static_cast<hipStream_t>(stream), x, x_dtype, K,
-                       static_cast<int>(A.Kw), reinterpret_cast<uint32_t*>(base + A.off_planes),
-                       reinterpret_cast<int32_t*>(base + A.off_S), reinterpret_cast<int8_t*>(base + A.off_q),
-                       reinterpret_cast<float*>(base + A.off_d));
+    auto* planes = reinterpret_cast<uint32_t*>(base + A.off_planes);
+    auto* S = reinterpret_cast<int32_t*>(base + A.off_S);
+    auto* q = reinterpret_cast<int8_t*>(base + A.off_q);
+    auto* d = reinterpret_cast<float*>(base + A.off_d);
+    const int Kw = static_cast<int>(A.Kw);
+    if (x_dtype == BITQ_DT_F32)
+        hipLaunchKernelGGL(quant_act_kernel<BITQ_DT_F32>, dim3(M), dim3(256), 0, static_cast<hipStream_t>(stream), x,
+                           K, Kw, planes, S, q, d);
+    else
+        hipLaunchKernelGGL(quant_act_kernel<BITQ_DT_BF16>, dim3(M), dim3(256), 0, static_cast<hipStream_t>(stream), x,
+                           K, Kw, planes, S, q, d);
     return static_cast<int>(hipGetLastError());
 }
 
-template <int P, int KB>
+template <int P, int KB, bool RABIT, int DT>
 static void launch_sign(const bitq_wdesc& d, const Plan& pl, const BlobLayout& L, const void* w, const void* x,
-                        int dt, float* y, void* ws, hipStream_t st) {
+                        float* y, void* ws, hipStream_t st) {
     uint8_t* wsb = static_cast<uint8_t*>(ws);
-    hipLaunchKernelGGL((gemv_sign_kernel<P, KB>), dim3(pl.row_groups, pl.splits), dim3(256), 0, st,
-                       static_cast<const uint8_t*>(w), L.off_c0, L.off_c1, x, dt, d.fmt, d.N, d.K,
-                       static_cast<int>(L.Np), static_cast<int>(L.Tn), static_cast<int>(L.Tb), pl.splits, y,
+    hipLaunchKernelGGL((gemv_sign_kernel<P, KB, RABIT, DT>), dim3(pl.row_groups, pl.splits), dim3(256), 0, st,
+                       static_cast<const uint8_t*>(w), L.off_c0, L.off_c1, x, d.N, d.K, static_cast<int>(L.Np),
+                       static_cast<int>(L.Tn), static_cast<int>(L.Tb), pl.splits, y,
                        reinterpret_cast<float*>(wsb + pl.off_partials),
                        reinterpret_cast<uint32_t*>(wsb + pl.off_counters));
 }
 
-template <int P>
+template <int P, bool RABIT, int DT>
 static void launch_sign_kb(const bitq_wdesc& d, const Plan& pl, const BlobLayout& L, const void* w,
-                           const void* x, int dt, float* y, void* ws, hipStream_t st) {
+                           const void* x, float* y, void* ws, hipStream_t st) {
     switch (pl.blocks_per_split) {
-        case 1: launch_sign<P, 1>(d, pl, L, w, x, dt, y, ws, st); break;
-        case 2: launch_sign<P, 2>(d, pl, L, w, x, dt, y, ws, st); break;
-        default: launch_sign<P, 4>(d, pl, L, w, x, dt, y, ws, st); break;
+        case 1: launch_sign<P, 1, RABIT, DT>(d, pl, L, w, x, y, ws, st); break;
+        case 2: launch_sign<P, 2, RABIT, DT>(d, pl, L, w, x, y, ws, st); break;
+        default: launch_sign<P, 4, RABIT, DT>(d, pl, L, w, x, y, ws, st); break;
+    }
+}
+
+template <int DT>
+static void launch_sign_fmt(const bitq_wdesc& d, const Plan& pl, const BlobLayout& L, const void* w,
+                            const void* x, float* y, void* ws, hipStream_t st) {
+    if (d.fmt == BITQ_SIGN1) {
+        launch_sign_kb<1, false, DT>(d, pl, L, w, x, y, ws, st);
+        return;
+    }
+    switch (d.planes) {
+        case 1: launch_sign_kb<1, true, DT>(d, pl, L, w, x, y, ws, st); break;
+        case 2: launch_sign_kb<2, true, DT>(d, pl, L, w, x, y, ws, st); break;
+        default: launch_sign_kb<3, true, DT>(d, pl, L, w, x, y, ws, st); break;
     }
 }
 
@@ -500,25 +901,57 @@ int launch_gemv_float(const bitq_wdesc& d, const Plan& pl, const void* w, const 
                       void* ws, void* stream) {
     BlobLayout L = blob_layout(d);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    switch (d.planes) {
-        case 1: launch_sign_kb<1>(d, pl, L, w, x, x_dtype, y, ws, st); break;
-        case 2: launch_sign_kb<2>(d, pl, L, w, x, x_dtype, y, ws, st); break;
-        default: launch_sign_kb<3>(d, pl, L, w, x, x_dtype, y, ws, st); break;
-    }
+    if (x_dtype == BITQ_DT_F32)
+        launch_sign_fmt<BITQ_DT_F32>(d, pl, L, w, x, y, ws, st);
+    else
+        launch_sign_fmt<BITQ_DT_BF16>(d, pl, L, w, x, y, ws, st);
     return static_cast<int>(hipGetLastError());
+}
+
+template <int FMT, bool ACC, int KB>
+static void launch_bits_kb(const bitq_wdesc& d, const Plan& pl, const BlobLayout& L, const void* w,
+                           const void* act, int M, float* y, void* ws, hipStream_t st) {
+    ActLayout A = act_layout(M, d.K);
+    uint8_t* wsb = static_cast<uint8_t*>(ws);
+    hipLaunchKernelGGL((gemv_bits_kernel<FMT, ACC, KB>), dim3(pl.row_groups, pl.splits), dim3(64), 0, st,
+                       static_cast<const uint8_t*>(w), L.off_c0, L.off_c1, static_cast<const uint8_t*>(act),
+                       A.off_S, A.off_d, M, d.N, d.K, static_cast<int>(L.Np), static_cast<int>(L.Tn),
+                       static_cast<int>(L.Tb), pl.splits, y, reinterpret_cast<float*>(wsb + pl.off_partials),
+                       reinterpret_cast<uint32_t*>(wsb + pl.off_counters));
 }
 
 template <int FMT, bool ACC>
 static void launch_bits(const bitq_wdesc& d, const Plan& pl, const BlobLayout& L, const void* w, const void* act,
                         int M, float* y, void* ws, hipStream_t st) {
+    switch (pl.blocks_per_split) {
+        case 1: launch_bits_kb<FMT, ACC, 1>(d, pl, L, w, act, M, y, ws, st); break;
+        case 2: launch_bits_kb<FMT, ACC, 2>(d, pl, L, w, act, M, y, ws, st); break;
+        case 4: launch_bits_kb<FMT, ACC, 4>(d, pl, L, w, act, M, y, ws, st); break;
+        default: launch_bits_kb<FMT, ACC, 8>(d, pl, L, w, act, M, y, ws, st); break;
+    }
+}
+
+template <int FMT, bool ACC, int BPL>
+static void launch_nr_bpl(const bitq_wdesc& d, const BlobLayout& L, const void* w, const void* act, int M,
+                          float* y, hipStream_t st) {
     ActLayout A = act_layout(M, d.K);
-    uint8_t* wsb = static_cast<uint8_t*>(ws);
-    hipLaunchKernelGGL((gemv_bits_kernel<FMT, ACC>), dim3(pl.row_groups, pl.splits), dim3(64), 0, st,
+    const int groups = (d.N + 15) / 16;
+    hipLaunchKernelGGL((gemv_bits_nr_kernel<FMT, ACC, BPL>), dim3(groups), dim3(256), 0, st,
                        static_cast<const uint8_t*>(w), L.off_c0, L.off_c1, static_cast<const uint8_t*>(act),
-                       A.off_S, A.off_d, M, d.N, d.K, static_cast<int>(L.Np), static_cast<int>(L.Tn),
-                       static_cast<int>(L.Tb), pl.blocks_per_split, pl.splits, y,
-                       reinterpret_cast<float*>(wsb + pl.off_partials),
-                       reinterpret_cast<uint32_t*>(wsb + pl.off_counters));
+                       A.off_S, A.off_d, M, d.N, d.K, static_cast<int>(L.Tb), y);
+}
+
+template <int FMT, bool ACC>
+static void launch_nr(const bitq_wdesc& d, const Plan& pl, const BlobLayout& L, const void* w, const void* act,
+                      int M, float* y, hipStream_t st) {
+    switch (pl.blocks_per_split) {  // blocks per lane
+        case 1: launch_nr_bpl<FMT, ACC, 1>(d, L, w, act, M, y, st); break;
+        case 2: launch_nr_bpl<FMT, ACC, 2>(d, L, w, act, M, y, st); break;
+        case 3: launch_nr_bpl<FMT, ACC, 3>(d, L, w, act, M, y, st); break;
+        case 4: launch_nr_bpl<FMT, ACC, 4>(d, L, w, act, M, y, st); break;
+        case 6: launch_nr_bpl<FMT, ACC, 6>(d, L, w, act, M, y, st); break;
+        default: launch_nr_bpl<FMT, ACC, 8>(d, L, w, act, M, y, st); break;
+    }
 }
 
 int launch_gemv_int(const bitq_wdesc& d, const Plan& pl, const void* w, const void* act, int M, float* y,
@@ -526,18 +959,19 @@ int launch_gemv_int(const bitq_wdesc& d, const Plan& pl, const void* w, const vo
     BlobLayout L = blob_layout(d);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool acc = (flags & BITQ_F_ACC_INT32) != 0;
+    (void)ws;
     switch (d.fmt) {
         case BITQ_TERNARY:
-            acc ? launch_bits<BITQ_TERNARY, true>(d, pl, L, w, act, M, y, ws, st)
-                : launch_bits<BITQ_TERNARY, false>(d, pl, L, w, act, M, y, ws, st);
+            acc ? launch_nr<BITQ_TERNARY, true>(d, pl, L, w, act, M, y, st)
+                : launch_nr<BITQ_TERNARY, false>(d, pl, L, w, act, M, y, st);
             break;
         case BITQ_W2A8:
-            acc ? launch_bits<BITQ_W2A8, true>(d, pl, L, w, act, M, y, ws, st)
-                : launch_bits<BITQ_W2A8, false>(d, pl, L, w, act, M, y, ws, st);
+            acc ? launch_nr<BITQ_W2A8, true>(d, pl, L, w, act, M, y, st)
+                : launch_nr<BITQ_W2A8, false>(d, pl, L, w, act, M, y, st);
             break;
         default:
-            acc ? launch_bits<BITQ_BVSR4, true>(d, pl, L, w, act, M, y, ws, st)
-                : launch_bits<BITQ_BVSR4, false>(d, pl, L, w, act, M, y, ws, st);
+            acc ? launch_nr<BITQ_BVSR4, true>(d, pl, L, w, act, M, y, st)
+                : launch_nr<BITQ_BVSR4, false>(d, pl, L, w, act, M, y, st);
             break;
     }
     return static_cast<int>(hipGetLastError());

@@ -212,8 +212,9 @@ bitq_status bitq_quantize_act(const void* x_dev, int32_t x_dtype, int32_t M, int
 
 /*
  * Workspace for one bitq_gemv / bitq_gemm_smallM call (device memory, 256-byte
- * aligned).  It holds per-split partial outputs and per-row-tile arrival
- * counters.  The caller zero-fills it once before its first use; every
+ * aligned).  It holds per-split partial outputs and per-row arrival
+ * counters.  The size is 0 when the call needs none (the integer formats,
+ * whose workgroups each cover the whole k range); ws_dev may then be NULL.  The caller zero-fills it once before its first use; every
  * completed call leaves the counters at zero again, so the same workspace is
  * reused without clearing.  Calls that share a workspace must be ordered
  * (same stream); concurrent calls need distinct workspaces.

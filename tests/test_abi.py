@@ -114,13 +114,19 @@ def test_device_entry_points_validate_before_any_device_call():
                              None) == bq.E_ALIGN
     assert bq._lib.bitq_gemv(ctypes.byref(d), good, good + 64, bq.DT_ACT, good, good, ws_need, 0,
                              None) == bq.E_ALIGN
-    assert bq._lib.bitq_gemv(ctypes.byref(d), good, good, bq.DT_ACT, good, good + 8, ws_need, 0,
-                             None) == bq.E_ALIGN
-    # workspace too small, unknown flag
-    assert bq._lib.bitq_gemv(ctypes.byref(d), good, good, bq.DT_ACT, good, good, ws_need - 1, 0,
-                             None) == bq.E_CAPACITY
+    # unknown flag
     assert bq._lib.bitq_gemv(ctypes.byref(d), good, good, bq.DT_ACT, good, good, ws_need, 8,
                              None) == bq.E_ARG
+    # integer formats need no workspace; the float formats do
+    assert ws_need == 0
+    dr = bq.wdesc(bq.RABIT, 4096, 4096)
+    wsr = bq.workspace_size(dr, 1)
+    assert wsr > 0
+    assert bq._lib.bitq_gemv(ctypes.byref(dr), good, good, bq.DT_BF16, good, None, wsr, 0, None) == bq.E_ARG
+    assert bq._lib.bitq_gemv(ctypes.byref(dr), good, good, bq.DT_BF16, good, good + 8, wsr, 0,
+                             None) == bq.E_ALIGN
+    assert bq._lib.bitq_gemv(ctypes.byref(dr), good, good, bq.DT_BF16, good, good, wsr - 1, 0,
+                             None) == bq.E_CAPACITY
     # float formats: M = 1 only, raw activations, no integer flag
     ds = bq.wdesc(bq.RABIT, 128, 256)
     wsn = bq.workspace_size(ds, 1)
