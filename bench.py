@@ -39,6 +39,23 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 ROTATE_BYTES = 1 << 30
+KERNEL_SRC = os.path.join(ROOT, "bit_plane_gemv_amd", "csrc", "bitq_kernels.hip")
+
+# HBM bytes moved per launch of the GEMV kernel, from rocprofv3 counter runs
+# (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0; factors calibrated on a plain copy
+# kernel of known size; profiles/ holds the runs).  Each entry is valid only
+# for the kernel source it was measured on (first 16 hex digits of the
+# sha256 of bitq_kernels.hip); otherwise traffic is reported as null.
+MEASURED_TRAFFIC = {
+    "rabit": {"kernels_sha256_16": "0a1390dae4162546", "bytes_per_launch": 14131200},
+    "w2a8": {"kernels_sha256_16": "0a1390dae4162546", "bytes_per_launch": 14251008},
+}
+
+
+def kernels_sha() -> str:
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
 
 # Algorithmic packed bytes of one layer (planes + coefficients), by format.
 def packed_bytes(fmt: str, N: int, K: int) -> int:
@@ -228,6 +245,10 @@ def main():
         torch.cuda.synchronize()
         gemv_ms = e0.elapsed_time(e1) / K_steps
     achieved = alg_bytes / (gemv_ms * 1e-3) / 1e9
+    traffic = None
+    mt = MEASURED_TRAFFIC.get(args.workload)
+    if mt is not None and mt["kernels_sha256_16"] == kernels_sha():
+        traffic = round(mt["bytes_per_launch"] / (gemv_ms * 1e-3) / 1e9, 2)
 
     out = {
         "metric": "packed-weight GB/s & % HBM peak, bit-plane GEMV 11008x4096 M=1; us/layer",
@@ -249,8 +270,9 @@ def main():
                    "rotating_copies": copies, "rotating_bytes": copies * stride,
                    "graph_replay": graph is not None, "host_wall_s": round(wall, 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "gemv_sign_kernel" if fmt in ("rabit", "sign") else "gemv_bits_kernel",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "traffic_bytes_per_launch": mt["bytes_per_launch"] if traffic is not None else None,
+                     "kernel": "gemv_sign_kernel" if fmt in ("rabit", "sign") else "gemv_bits_nr_kernel",
                      "kernel_us": round(gemv_ms * 1e3, 3)},
         "cpu_baseline": None,
     }

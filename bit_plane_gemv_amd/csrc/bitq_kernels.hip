@@ -105,113 +105,109 @@ __device__ __forceinline__ bool arrive_last_row(uint32_t* row_counter, int split
 }
 
 // ======================================================= activation quantizer
-// One workgroup (256 threads) per token.  [HGF] §1.2: int8 activations with a
-// per-token absmax scale, dequantized with amax/127; [BVSR] intro: online
-// conversion of activations to the bit format.  Arithmetic order fixed for
-// bit-exactness: s = fl32(127/amax) correctly rounded, q = rint(fl32(x*s)).
-// Thread t owns the 32-input words t, t+256, ...: it reads each word's 32
-// activations with 16-byte loads, keeps them for the second pass, and writes
-// the word's 8 planes, its sum and its 32 codes.
+// [HGF] §1.2: int8 activations with a per-token absmax scale, dequantized
+// with amax/127; [BVSR] intro: online conversion of activations to the bit
+// format.  Arithmetic order fixed for bit-exactness: s = fl32(127/amax)
+// correctly rounded, q = clamp(rint(fl32(x*s)), -127, 127), d = fl32(amax/127).
+//
+// Grid (words / 8, M): each workgroup (4 waves) owns 8 consecutive 32-input
+// words of one token.  It first reduces amax over the token's whole row (the
+// row is small and L2-resident, so every workgroup recomputing it is cheaper
+// than a second launch; the same single pass parks the workgroup's own 256
+// inputs in LDS), then each lane quantizes one input and each of the
+// 8 planes of the wave's 64 inputs comes out of one ballot: bit i of the
+// ballot of (q >> j) & 1 is plane j of input i.
 template <int DT>
-__device__ __forceinline__ void load_word(const void* x, size_t row, int K, int w, float (&v)[32]) {
-    const int k0 = 32 * w;
-    if (k0 + 32 <= K) {
-        if (DT == BITQ_DT_F32) {
-            const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(x) + row + k0);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint4 u = p[i];
-                v[4 * i] = __uint_as_float(u.x);
-                v[4 * i + 1] = __uint_as_float(u.y);
-                v[4 * i + 2] = __uint_as_float(u.z);
-                v[4 * i + 3] = __uint_as_float(u.w);
-            }
-        } else {
-            const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + row + k0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint4 u = p[i];
-                const uint32_t a[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    v[8 * i + 2 * j] = __uint_as_float(a[j] << 16);
-                    v[8 * i + 2 * j + 1] = __uint_as_float(a[j] & 0xFFFF0000u);
-                }
-            }
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) v[i] = 0.0f;  // word entirely beyond K (K is a multiple of 32)
-    }
+__device__ __forceinline__ float act_at(const void* x, size_t i) {
+    if (DT == BITQ_DT_F32) return static_cast<const float*>(x)[i];
+    return bf16_to_f32(static_cast<const uint16_t*>(x)[i]);
 }
 
 template <int DT>
 __global__ __launch_bounds__(256) void quant_act_kernel(const void* __restrict__ x, int K, int Kw,
                                                         uint32_t* __restrict__ planes, int32_t* __restrict__ S,
                                                         int8_t* __restrict__ q, float* __restrict__ dq) {
+    constexpr int VEC = (DT == BITQ_DT_F32) ? 4 : 8;  // inputs per 16-byte load
+    constexpr int HOLD = 4;                            // 16-byte loads kept per thread
     __shared__ float s_red[4];
-    const int m = blockIdx.x;
+    __shared__ float s_slice[256];                     // this workgroup's 256 inputs
+    const int m = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t xrow = static_cast<size_t>(m) * K;
-    constexpr int kHold = 2;  // words kept in registers between the passes
-    float v[kHold][32];
+    const uint4* xv = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(x) +
+                                                     xrow * (DT == BITQ_DT_F32 ? 4 : 2));
+    const int nvec = K / VEC;           // K is a multiple of 32
+    const int lo = 256 * blockIdx.x;    // first input of this workgroup
+
+    // ---- one pass over the row: amax, and this workgroup's inputs to LDS
     float amax = 0.0f;
+    auto take = [&](int i, const uint4& u) {
+        const uint32_t a[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-    for (int h = 0; h < kHold; ++h) {
-        const int w = threadIdx.x + 256 * h;
-        if (w < Kw) {
-            load_word<DT>(x, xrow, K, w, v[h]);
-#pragma unroll
-            for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[h][i]));
+        for (int e = 0; e < 4; ++e) {
+            float v0, v1;
+            if (DT == BITQ_DT_F32) {
+                v0 = __uint_as_float(a[e]);
+                amax = fmaxf(amax, fabsf(v0));
+                const int k = i * VEC + e;
+                if (k >= lo && k < lo + 256) s_slice[k - lo] = v0;
+            } else {
+                v0 = __uint_as_float(a[e] << 16);
+                v1 = __uint_as_float(a[e] & 0xFFFF0000u);
+                amax = fmaxf(amax, fmaxf(fabsf(v0), fabsf(v1)));
+                const int k = i * VEC + 2 * e;
+                if (k >= lo && k < lo + 256) {
+                    s_slice[k - lo] = v0;
+                    s_slice[k + 1 - lo] = v1;
+                }
+            }
         }
-    }
-    for (int w = threadIdx.x + 256 * kHold; w < Kw; w += 256) {
-        float t[32];
-        load_word<DT>(x, xrow, K, w, t);
+    };
+    {
+        uint4 hold[HOLD];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(t[i]));
+        for (int h = 0; h < HOLD; ++h) {  // all loads of the first pass in flight together
+            const int i = tid + 256 * h;
+            hold[h] = (i < nvec) ? xv[i] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int h = 0; h < HOLD; ++h)
+            if (tid + 256 * h < nvec) take(tid + 256 * h, hold[h]);
     }
+    for (int i = tid + 256 * HOLD; i < nvec; i += 256) take(i, xv[i]);
     amax = wave_max(amax);
-    if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = amax;
+    if (lane == 0) s_red[wave] = amax;
     __syncthreads();
     amax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-    float s = 0.0f, d = 0.0f;
-    if (amax > 0.0f) {
-        s = __fdiv_rn(127.0f, amax);
-        d = __fdiv_rn(amax, 127.0f);
+    float s = 0.0f;
+    if (amax > 0.0f) s = __fdiv_rn(127.0f, amax);
+    if (blockIdx.x == 0 && tid == 0) dq[m] = (amax > 0.0f) ? __fdiv_rn(amax, 127.0f) : 0.0f;
+
+    // ---- this wave's 64 inputs = words w0 and w0 + 1
+    const int w0 = 8 * blockIdx.x + 2 * wave;
+    if (w0 >= Kw) return;
+    const int k = 32 * w0 + lane;
+    int qi = 0;
+    if (k < K && amax > 0.0f) {
+        const float r = rintf(__fmul_rn(s_slice[k - lo], s));
+        qi = static_cast<int>(fminf(fmaxf(r, -127.0f), 127.0f));
     }
-    for (int w = threadIdx.x, h = 0; w < Kw; w += 256, ++h) {
-        float t[32];
-        if (h < kHold) {
+    q[static_cast<size_t>(m) * (Kw * 32) + k] = static_cast<int8_t>(qi);
+    // planes: lane j (< 8) keeps plane j of word w0, lane 8 + j of word w0 + 1
+    uint32_t mine = 0;
 #pragma unroll
-            for (int i = 0; i < 32; ++i) t[i] = (h == 0) ? v[0][i] : v[1][i];
-        } else {
-            load_word<DT>(x, xrow, K, w, t);
-        }
-        uint32_t pl[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        uint32_t qb[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        int sum = 0;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            int qi = 0;
-            if (amax > 0.0f) {
-                float r = rintf(__fmul_rn(t[i], s));
-                qi = static_cast<int>(fminf(fmaxf(r, -127.0f), 127.0f));
-            }
-            sum += qi;
-            const uint32_t byte = static_cast<uint32_t>(qi) & 0xFFu;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) pl[j] |= ((byte >> j) & 1u) << i;
-            qb[i >> 2] |= byte << (8 * (i & 3));
-        }
-        uint4* pdst = reinterpret_cast<uint4*>(planes + (static_cast<size_t>(m) * Kw + w) * 8);
-        pdst[0] = make_uint4(pl[0], pl[1], pl[2], pl[3]);
-        pdst[1] = make_uint4(pl[4], pl[5], pl[6], pl[7]);
-        S[static_cast<size_t>(m) * Kw + w] = sum;
-        uint4* qdst = reinterpret_cast<uint4*>(q + (static_cast<size_t>(m) * Kw + w) * 32);
-        qdst[0] = make_uint4(qb[0], qb[1], qb[2], qb[3]);
-        qdst[1] = make_uint4(qb[4], qb[5], qb[6], qb[7]);
+    for (int j = 0; j < 8; ++j) {
+        const uint64_t b = __ballot((qi >> j) & 1);
+        if (lane == j) mine = static_cast<uint32_t>(b);
+        if (lane == 8 + j) mine = static_cast<uint32_t>(b >> 32);
     }
-    if (threadIdx.x == 0) dq[m] = d;
+    if (lane < 16) planes[(static_cast<size_t>(m) * Kw + w0) * 8 + lane] = mine;
+    // group sums of the two words: reductions inside each half of the wave
+    int sum = qi;
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) sum += __shfl_xor(sum, o, 64);
+    if (lane == 0) S[static_cast<size_t>(m) * Kw + w0] = sum;
+    if (lane == 32) S[static_cast<size_t>(m) * Kw + w0 + 1] = sum;
 }
 
 // ========================================================= sign-apply GEMV
@@ -853,11 +849,12 @@ int launch_quantize_act(const void* x, int x_dtype, int M, int K, void* act, voi
     auto* q = reinterpret_cast<int8_t*>(base + A.off_q);
     auto* d = reinterpret_cast<float*>(base + A.off_d);
     const int Kw = static_cast<int>(A.Kw);
+    const dim3 grid((Kw + 7) / 8, M);
     if (x_dtype == BITQ_DT_F32)
-        hipLaunchKernelGGL(quant_act_kernel<BITQ_DT_F32>, dim3(M), dim3(256), 0, static_cast<hipStream_t>(stream), x,
+        hipLaunchKernelGGL(quant_act_kernel<BITQ_DT_F32>, grid, dim3(256), 0, static_cast<hipStream_t>(stream), x,
                            K, Kw, planes, S, q, d);
     else
-        hipLaunchKernelGGL(quant_act_kernel<BITQ_DT_BF16>, dim3(M), dim3(256), 0, static_cast<hipStream_t>(stream), x,
+        hipLaunchKernelGGL(quant_act_kernel<BITQ_DT_BF16>, grid, dim3(256), 0, static_cast<hipStream_t>(stream), x,
                            K, Kw, planes, S, q, d);
     return static_cast<int>(hipGetLastError());
 }
