@@ -576,6 +576,9 @@ ActLayout act_layout(int M, int K) {
     return A;
 }
 
+// Rows per workgroup of the integer GEMV (16, 8 or 4).
+constexpr int kIntRowsPerWg = 16;
+
 Plan make_plan(const bitq_wdesc& d, int M) {
     Plan p{};
     const bool lut = (d.fmt == BITQ_SIGN1 || d.fmt == BITQ_RABIT);
@@ -583,9 +586,12 @@ Plan make_plan(const bitq_wdesc& d, int M) {
     const int64_t NB = round_up(d.K, kKBlock) / kKBlock;
     p.M = M;
     if (!lut) {
-        // Integer formats: one workgroup per 16 rows covers the whole k range
-        // (16 k-groups x blocks_per_split blocks per round); no workspace.
-        const int64_t need = (NB + 15) / 16;
+        // Integer formats: one workgroup of 256 lanes per rows_per_wg rows
+        // covers the whole k range (256/rows_per_wg k-groups x
+        // blocks_per_split blocks per round); no workspace.
+        const int rg = kIntRowsPerWg;
+        const int64_t kgroups = 256 / rg;
+        const int64_t need = (NB + kgroups - 1) / kgroups;
         const int sizes[6] = {1, 2, 3, 4, 6, 8};
         p.blocks_per_split = 8;
         for (int sz : sizes)
@@ -594,8 +600,8 @@ Plan make_plan(const bitq_wdesc& d, int M) {
                 break;
             }
         p.waves_per_wg = 4;
-        p.rows_per_wg = 16;
-        p.row_groups = static_cast<int>((d.N + 15) / 16);
+        p.rows_per_wg = rg;
+        p.row_groups = static_cast<int>((d.N + rg - 1) / rg);
         p.splits = 1;
         p.off_partials = p.off_counters = 0;
         p.ws_bytes = 0;

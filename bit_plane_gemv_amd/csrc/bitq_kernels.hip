@@ -414,6 +414,14 @@ struct IntCfg<BITQ_W2A8> { static constexpr int P = 2; };
 template <>
 struct IntCfg<BITQ_BVSR4> { static constexpr int P = 4; };
 
+// popcount(v) + acc as one v_bcnt_u32_b32 (keeps the accumulation a chain
+// of accumulating popcounts instead of separate popcounts plus adds).
+__device__ __forceinline__ int bcnt_acc(uint32_t v, int acc) {
+    int r;
+    asm("v_bcnt_u32_b32 %0, %1, %2" : "=v"(r) : "v"(v), "v"(acc));
+    return r;
+}
+
 // Horner combination of per-plane popcounts: sum_j c_j a_j.
 __device__ __forceinline__ int combine_planes(const int (&a)[8]) {
     int r = -a[7];
@@ -612,25 +620,36 @@ __global__ __launch_bounds__(64) void gemv_bits_kernel(const uint8_t* __restrict
 // contiguous bytes per load).  Activation planes and group sums of the round
 // are staged once in LDS; the 16 k-groups' results for a row are added in a
 // fixed order (two lane exchanges, then four waves through LDS).
-template <int FMT, bool ACC, int BPL>
+template <int FMT, bool ACC, int BPL, int RG, bool ONE>
 __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __restrict__ blob, size_t off_c0,
                                                            size_t off_c1, const uint8_t* __restrict__ act,
                                                            size_t act_off_S, size_t act_off_d, int M, int N, int K,
                                                            int Tb, float* __restrict__ y) {
     constexpr int P = IntCfg<FMT>::P;
-    constexpr int NBW = 16 * BPL;  // k blocks per round
-    constexpr int BSTR = 36;       // LDS words per block: 32 + 4 padding, so the
-                                   // 4 k-groups of a wave hit disjoint banks
-    __shared__ __attribute__((aligned(16))) uint32_t s_act[NBW * BSTR];
-    __shared__ __attribute__((aligned(16))) int32_t s_S[NBW * 4];
+    constexpr int G = 256 / RG;    // k-groups: lanes that share a row
+    constexpr int Q = 64 / RG;     // row groups per 64-row tile
+    constexpr int NBW = G * BPL;   // k blocks per round
+    constexpr int BSTR = 36;       // LDS words per block: 32 + 4 padding, so up to
+                                   // 8 k-groups of a wave hit disjoint banks
+    constexpr int SV = (NBW * 8 + 255) / 256;  // staged uint4 per lane: 8 per block
+    // sized for whole passes of 256 lanes, so that every lane stores (a store
+    // under a condition lets the compiler sink the load next to it)
+    __shared__ __attribute__((aligned(16))) uint32_t s_act[SV * 32 * BSTR];
+    __shared__ __attribute__((aligned(16))) int32_t s_S[(NBW > 256 ? NBW : 256) * 4];
     __shared__ float4 s_cache[FMT == BITQ_BVSR4 ? 512 : 1];
     __shared__ float s_red[4][16];
     __shared__ int32_t s_redi[4][16];
 
-    const int tid = threadIdx.x, r = tid & 15, g = tid >> 4, wave = tid >> 6;
-    const int rg = blockIdx.x;
-    const int t = rg >> 2;                   // 64-row tile
-    const int rowin = 16 * (rg & 3) + r;     // row inside the tile
+    const int tid = threadIdx.x, r = tid % RG, g = tid / RG, wave = tid >> 6;
+    // Workgroup wg runs on XCD wg mod 8 (round-robin dispatch); the Q row
+    // groups of a 64-row tile go to workgroups wg, wg+8, ..., wg+8(Q-1) of one
+    // XCD, so the tile's coefficient lines (64 rows x 4 bytes) are fetched
+    // into a single L2.
+    const int wg = blockIdx.x;
+    const int t = 8 * (wg / (8 * Q)) + (wg & 7);  // 64-row tile
+    const int quarter = (wg >> 3) % Q;
+    if (t >= (N + 63) / 64) return;               // padding workgroups of the last XCD round
+    const int rowin = RG * quarter + r;           // row inside the tile
     const int n = 64 * t + rowin;
     const int NB = Tb;
     const int Kw = Tb * 4;
@@ -641,37 +660,54 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
 
     uint4 wv[BPL][P];
     uint32_t coef[BPL];
+    // uniform 64-bit bases of this tile; per-lane offsets fit in 32 bits
+    const uint8_t* __restrict__ tile_planes = blob + kHeaderBytes + static_cast<size_t>(t) * Tb * P * 1024;
+    const uint32_t* __restrict__ tile_coef = reinterpret_cast<const uint32_t*>(blob + off_c0) + static_cast<size_t>(t) * Tb * 64;
     auto load_weights = [&](int b_base) {
 #pragma unroll
         for (int j = 0; j < BPL; ++j) {
-            const int b = min(b_base + g + 16 * j, NB - 1);  // in bounds; surplus skipped below
+            const int b = min(b_base + g + G * j, NB - 1);  // in bounds; surplus skipped below
 #pragma unroll
             for (int p = 0; p < P; ++p) {
-                const size_t off = (static_cast<size_t>(t) * Tb + b) * P + p;
-                wv[j][p] = *reinterpret_cast<const uint4*>(blob + kHeaderBytes + off * 1024 + rowin * 16);
+                const uint32_t off = static_cast<uint32_t>((b * P + p) * 1024 + rowin * 16);
+                wv[j][p] = *reinterpret_cast<const uint4*>(tile_planes + off);
             }
             coef[j] = 0;
-            if (FMT == BITQ_W2A8 || FMT == BITQ_BVSR4)
-                coef[j] = reinterpret_cast<const uint32_t*>(blob + off_c0)[(static_cast<size_t>(t) * Tb + b) * 64 + rowin];
+            if (FMT == BITQ_W2A8 || FMT == BITQ_BVSR4) coef[j] = tile_coef[static_cast<uint32_t>(b * 64 + rowin)];
         }
     };
-    // stage the activation planes and sums of blocks [b_base, b_base + NBW)
-    auto stage = [&](int m, int b_base) {
+    // Staging of the activation planes and sums of blocks [b_base, b_base +
+    // NBW) into LDS, split into the global loads (into registers) and the LDS
+    // stores, so that the small activation loads can be issued ahead of the
+    // weight stream and land while it is still in flight.
+    uint4 sv[SV];
+    int4 sS;
+    auto stage_load = [&](int m, int b_base) {
         const uint4* src = reinterpret_cast<const uint4*>(aplanes + (static_cast<size_t>(m) * Kw + 4 * b_base) * 8);
-        for (int i = tid; i < NBW * 8; i += 256) {  // 8 uint4 per block
-            const int blk = i >> 3, part = i & 7;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (b_base + blk < NB) v = src[i];
-            *reinterpret_cast<uint4*>(&s_act[blk * BSTR + 4 * part]) = v;
+        const int valid = 8 * min(NBW, NB - b_base);  // uint4 of real blocks in this round
+#pragma unroll
+        for (int v = 0; v < SV; ++v) {
+            const int i = tid + 256 * v;
+            sv[v] = src[min(i, valid - 1)];  // clamped: always in bounds
         }
-        for (int i = tid; i < NBW; i += 256) {
-            int4 v = make_int4(0, 0, 0, 0);
-            if (b_base + i < NB) v = *reinterpret_cast<const int4*>(aS + static_cast<size_t>(m) * Kw + 4 * (b_base + i));
-            *reinterpret_cast<int4*>(&s_S[4 * i]) = v;
+        const int iS = min(tid, min(NBW, NB - b_base) - 1);
+        sS = *reinterpret_cast<const int4*>(aS + static_cast<size_t>(m) * Kw + 4 * (b_base + iS));
+    };
+    // Slots past the last real block receive copies of it (the loads are
+    // clamped); the compute loop skips those blocks.
+    auto stage_store = [&]() {
+#pragma unroll
+        for (int v = 0; v < SV; ++v) {
+            const int i = tid + 256 * v;
+            *reinterpret_cast<uint4*>(&s_act[(i >> 3) * BSTR + 4 * (i & 7)]) = sv[v];
         }
+        *reinterpret_cast<int4*>(&s_S[4 * tid]) = sS;
     };
 
-    if (rounds == 1) load_weights(0);
+    if (ONE) {  // a single round: issue the whole weight stream up front
+        stage_load(0, 0);
+        load_weights(0);
+    }
     if (FMT == BITQ_BVSR4 && !ACC) {
         const float* cache = reinterpret_cast<const float*>(blob + off_c1);
         for (int e = tid; e < 256; e += 256) {
@@ -681,7 +717,9 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
         }
     }
 
-    for (int m = 0; m < M; ++m) {
+    // one activation row; the first is peeled so that its loads need no wait
+    // at a loop header
+    auto pass = [&](int m, bool first) {
         float yacc = 0.0f;
         int tacc[2][8];
 #pragma unroll
@@ -689,15 +727,20 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
 #pragma unroll
             for (int j = 0; j < 8; ++j) tacc[i][j] = 0;
 
-        for (int rd = 0; rd < rounds; ++rd) {
+        for (int rd = 0; rd < (ONE ? 1 : rounds); ++rd) {
             const int b_base = rd * NBW;
-            if (rounds > 1) load_weights(b_base);
-            __syncthreads();  // previous readers of s_act are done
-            stage(m, b_base);
+            if (!ONE) {
+                stage_load(m, b_base);
+                load_weights(b_base);
+            } else if (!first) {
+                stage_load(m, b_base);
+            }
+            if (!first || rd > 0) __syncthreads();  // previous readers of s_act are done
+            stage_store();
             __syncthreads();
 #pragma unroll
             for (int j = 0; j < BPL; ++j) {
-                const int bl = g + 16 * j;  // block inside the round
+                const int bl = g + G * j;  // block inside the round
                 const int b = b_base + bl;
                 if (b >= NB) continue;
                 const uint32_t* xa = &s_act[bl * BSTR];
@@ -710,8 +753,8 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
                         const uint32_t wp = (&wv[j][0].x)[w], wm = (&wv[j][1].x)[w];
 #pragma unroll
                         for (int jj = 0; jj < 8; ++jj) {
-                            tacc[0][jj] += __builtin_popcount(wp & xj[jj]);
-                            tacc[1][jj] += __builtin_popcount(wm & xj[jj]);
+                            tacc[0][jj] = bcnt_acc(wp & xj[jj], tacc[0][jj]);
+                            tacc[1][jj] = bcnt_acc(wm & xj[jj], tacc[1][jj]);
                         }
                     }
                 } else if (FMT == BITQ_W2A8) {
@@ -728,8 +771,8 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
                         const uint32_t w0 = (&wv[j][0].x)[w], w1 = (&wv[j][1].x)[w];
 #pragma unroll
                         for (int jj = 0; jj < 8; ++jj) {
-                            a[0][jj] += __builtin_popcount(w0 & xj[jj]);
-                            a[1][jj] += __builtin_popcount(w1 & xj[jj]);
+                            a[0][jj] = bcnt_acc(w0 & xj[jj], a[0][jj]);
+                            a[1][jj] = bcnt_acc(w1 & xj[jj], a[1][jj]);
                         }
                     }
                     int t8[8];
@@ -757,7 +800,7 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
                             const uint32_t bk = (&wv[j][k].x)[w];
                             int a8[8];
 #pragma unroll
-                            for (int jj = 0; jj < 8; ++jj) a8[jj] = __builtin_popcount(bk & xj[jj]);
+                            for (int jj = 0; jj < 8; ++jj) a8[jj] = bcnt_acc(bk & xj[jj], 0);
                             Pk[k] = combine_planes(a8);
                         }
                         const int gi = 4 * b + w;
@@ -777,19 +820,19 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
                 }
             }
         }
-        if (ACC && FMT != BITQ_TERNARY) continue;  // partials already written per group
+        if (ACC && FMT != BITQ_TERNARY) return;  // partials already written per group
 
-        // ---- add the 16 k-groups of each row in a fixed order
+        // ---- add the G k-groups of each row in a fixed order
         if (FMT == BITQ_TERNARY && ACC) {
             int Y[8];
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) Y[jj] = tacc[0][jj] - tacc[1][jj];
             int v = combine_planes(Y);
-            v += __shfl_xor(v, 16, 64);
-            v += __shfl_xor(v, 32, 64);
-            if ((tid & 63) < 16) s_redi[wave][r] = v;
+#pragma unroll
+            for (int sh = RG; sh < 64; sh *= 2) v += __shfl_xor(v, sh, 64);
+            if ((tid & 63) < RG) s_redi[wave][r] = v;
             __syncthreads();
-            if (tid < 16 && n < N)
+            if (tid < RG && n < N)
                 reinterpret_cast<int32_t*>(y)[static_cast<size_t>(m) * N + n] =
                     (s_redi[0][r] + s_redi[1][r]) + (s_redi[2][r] + s_redi[3][r]);
         } else {
@@ -802,18 +845,20 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
             } else {
                 v = yacc;
             }
-            v += __shfl_xor(v, 16, 64);
-            v += __shfl_xor(v, 32, 64);
-            if ((tid & 63) < 16) s_red[wave][r] = v;
+#pragma unroll
+            for (int sh = RG; sh < 64; sh *= 2) v += __shfl_xor(v, sh, 64);
+            if ((tid & 63) < RG) s_red[wave][r] = v;
             __syncthreads();
-            if (tid < 16 && n < N) {
+            if (tid < RG && n < N) {
                 float tot = (s_red[0][r] + s_red[1][r]) + (s_red[2][r] + s_red[3][r]);
                 if (FMT == BITQ_TERNARY) tot = *reinterpret_cast<const float*>(blob + off_c0) * ad[m] * tot;
                 else tot = ad[m] * tot;
                 y[static_cast<size_t>(m) * N + n] = tot;
             }
         }
-    }
+    };
+    pass(0, true);
+    for (int m = 1; m < M; ++m) pass(m, false);
 }
 
 // =============================================================== launchers
@@ -928,26 +973,40 @@ static void launch_bits(const bitq_wdesc& d, const Plan& pl, const BlobLayout& L
     }
 }
 
-template <int FMT, bool ACC, int BPL>
+template <int FMT, bool ACC, int BPL, int RG>
 static void launch_nr_bpl(const bitq_wdesc& d, const BlobLayout& L, const void* w, const void* act, int M,
                           float* y, hipStream_t st) {
     ActLayout A = act_layout(M, d.K);
-    const int groups = (d.N + 15) / 16;
-    hipLaunchKernelGGL((gemv_bits_nr_kernel<FMT, ACC, BPL>), dim3(groups), dim3(256), 0, st,
-                       static_cast<const uint8_t*>(w), L.off_c0, L.off_c1, static_cast<const uint8_t*>(act),
-                       A.off_S, A.off_d, M, d.N, d.K, static_cast<int>(L.Tb), y);
+    // 64/RG row groups per 64-row tile, tiles dealt round-robin to the 8 XCDs:
+    // the grid is padded to whole rounds of 8 tiles (extra workgroups exit)
+    const int tiles = static_cast<int>(L.Tn);
+    const int groups = 8 * (64 / RG) * ((tiles + 7) / 8);
+    const bool one = L.Tb <= (256 / RG) * BPL;  // the whole k range in one round
+    auto kern = one ? gemv_bits_nr_kernel<FMT, ACC, BPL, RG, true> : gemv_bits_nr_kernel<FMT, ACC, BPL, RG, false>;
+    hipLaunchKernelGGL(kern, dim3(groups), dim3(256), 0, st, static_cast<const uint8_t*>(w), L.off_c0, L.off_c1,
+                       static_cast<const uint8_t*>(act), A.off_S, A.off_d, M, d.N, d.K, static_cast<int>(L.Tb), y);
+}
+
+template <int FMT, bool ACC, int RG>
+static void launch_nr_rg(const bitq_wdesc& d, const Plan& pl, const BlobLayout& L, const void* w,
+                         const void* act, int M, float* y, hipStream_t st) {
+    switch (pl.blocks_per_split) {  // blocks per lane
+        case 1: launch_nr_bpl<FMT, ACC, 1, RG>(d, L, w, act, M, y, st); break;
+        case 2: launch_nr_bpl<FMT, ACC, 2, RG>(d, L, w, act, M, y, st); break;
+        case 3: launch_nr_bpl<FMT, ACC, 3, RG>(d, L, w, act, M, y, st); break;
+        case 4: launch_nr_bpl<FMT, ACC, 4, RG>(d, L, w, act, M, y, st); break;
+        case 6: launch_nr_bpl<FMT, ACC, 6, RG>(d, L, w, act, M, y, st); break;
+        default: launch_nr_bpl<FMT, ACC, 8, RG>(d, L, w, act, M, y, st); break;
+    }
 }
 
 template <int FMT, bool ACC>
 static void launch_nr(const bitq_wdesc& d, const Plan& pl, const BlobLayout& L, const void* w, const void* act,
                       int M, float* y, hipStream_t st) {
-    switch (pl.blocks_per_split) {  // blocks per lane
-        case 1: launch_nr_bpl<FMT, ACC, 1>(d, L, w, act, M, y, st); break;
-        case 2: launch_nr_bpl<FMT, ACC, 2>(d, L, w, act, M, y, st); break;
-        case 3: launch_nr_bpl<FMT, ACC, 3>(d, L, w, act, M, y, st); break;
-        case 4: launch_nr_bpl<FMT, ACC, 4>(d, L, w, act, M, y, st); break;
-        case 6: launch_nr_bpl<FMT, ACC, 6>(d, L, w, act, M, y, st); break;
-        default: launch_nr_bpl<FMT, ACC, 8>(d, L, w, act, M, y, st); break;
+    switch (pl.rows_per_wg) {  // rows per workgroup
+        case 4: launch_nr_rg<FMT, ACC, 4>(d, pl, L, w, act, M, y, st); break;
+        case 8: launch_nr_rg<FMT, ACC, 8>(d, pl, L, w, act, M, y, st); break;
+        default: launch_nr_rg<FMT, ACC, 16>(d, pl, L, w, act, M, y, st); break;
     }
 }
 
