@@ -422,6 +422,19 @@ __device__ __forceinline__ int bcnt_acc(uint32_t v, int acc) {
     return r;
 }
 
+// Workgroup barrier that first waits until at most N vector-memory loads of
+// this wave are still outstanding (loads retire in issue order, so every load
+// issued before the last N has landed, including copies into LDS) and all LDS
+// accesses are done.  Loads issued after the copies can stay in flight.
+template <int N>
+__device__ __forceinline__ void barrier_after_loads() {
+    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));  // vmcnt(N) expcnt(7) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Horner combination of per-plane popcounts: sum_j c_j a_j.
 __device__ __forceinline__ int combine_planes(const int (&a)[8]) {
     int r = -a[7];
@@ -631,11 +644,14 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
     constexpr int NBW = G * BPL;   // k blocks per round
     constexpr int BSTR = 36;       // LDS words per block: 32 + 4 padding, so up to
                                    // 8 k-groups of a wave hit disjoint banks
-    constexpr int SV = (NBW * 8 + 255) / 256;  // staged uint4 per lane: 8 per block
-    // sized for whole passes of 256 lanes, so that every lane stores (a store
-    // under a condition lets the compiler sink the load next to it)
-    __shared__ __attribute__((aligned(16))) uint32_t s_act[SV * 32 * BSTR];
-    __shared__ __attribute__((aligned(16))) int32_t s_S[(NBW > 256 ? NBW : 256) * 4];
+    // Activation staging goes straight from global memory into LDS
+    // (global_load_lds_dwordx4: lane l of a wave fills the 16-byte slot l of
+    // the wave's destination), in whole passes of 256 lanes.  A block takes 9
+    // slots: its 8 plane uint4 and one slot of padding.
+    constexpr int SLOT_PASSES = (NBW * 9 + 255) / 256;
+    constexpr int S_PASSES = (NBW + 255) / 256;
+    __shared__ __attribute__((aligned(16))) uint32_t s_act[SLOT_PASSES * 256 * 4];
+    __shared__ __attribute__((aligned(16))) int32_t s_S[S_PASSES * 256 * 4];
     __shared__ float4 s_cache[FMT == BITQ_BVSR4 ? 512 : 1];
     __shared__ float s_red[4][16];
     __shared__ int32_t s_redi[4][16];
@@ -663,7 +679,7 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
     // uniform 64-bit bases of this tile; per-lane offsets fit in 32 bits
     const uint8_t* __restrict__ tile_planes = blob + kHeaderBytes + static_cast<size_t>(t) * Tb * P * 1024;
     const uint32_t* __restrict__ tile_coef = reinterpret_cast<const uint32_t*>(blob + off_c0) + static_cast<size_t>(t) * Tb * 64;
-    auto load_weights = [&](int b_base) {
+    auto load_weights = [&](int b_base) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < BPL; ++j) {
             const int b = min(b_base + g + G * j, NB - 1);  // in bounds; surplus skipped below
@@ -677,49 +693,51 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
         }
     };
     // Staging of the activation planes and sums of blocks [b_base, b_base +
-    // NBW) into LDS, split into the global loads (into registers) and the LDS
-    // stores, so that the small activation loads can be issued ahead of the
-    // weight stream and land while it is still in flight.
-    uint4 sv[SV];
-    int4 sS;
-    auto stage_load = [&](int m, int b_base) {
-        const uint4* src = reinterpret_cast<const uint4*>(aplanes + (static_cast<size_t>(m) * Kw + 4 * b_base) * 8);
-        const int valid = 8 * min(NBW, NB - b_base);  // uint4 of real blocks in this round
+    // NBW) into LDS.  The copies complete asynchronously (counted like any
+    // other load), so they are issued ahead of the weight stream and land
+    // while it is still in flight.  Slots past the last real block receive
+    // copies of it (clamped addresses); the compute loop skips those blocks.
+    auto stage = [&](int m, int b_base) __attribute__((always_inline)) {
+        const uint4* src = reinterpret_cast<const uint4*>(aplanes) + (static_cast<size_t>(m) * Kw + 4 * b_base) * 2;
+        const int last = min(NBW, NB - b_base) - 1;  // last real block of the round
 #pragma unroll
-        for (int v = 0; v < SV; ++v) {
-            const int i = tid + 256 * v;
-            sv[v] = src[min(i, valid - 1)];  // clamped: always in bounds
+        for (int v = 0; v < SLOT_PASSES; ++v) {
+            const int slot = tid + 256 * v;
+            const int blk = slot / 9, part = slot - 9 * blk;
+            __builtin_amdgcn_global_load_lds(src + 8 * min(blk, last) + min(part, 7),
+                                             reinterpret_cast<uint4*>(s_act) + 256 * v + 64 * wave, 16, 0, 0);
         }
-        const int iS = min(tid, min(NBW, NB - b_base) - 1);
-        sS = *reinterpret_cast<const int4*>(aS + static_cast<size_t>(m) * Kw + 4 * (b_base + iS));
-    };
-    // Slots past the last real block receive copies of it (the loads are
-    // clamped); the compute loop skips those blocks.
-    auto stage_store = [&]() {
+        const int4* srcS = reinterpret_cast<const int4*>(aS + static_cast<size_t>(m) * Kw + 4 * b_base);
 #pragma unroll
-        for (int v = 0; v < SV; ++v) {
-            const int i = tid + 256 * v;
-            *reinterpret_cast<uint4*>(&s_act[(i >> 3) * BSTR + 4 * (i & 7)]) = sv[v];
-        }
-        *reinterpret_cast<int4*>(&s_S[4 * tid]) = sS;
+        for (int v = 0; v < S_PASSES; ++v)
+            __builtin_amdgcn_global_load_lds(srcS + min(tid + 256 * v, last),
+                                             reinterpret_cast<int4*>(s_S) + 256 * v + 64 * wave, 16, 0, 0);
     };
 
-    if (ONE) {  // a single round: issue the whole weight stream up front
-        stage_load(0, 0);
-        load_weights(0);
-    }
+    // Issue order: coefficient cache (BVSR), activation copies, then the
+    // weight stream; kWeightLoads loads follow the copies, so the barrier
+    // below waits for the copies without waiting for the weights.
+    constexpr int kWeightLoads = BPL * P + ((FMT == BITQ_W2A8 || FMT == BITQ_BVSR4) ? BPL : 0);
     if (FMT == BITQ_BVSR4 && !ACC) {
+        // cache entry e (c0..c3, b; 5 floats) -> LDS floats 8e..8e+4 by 4-byte
+        // copies; floats 8e+5..8e+7 are never read (they get copies of b)
         const float* cache = reinterpret_cast<const float*>(blob + off_c1);
-        for (int e = tid; e < 256; e += 256) {
-            const float* c = cache + 5 * e;
-            s_cache[2 * e] = make_float4(c[0], c[1], c[2], c[3]);
-            s_cache[2 * e + 1] = make_float4(c[4], 0.0f, 0.0f, 0.0f);
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+            const int slot = tid + 256 * v, e = slot >> 3, f = slot & 7;
+            __builtin_amdgcn_global_load_lds(cache + 5 * e + min(f, 4),
+                                             reinterpret_cast<float*>(s_cache) + 256 * v + 64 * wave, 4, 0, 0);
         }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    if (ONE) stage(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (ONE) load_weights(0);
+    __builtin_amdgcn_sched_barrier(0);
 
     // one activation row; the first is peeled so that its loads need no wait
     // at a loop header
-    auto pass = [&](int m, bool first) {
+    auto pass = [&](int m, bool first) __attribute__((always_inline)) {
         float yacc = 0.0f;
         int tacc[2][8];
 #pragma unroll
@@ -729,21 +747,30 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
 
         for (int rd = 0; rd < (ONE ? 1 : rounds); ++rd) {
             const int b_base = rd * NBW;
-            if (!ONE) {
-                stage_load(m, b_base);
-                load_weights(b_base);
-            } else if (!first) {
-                stage_load(m, b_base);
-            }
             if (!first || rd > 0) __syncthreads();  // previous readers of s_act are done
-            stage_store();
-            __syncthreads();
+            if (!ONE) {
+                stage(m, b_base);
+                __builtin_amdgcn_sched_barrier(0);
+                load_weights(b_base);
+                __builtin_amdgcn_sched_barrier(0);
+                barrier_after_loads<kWeightLoads>();
+            } else if (first) {
+                barrier_after_loads<kWeightLoads>();  // copies issued in the prologue
+            } else {
+                stage(m, b_base);
+                barrier_after_loads<0>();
+            }
 #pragma unroll
             for (int j = 0; j < BPL; ++j) {
                 const int bl = g + G * j;  // block inside the round
                 const int b = b_base + bl;
                 if (b >= NB) continue;
                 const uint32_t* xa = &s_act[bl * BSTR];
+                // Use of this block's coefficient word starts here: without the
+                // empty asm the compiler hoists its decoding, and the wait for
+                // it, above the barrier, ahead of the whole weight stream.
+                uint32_t cw = coef[j];
+                asm volatile("" : "+v"(cw));
                 if (FMT == BITQ_TERNARY) {
 #pragma unroll
                     for (int w = 0; w < 4; ++w) {
@@ -784,8 +811,8 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
                     } else {
                         const int4 S4 = *reinterpret_cast<const int4*>(&s_S[4 * bl]);
                         const int S128 = S4.x + S4.y + S4.z + S4.w;
-                        const float delta = f16_bits_to_f32(coef[j]);
-                        const float z = f16_bits_to_f32(coef[j] >> 16);
+                        const float delta = f16_bits_to_f32(cw);
+                        const float z = f16_bits_to_f32(cw >> 16);
                         yacc += delta * (static_cast<float>(A) - z * static_cast<float>(S128));
                     }
                 } else {  // BVSR4
@@ -809,7 +836,7 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
                             int4* dst = reinterpret_cast<int4*>(y) + (static_cast<size_t>(m) * N + n) * G + gi;
                             if (n < N && gi < G) *dst = make_int4(Pk[0], Pk[1], Pk[2], Pk[3]);
                         } else {
-                            const int id = (coef[j] >> (8 * w)) & 0xFF;
+                            const int id = (cw >> (8 * w)) & 0xFF;
                             const float4 c = s_cache[2 * id];
                             const float bo = s_cache[2 * id + 1].x;
                             const float S32 = static_cast<float>(s_S[4 * bl + w]);
