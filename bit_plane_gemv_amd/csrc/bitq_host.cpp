@@ -103,6 +103,8 @@ bitq_status check_desc(const bitq_wdesc* d) {
     if (d->N < 1 || d->N > (1 << 24)) return fail(BITQ_E_SHAPE, "N=%d out of range [1, 2^24]", d->N);
     if (d->K < 32 || d->K > (1 << 20)) return fail(BITQ_E_SHAPE, "K=%d out of range [32, 2^20]", d->K);
     if (d->K % 32) return fail(BITQ_E_SHAPE, "K=%d is not a multiple of 32", d->K);
+    if ((d->fmt == BITQ_SIGN1 || d->fmt == BITQ_RABIT) && d->K > kMaxFloatK)
+        return fail(BITQ_E_SHAPE, "K=%d: SIGN1/RABIT support K <= %d", d->K, kMaxFloatK);
     switch (d->fmt) {
         case BITQ_SIGN1:
             if (d->planes != 1 || d->group != 0)
@@ -284,6 +286,21 @@ bitq_status pack_impl(const bitq_wdesc& d, const bitq_logical* s, void* dstv, si
             break;
     }
     pack_coefficients(d, L, s, dst);
+    if (d.fmt == BITQ_SIGN1 || d.fmt == BITQ_RABIT) {
+        // header bound max_k |h_p[k]| (1 for SIGN1): the float GEMV scales its
+        // split-k fixed-point sums from it
+        float hb[3] = {0.0f, 0.0f, 0.0f};
+        for (int64_t p = 0; p < L.P; ++p) {
+            double m = d.fmt == BITQ_SIGN1 ? 1.0 : 0.0;
+            if (d.fmt == BITQ_RABIT)
+                for (int64_t k = 0; k < K; ++k) {
+                    const double a = std::fabs(f16_to_f64(s->h[p * K + k]));
+                    m = (a > m || a != a) ? a : m;  // NaN propagates
+                }
+            hb[p] = static_cast<float>(m);
+        }
+        std::memcpy(dst + kHdrHBound, hb, sizeof(hb));
+    }
     return ok();
 }
 
@@ -576,9 +593,6 @@ ActLayout act_layout(int M, int K) {
     return A;
 }
 
-// Rows per workgroup of the integer GEMV (16, 8 or 4).
-constexpr int kIntRowsPerWg = 16;
-
 Plan make_plan(const bitq_wdesc& d, int M) {
     Plan p{};
     const bool lut = (d.fmt == BITQ_SIGN1 || d.fmt == BITQ_RABIT);
@@ -589,7 +603,10 @@ Plan make_plan(const bitq_wdesc& d, int M) {
         // Integer formats: one workgroup of 256 lanes per rows_per_wg rows
         // covers the whole k range (256/rows_per_wg k-groups x
         // blocks_per_split blocks per round); no workspace.
-        const int rg = kIntRowsPerWg;
+        // Rows per workgroup (16 or 8): 8 rows double the waves of layers
+        // with fewer than 16384 rows, which keeps more waves per SIMD to hide
+        // the popcount chains (measured faster on every such layer shape).
+        const int rg = d.N >= 16384 ? 16 : 8;
         const int64_t kgroups = 256 / rg;
         const int64_t need = (NB + kgroups - 1) / kgroups;
         const int sizes[6] = {1, 2, 3, 4, 6, 8};
@@ -610,17 +627,18 @@ Plan make_plan(const bitq_wdesc& d, int M) {
     p.waves_per_wg = lut ? 4 : 1;
     p.rows_per_wg = kRowTile * p.waves_per_wg;
     p.row_groups = static_cast<int>((Np + p.rows_per_wg - 1) / p.rows_per_wg);
-    // Blocks per split are compile-time variants of the kernels (1, 2, 4, and
-    // 8 for the integer kernels): take the largest that still gives at least
-    // `target` workgroups.
-    const int64_t target = lut ? 512 : 1024;
-    int kb = lut ? 4 : 8;
-    while (kb > 1 && p.row_groups * ((NB + kb - 1) / kb) < target) kb >>= 1;
+    // Blocks per split are compile-time variants of the kernel (1, 2, 4, 8):
+    // the largest of 1, 2, 4 that still gives at least 512 workgroups, and
+    // never more than 63 splits (the split-k word counts arrivals in 6 bits).
+    const int64_t target = 512;
+    int kb = 4;
+    while (kb > 1 && p.row_groups * ((NB + kb - 1) / kb) < target && (NB + kb / 2 - 1) / (kb / 2) <= 63) kb >>= 1;
+    while ((NB + kb - 1) / kb > 63) kb *= 2;  // K > 32256: 8 blocks per split (K <= 64512, checked)
     p.blocks_per_split = kb;
     p.splits = static_cast<int>((NB + p.blocks_per_split - 1) / p.blocks_per_split);
     p.off_partials = 0;
-    p.off_counters = align256(static_cast<size_t>(p.splits) * M * Np * 4);
-    p.ws_bytes = align256(p.off_counters + static_cast<size_t>(Np) * 4);  // one counter per row
+    p.off_counters = 0;
+    p.ws_bytes = p.splits > 1 ? align256(static_cast<size_t>(M) * Np * 8) : 0;  // one split-k word per row
     return p;
 }
 

@@ -13,6 +13,8 @@ constexpr int kRowTile = 64;      // rows per tile = lanes per wave
 constexpr int kKBlock = 128;      // inputs per k block = 4 words per row
 constexpr int kHeaderBytes = 256;
 constexpr uint32_t kMagic = 0x51544942u;
+constexpr int kHdrHBound = 72;    // header: f32 [3] max_k |h_p[k]| (SIGN1: 1)
+constexpr int kMaxFloatK = 63 * 8 * kKBlock;  // float formats: <= 63 splits of <= 8 k blocks
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -42,8 +44,8 @@ struct Plan {
     int blocks_per_split;  // k blocks (128 inputs) per workgroup
     int splits;            // ceil((Kp/128) / blocks_per_split)
     int M;
-    size_t off_partials;   // f32 [splits][M][Np]
-    size_t off_counters;   // u32 [Np]: per-row arrival counters
+    size_t off_partials;   // float formats: u64 [Np] split-k words (count + fixed-point sum)
+    size_t off_counters;   // unused (0)
     size_t ws_bytes;
 };
 Plan make_plan(const bitq_wdesc& d, int M);

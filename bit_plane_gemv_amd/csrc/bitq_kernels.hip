@@ -94,6 +94,21 @@ __device__ __forceinline__ T sum_partials(const T* p, size_t stride, int count) 
     return s;
 }
 
+// Per-wave arrival after the wave's partial stores (one atomic per wave on
+// the counter of its 64-row tile): true, in every lane, for the wave of the
+// last split to arrive, which then resets the counter to zero.
+__device__ __forceinline__ bool arrive_last_wave(uint32_t* tile_counter, int splits) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are complete
+    uint32_t prev = 0;
+    if ((threadIdx.x & 63) == 0)
+        prev = __hip_atomic_fetch_add(tile_counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    prev = __builtin_amdgcn_readfirstlane(prev);
+    const bool last = prev == static_cast<uint32_t>(splits - 1);
+    if (last && (threadIdx.x & 63) == 0)
+        __hip_atomic_store(tile_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return last;
+}
+
 // Per-lane arrival after this lane's partial stores: true for the last split
 // of the lane's row (whose counter is then reset to zero).
 __device__ __forceinline__ bool arrive_last_row(uint32_t* row_counter, int splits) {
@@ -247,15 +262,61 @@ __device__ __forceinline__ uint32_t nib_addr(uint32_t w, int byte) {
     }
 }
 
+// Split-k hand-off of the float GEMV: one 64-bit device-scope atomic add per
+// row and split.  Each split turns its partial p into the fixed-point integer
+// v = rint(p 2^S) (S per row, below) and adds (1 << 58) + v to the row's
+// word, so the top bits count arrivals and the rest hold the exact integer
+// sum.  Integer addition is exact and associative, so the total does not
+// depend on the order in which splits arrive (deterministic output).  The
+// add returns the previous word: the split that sees splits - 1 arrivals in
+// it is the last, already holds the whole sum, writes y and resets the word.
+// S comes from a bound every split of the row computes identically:
+//   |y_n| <= B_n = sum_p |g_p[n]| max_k |h_p[k]| sum_k |x_k|
+// (max |h_p| is stored in the blob header), with 2^52 >= B_n 2^S, so
+// |v| and every partial sum stay below 2^53 (the count field starts at bit
+// 58; at most 63 splits) and the rounding error is at most splits/2 units of 2^-S, i.e. a
+// relative 2^-52 of B_n per split.  A non-finite bound (inf/NaN in x, g or h)
+// makes the row NaN.
+__device__ __forceinline__ void split_k_add(unsigned long long* word, float part, float bound, int splits,
+                                            float* y_n) {
+    const bool finite = bound <= 3.402823466e38f;  // false for inf and NaN
+    int e = 0;
+    if (finite && bound > 0.0f) (void)frexpf(bound, &e);  // bound < 2^e
+    const int S = 52 - e;
+    const long long v = finite ? static_cast<long long>(rint(ldexp(static_cast<double>(part), S))) : 0;
+    const unsigned long long add = (1ull << 58) + static_cast<unsigned long long>(v);
+    const unsigned long long prev = __hip_atomic_fetch_add(word, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // prev = c 2^58 + V (mod 2^64) with |V| < 2^57: c = (prev + 2^57) >> 58
+    const unsigned long long arrived = (prev + (1ull << 57)) >> 58;
+    if (arrived != static_cast<unsigned long long>(splits - 1)) return;
+    const long long total = static_cast<long long>(prev + add - (static_cast<unsigned long long>(splits) << 58));
+    *y_n = finite ? static_cast<float>(ldexp(static_cast<double>(total), -S)) : __builtin_nanf("");
+    __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int DT>
+__device__ __forceinline__ float abs_sum8(uint4 v) {  // |.| summed over 8 bf16 or 4 f32 inputs
+    if (DT == BITQ_DT_F32)
+        return (fabsf(__uint_as_float(v.x)) + fabsf(__uint_as_float(v.y))) +
+               (fabsf(__uint_as_float(v.z)) + fabsf(__uint_as_float(v.w)));
+    float s = 0.0f;
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s += fabsf(__uint_as_float(u[i] << 16)) + fabsf(__uint_as_float(u[i] & 0xFFFF0000u));
+    return s;
+}
+
 template <int P, int KB, bool RABIT, int DT>
 __global__ __launch_bounds__(256) void gemv_sign_kernel(const uint8_t* __restrict__ blob, size_t off_c0,
                                                         size_t off_c1, const void* __restrict__ x, int N, int K,
                                                         int Np, int Tn, int Tb, int splits, float* __restrict__ y,
-                                                        float* __restrict__ ws_part, uint32_t* __restrict__ ws_cnt) {
-    constexpr int CH = KB * 32;          // 4-input chunks in the k slice
-    constexpr int NT = CH * P;           // tables in the k slice
+                                                        unsigned long long* __restrict__ ws_acc) {
+    constexpr int CH = KB * 32;            // 4-input chunks in the k slice
+    constexpr int NT = CH * P;             // tables in the k slice
     constexpr int TPT = (NT + 255) / 256;  // tables per thread
-    __shared__ float4 lut4[NT * 4];      // [chunk][plane][16 floats]
+    constexpr int XPT = 8;                 // uint4 of x per thread for sum |x| (more: a loop)
+    __shared__ float4 lut4[NT * 4];        // [chunk][plane][16 floats]
+    __shared__ float s_xsum[4];
     const int split = blockIdx.y;
     const int k0 = split * KB * kKBlock;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -263,13 +324,41 @@ __global__ __launch_bounds__(256) void gemv_sign_kernel(const uint8_t* __restric
     const int n = t * kRowTile + lane;
     const uint16_t* hbits = reinterpret_cast<const uint16_t*>(blob + off_c1);
 
-    // ---- 1. weight words and row scales (raw bits, converted at the end),
-    //         all in flight before anything waits.
-    //         Loads are unconditional (no branch, so nothing waits on
-    //         them early): a wave beyond the last row tile re-reads the last
-    //         tile and stores nothing; a block beyond K re-reads the last
-    //         block, whose chunks here have all-zero tables (zero
-    //         activations), so it adds nothing.
+    // ---- 1. activations and column scales of this thread's tables (small,
+    //         shared by all workgroups: L2 hits), issued first so that the
+    //         tables are built while the weight stream is still arriving.
+    //         K is a multiple of 32: a chunk of 4 inputs is entirely in or out.
+    uint2 xraw[TPT][2], hraw[TPT];
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+        const int tbl = min(static_cast<int>(threadIdx.x) + 256 * i, NT - 1);
+        const int c = tbl / P, p = tbl % P;
+        const int k = min(k0 + 4 * c, K - 4);  // clamped; chunks past K get zero tables below
+        if (DT == BITQ_DT_F32) {
+            const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const float*>(x) + k);
+            xraw[i][0] = make_uint2(v.x, v.y);
+            xraw[i][1] = make_uint2(v.z, v.w);
+        } else {
+            xraw[i][0] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(x) + k);
+        }
+        if (RABIT) hraw[i] = *reinterpret_cast<const uint2*>(hbits + static_cast<size_t>(p) * (Tb * kKBlock) + k);
+    }
+
+    // ---- 2. all of x, for the bound of the split-k hand-off: the same
+    //         fixed-order sum in every workgroup
+    const int n16 = (DT == BITQ_DT_F32 ? K / 4 : K / 8);  // uint4 of x
+    const uint4* x16 = reinterpret_cast<const uint4*>(x);
+    uint4 xall[XPT];
+    if (splits > 1) {
+#pragma unroll
+        for (int i = 0; i < XPT; ++i) xall[i] = x16[min(static_cast<int>(threadIdx.x) + 256 * i, n16 - 1)];
+    }
+
+    // ---- 3. weight words and row scales (raw bits, converted at the end).
+    //         Loads are unconditional (no branch, so nothing waits on them
+    //         early): a wave beyond the last row tile re-reads the last tile
+    //         and stores nothing; a block beyond K re-reads the last block,
+    //         whose chunks here have all-zero tables, so it adds nothing.
     const int tl = min(t, Tn - 1);
     const int nl = tl * kRowTile + lane;
     uint4 wv[KB][P];
@@ -291,48 +380,28 @@ __global__ __launch_bounds__(256) void gemv_sign_kernel(const uint8_t* __restric
         graw[0] = reinterpret_cast<const uint32_t*>(blob + off_c0)[nl];  // alpha, fp32 bits
     }
 
-    // ---- 2. activations (and column scales) of this thread's tables: small
-    //         and shared by all workgroups (L2 hits).  They are issued after
-    //         the weight loads; since loads complete in order, the short table
-    //         build then runs once the weights have arrived instead of holding
-    //         the weight loads back by an L2 round trip.  K is a multiple of
-    //         32: a chunk of 4 inputs is entirely in or out.
-    float xv[TPT][4], hv[TPT][4];
-#pragma unroll
-    for (int i = 0; i < TPT; ++i) {
-        const int tbl = threadIdx.x + 256 * i;
-        const int c = tbl / P, p = tbl % P;
-        const int k = k0 + 4 * c;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            xv[i][e] = 0.0f;
-            hv[i][e] = 1.0f;
-        }
-        if (tbl < NT && k < K) {
-            if (DT == BITQ_DT_F32) {
-                const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(x) + k);
-                xv[i][0] = v.x; xv[i][1] = v.y; xv[i][2] = v.z; xv[i][3] = v.w;
-            } else {
-                const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(x) + k);
-                xv[i][0] = __uint_as_float(v.x << 16); xv[i][1] = __uint_as_float(v.x & 0xFFFF0000u);
-                xv[i][2] = __uint_as_float(v.y << 16); xv[i][3] = __uint_as_float(v.y & 0xFFFF0000u);
-            }
-            if (RABIT) {
-                const uint2 h2 = *reinterpret_cast<const uint2*>(hbits + static_cast<size_t>(p) * (Tb * kKBlock) + k);
-                hv[i][0] = f16_bits_to_f32(h2.x); hv[i][1] = f16_bits_to_f32(h2.x >> 16);
-                hv[i][2] = f16_bits_to_f32(h2.y); hv[i][3] = f16_bits_to_f32(h2.y >> 16);
-            }
-        }
-    }
-
-    // ---- 3. tables: x~ = h x, then the 16 signed sums of each chunk
+    // ---- 4. tables: x~ = h x, then the 16 signed sums of each chunk
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
         const int tbl = threadIdx.x + 256 * i;
         if (tbl < NT) {
-            const float a = xv[i][0] * hv[i][0], b = xv[i][1] * hv[i][1];
-            const float cc = xv[i][2] * hv[i][2], dd = xv[i][3] * hv[i][3];
-            const float lo[4] = {-a - b, a - b, -a + b, a + b};
+            const int c = tbl / P;
+            float xv[4], hv[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+            if (DT == BITQ_DT_F32) {
+                xv[0] = __uint_as_float(xraw[i][0].x); xv[1] = __uint_as_float(xraw[i][0].y);
+                xv[2] = __uint_as_float(xraw[i][1].x); xv[3] = __uint_as_float(xraw[i][1].y);
+            } else {
+                xv[0] = __uint_as_float(xraw[i][0].x << 16); xv[1] = __uint_as_float(xraw[i][0].x & 0xFFFF0000u);
+                xv[2] = __uint_as_float(xraw[i][0].y << 16); xv[3] = __uint_as_float(xraw[i][0].y & 0xFFFF0000u);
+            }
+            if (RABIT) {
+                hv[0] = f16_bits_to_f32(hraw[i].x); hv[1] = f16_bits_to_f32(hraw[i].x >> 16);
+                hv[2] = f16_bits_to_f32(hraw[i].y); hv[3] = f16_bits_to_f32(hraw[i].y >> 16);
+            }
+            const bool in = k0 + 4 * c < K;
+            const float a = in ? xv[0] * hv[0] : 0.0f, bq = in ? xv[1] * hv[1] : 0.0f;
+            const float cc = in ? xv[2] * hv[2] : 0.0f, dd = in ? xv[3] * hv[3] : 0.0f;
+            const float lo[4] = {-a - bq, a - bq, -a + bq, a + bq};
             const float hi[4] = {-cc - dd, cc - dd, -cc + dd, cc + dd};
             float4* dst = &lut4[tbl * 4];
 #pragma unroll
@@ -340,9 +409,19 @@ __global__ __launch_bounds__(256) void gemv_sign_kernel(const uint8_t* __restric
                 dst[q4] = make_float4(lo[0] + hi[q4], lo[1] + hi[q4], lo[2] + hi[q4], lo[3] + hi[q4]);
         }
     }
+    if (splits > 1) {  // sum |x| of this thread's inputs, then of the wave's
+        float xs = 0.0f;
+#pragma unroll
+        for (int i = 0; i < XPT; ++i)
+            if (static_cast<int>(threadIdx.x) + 256 * i < n16) xs += abs_sum8<DT>(xall[i]);
+        for (int i = threadIdx.x + 256 * XPT; i < n16; i += 256) xs += abs_sum8<DT>(x16[i]);  // K > 16384 (bf16)
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) xs += __shfl_xor(xs, o, 64);
+        if (lane == 0) s_xsum[wave] = xs;
+    }
     __syncthreads();
 
-    // ---- 4. table lookups: one row per lane
+    // ---- 5. table lookups: one row per lane
     float part = 0.0f;
     {
         const uint8_t* lut_bytes = reinterpret_cast<const uint8_t*>(lut4);
@@ -379,10 +458,17 @@ __global__ __launch_bounds__(256) void gemv_sign_kernel(const uint8_t* __restric
         if (t < Tn && n < N) y[n] = part;
         return;
     }
-    if (t < Tn) {
-        store_partial(&ws_part[static_cast<size_t>(split) * Np + n], part);
-        if (arrive_last_row(&ws_cnt[n], splits) && n < N)
-            y[n] = sum_partials<float>(ws_part + n, static_cast<size_t>(Np), splits);
+    if (t < Tn && n < N) {
+        const float xsum = (s_xsum[0] + s_xsum[1]) + (s_xsum[2] + s_xsum[3]);
+        const float* hbound = reinterpret_cast<const float*>(blob + kHdrHBound);
+        float gh = 0.0f;
+        if (RABIT) {
+#pragma unroll
+            for (int p = 0; p < P; ++p) gh += fabsf(f16_bits_to_f32(graw[p])) * hbound[p];
+        } else {
+            gh = fabsf(__uint_as_float(graw[0]));
+        }
+        split_k_add(&ws_acc[n], part, gh * xsum, splits, &y[n]);
     }
 }
 
@@ -738,6 +824,10 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
     // one activation row; the first is peeled so that its loads need no wait
     // at a loop header
     auto pass = [&](int m, bool first) __attribute__((always_inline)) {
+        // per-token (and per-tensor) scales: uniform loads issued now, long
+        // before the epilogue needs them
+        const float scale = (FMT == BITQ_TERNARY && !ACC ? *reinterpret_cast<const float*>(blob + off_c0) : 1.0f) *
+                            (ACC ? 1.0f : ad[m]);
         float yacc = 0.0f;
         int tacc[2][8];
 #pragma unroll
@@ -878,8 +968,7 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
             __syncthreads();
             if (tid < RG && n < N) {
                 float tot = (s_red[0][r] + s_red[1][r]) + (s_red[2][r] + s_red[3][r]);
-                if (FMT == BITQ_TERNARY) tot = *reinterpret_cast<const float*>(blob + off_c0) * ad[m] * tot;
-                else tot = ad[m] * tot;
+                tot = scale * tot;
                 y[static_cast<size_t>(m) * N + n] = tot;
             }
         }
@@ -938,8 +1027,7 @@ static void launch_sign(const bitq_wdesc& d, const Plan& pl, const BlobLayout& L
     hipLaunchKernelGGL((gemv_sign_kernel<P, KB, RABIT, DT>), dim3(pl.row_groups, pl.splits), dim3(256), 0, st,
                        static_cast<const uint8_t*>(w), L.off_c0, L.off_c1, x, d.N, d.K, static_cast<int>(L.Np),
                        static_cast<int>(L.Tn), static_cast<int>(L.Tb), pl.splits, y,
-                       reinterpret_cast<float*>(wsb + pl.off_partials),
-                       reinterpret_cast<uint32_t*>(wsb + pl.off_counters));
+                       reinterpret_cast<unsigned long long*>(wsb + pl.off_partials));
 }
 
 template <int P, bool RABIT, int DT>
@@ -948,7 +1036,8 @@ static void launch_sign_kb(const bitq_wdesc& d, const Plan& pl, const BlobLayout
     switch (pl.blocks_per_split) {
         case 1: launch_sign<P, 1, RABIT, DT>(d, pl, L, w, x, y, ws, st); break;
         case 2: launch_sign<P, 2, RABIT, DT>(d, pl, L, w, x, y, ws, st); break;
-        default: launch_sign<P, 4, RABIT, DT>(d, pl, L, w, x, y, ws, st); break;
+        case 4: launch_sign<P, 4, RABIT, DT>(d, pl, L, w, x, y, ws, st); break;
+        default: launch_sign<P, 8, RABIT, DT>(d, pl, L, w, x, y, ws, st); break;
     }
 }
 

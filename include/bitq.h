@@ -91,7 +91,8 @@ typedef enum {
 typedef struct {
     int32_t fmt;      /* bitq_format */
     int32_t N;        /* outputs, 1 .. 2^24 */
-    int32_t K;        /* inputs, multiple of 32 (of 128 for BITQ_W2A8), <= 2^20 */
+    int32_t K;        /* inputs, multiple of 32 (of 128 for BITQ_W2A8), <= 2^20
+                         (SIGN1/RABIT: <= 64512) */
     int32_t planes;   /* see bitq_format */
     int32_t group;    /* see bitq_format */
 } bitq_wdesc;
@@ -133,7 +134,9 @@ typedef struct {
  *   header, 256 bytes: u32 magic 0x51544942 ("BITQ"), u32 version (1),
  *     u32 fmt, u32 N, u32 K, u32 P (planes), u32 group, u32 Np, u32 Kp,
  *     u32 reserved (0), u64 off_planes, u64 off_c0, u64 off_c1,
- *     u64 total_bytes; the rest is zero.
+ *     u64 total_bytes, then at byte 72 f32 hbound[3]: SIGN1 1, RABIT
+ *     max_k |h_p[k]| for p < P (the float GEMV bounds its split-k sums with
+ *     it); the rest is zero.
  *   planes section: tiles of 64 rows x 128 inputs x 1 plane = 1024 bytes,
  *     ordered [row tile t][k block b][plane p].  Inside a tile, row
  *     r = n - 64t owns 16 contiguous bytes = 4 uint32 words; word w holds
@@ -212,12 +215,15 @@ bitq_status bitq_quantize_act(const void* x_dev, int32_t x_dtype, int32_t M, int
 
 /*
  * Workspace for one bitq_gemv / bitq_gemm_smallM call (device memory, 256-byte
- * aligned).  It holds per-split partial outputs and per-row arrival
- * counters.  The size is 0 when the call needs none (the integer formats,
- * whose workgroups each cover the whole k range); ws_dev may then be NULL.  The caller zero-fills it once before its first use; every
- * completed call leaves the counters at zero again, so the same workspace is
- * reused without clearing.  Calls that share a workspace must be ordered
- * (same stream); concurrent calls need distinct workspaces.
+ * aligned).  SIGN1/RABIT layers whose k range is split over several
+ * workgroups need one 64-bit word per row (Np words), in which the splits
+ * add their fixed-point partial sums together with an arrival count.  The
+ * size is 0 when the call needs none (the integer formats, whose workgroups
+ * each cover the whole k range, and float layers with a single split);
+ * ws_dev may then be NULL.  The caller zero-fills it once before its first
+ * use; every completed call leaves the words at zero again, so the same
+ * workspace is reused without clearing.  Calls that share a workspace must
+ * be ordered (same stream); concurrent calls need distinct workspaces.
  */
 bitq_status bitq_workspace_size(const bitq_wdesc* desc, int32_t M, size_t* bytes);
 
@@ -229,7 +235,11 @@ bitq_status bitq_workspace_size(const bitq_wdesc* desc, int32_t M, size_t* bytes
  *          bitq_quantize_act with M = 1 (x_dtype = BITQ_DT_ACT).
  *   y_dev  fp32 [N], 4-byte aligned.
  * Float formats ([RaBiT] §3.2 sign-apply instead of multiplies): y_n =
- *   sum_p g_p[n] sum_k B_p[n,k] h_p[k] x_k (SIGN1: alpha_n sum_k B[n,k] x_k).
+ *   sum_p g_p[n] sum_k B_p[n,k] h_p[k] x_k (SIGN1: alpha_n sum_k B[n,k] x_k),
+ *   accumulated in fp32 per k slice; the slices are added exactly in 64-bit
+ *   fixed point scaled to the bound sum_p |g_p[n]| max|h_p| sum_k |x_k|, so
+ *   y does not depend on the order of the workgroups.  A row whose bound is
+ *   not finite (inf/NaN in x, g or h) comes out NaN.
  * Integer formats (AND+popcount of weight planes with activation planes,
  *   [ABQ] abstract/§1, [BVSR] intro; exact int32 partial sums):
  *   TERNARY y_n = gamma d Y_n, Y_n = sum_k T[n,k] q_k

@@ -8,7 +8,8 @@ trip and the GEMV parity can start from what the device actually reads.
 Specification (all little-endian):
   header, 256 bytes: u32 magic 0x51544942, u32 version 1, u32 format,
       u32 N, u32 K, u32 P (planes), u32 group, u32 Np, u32 Kp, u32 reserved,
-      u64 off_planes, u64 off_c0, u64 off_c1, u64 total_bytes.
+      u64 off_planes, u64 off_c0, u64 off_c1, u64 total_bytes; then at byte
+      72 f32 hbound[3] (SIGN1: 1; RABIT: max over k of |h_p[k]|).
   Np = N rounded up to 64 (row tile), Kp = K rounded up to 128 (k block).
   planes section: 1024-byte tiles ordered [row tile t][k block b][plane p];
       inside a tile, row r (= n - 64 t) owns 16 bytes = 4 uint32 words,
@@ -44,7 +45,8 @@ def parse_header(blob: np.ndarray) -> dict:
     h = dict(magic=int(u32[0]), version=int(u32[1]), fmt=int(u32[2]), N=int(u32[3]),
              K=int(u32[4]), P=int(u32[5]), group=int(u32[6]), Np=int(u32[7]),
              Kp=int(u32[8]), off_planes=int(u64[0]), off_c0=int(u64[1]),
-             off_c1=int(u64[2]), total=int(u64[3]))
+             off_c1=int(u64[2]), total=int(u64[3]),
+             hbound=b[72:84].view(np.float32).astype(np.float64))
     if h["magic"] != MAGIC:
         raise ValueError("bad magic")
     return h

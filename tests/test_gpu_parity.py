@@ -13,7 +13,7 @@ import pytest
 import bit_plane_gemv_amd as bq
 from oracle import act as oact, gemv as og, weights as ow, bitserial
 import synth
-from gpuhelp import (assert_within, dev_blob, parse_act, quantize_act_dev, run_gemv, say, to_dev,
+from gpuhelp import (assert_within, dev_blob, parse_act, quantize_act_dev, run_gemv, say, to_dev, torch,
                      workspace)
 
 pytestmark = pytest.mark.gpu
@@ -105,6 +105,42 @@ def _rabit_case(N, K, P, W=None, xs=None, x=None, seed=0):
 def test_rabit_gemv_small(N, K, P):
     say("rabit", N, K, P)
     _rabit_case(N, K, P)
+
+
+@pytest.mark.parametrize("N,K,P", [(200, 32256, 2), (256, 32768, 1), (70, 64512, 1)])
+def test_rabit_gemv_many_splits(N, K, P):
+    # 63 splits (the most the split-k arrival count holds), 8 k blocks per
+    # split, and the largest K of the float formats
+    say("rabit many splits", N, K, P)
+    _rabit_case(N, K, P, seed=3)
+
+
+def test_rabit_split_k_deterministic_and_workspace_reuse():
+    """The fixed-point split-k sum does not depend on the arrival order:
+    repeated calls on one workspace give bit-identical y, and each call
+    leaves the workspace words at zero for the next."""
+    N, K = 11008, 4096
+    say("rabit determinism", N, K)
+    t = torch()
+    W = synth.weights("rabit", 1, N, K)
+    xs, x = synth.activations("rabit", 1, 1, K)
+    B, g, h = ow.quantize_rabit(W, paths=2)
+    desc = bq.wdesc(bq.RABIT, N, K, planes=2)
+    bd = dev_blob(bq.pack_weights(desc, sign=B, g=g, h=h))
+    xd = to_dev(xs[0])
+    ws = workspace(desc)
+    assert ws.numel() > 0
+    outs = []
+    for _ in range(5):
+        y = t.full((N,), float("nan"), dtype=t.float32, device="cuda")
+        bq.gemv(desc, bd, xd, bq.DT_BF16, y, ws)
+        t.cuda.synchronize()
+        outs.append(y.cpu().numpy())
+        assert not ws.any().item(), "split-k words not reset"
+    for o in outs[1:]:
+        assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
+    y_ref, tol = og.gemv_rabit(B, g, h, x)
+    assert_within(outs[0][None, :], y_ref, tol, "rabit determinism")
 
 
 @pytest.mark.parametrize("shape_idx", [0, 1, 2])

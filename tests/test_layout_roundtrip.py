@@ -23,6 +23,7 @@ def test_roundtrip_sign(N, K):
     assert (h["fmt"], h["N"], h["K"], h["P"], h["version"]) == (1, N, K, 1, 1)
     assert h["total"] == blob.nbytes and h["off_planes"] == 256
     assert np.array_equal(out["B"], B) and np.array_equal(out["alpha"], alpha) and out["pad_ok"]
+    assert list(h["hbound"]) == [1.0, 0.0, 0.0]
 
 
 @pytest.mark.parametrize("N,K", SHAPES)
@@ -34,6 +35,10 @@ def test_roundtrip_rabit(N, K, P):
     assert np.array_equal(out["B"], B) and out["pad_ok"]
     assert np.array_equal(out["g"].view(np.uint16), g.view(np.uint16))
     assert np.array_equal(out["h"].view(np.uint16), h.view(np.uint16))
+    # header bound of the split-k fixed point: max |h_p| per path, zero past P
+    hb = out["header"]["hbound"]
+    assert list(hb[:P]) == [float(np.max(np.abs(h[p].astype(np.float64)))) for p in range(P)]
+    assert not np.any(hb[P:])
 
 
 @pytest.mark.parametrize("N,K", SHAPES)
