@@ -294,6 +294,15 @@ __device__ __forceinline__ void split_k_add(unsigned long long* word, float part
     __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// 16-byte load of element i of a global array given by its address as an
+// integer (so the load carries no restrict/invariant provenance and stays in
+// program order around memory clobbers), as a global (not flat) access.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 global_load16(uintptr_t base, int i) {
+    const u32x4_t v = ((const __attribute__((address_space(1))) u32x4_t*)base)[i];
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 template <int DT>
 __device__ __forceinline__ float abs_sum8(uint4 v) {  // |.| summed over 8 bf16 or 4 f32 inputs
     if (DT == BITQ_DT_F32)
@@ -344,15 +353,23 @@ __global__ __launch_bounds__(256) void gemv_sign_kernel(const uint8_t* __restric
         if (RABIT) hraw[i] = *reinterpret_cast<const uint2*>(hbits + static_cast<size_t>(p) * (Tb * kKBlock) + k);
     }
 
-    // ---- 2. all of x, for the bound of the split-k hand-off: the same
-    //         fixed-order sum in every workgroup
+    __builtin_amdgcn_sched_barrier(0);  // issue order: table inputs, weights, all of x
+
+    // ---- 2. all of x, for the bound of the split-k hand-off (the same
+    //         fixed-order sum in every workgroup), ahead of the weights
     const int n16 = (DT == BITQ_DT_F32 ? K / 4 : K / 8);  // uint4 of x
-    const uint4* x16 = reinterpret_cast<const uint4*>(x);
-    uint4 xall[XPT];
-    if (splits > 1) {
+    // (through an address without the kernel argument's restrict/invariant
+    // provenance: these loads are not moved across the memory clobber below)
+    uintptr_t xaddr = reinterpret_cast<uintptr_t>(x);
+    asm volatile("" : "+s"(xaddr));
+    uint4 xall[XPT];  // unconditional: a conditional block of loads would make
+                      // the compiler count the outstanding loads from its
+                      // shorter path and wait too early for the others
 #pragma unroll
-        for (int i = 0; i < XPT; ++i) xall[i] = x16[min(static_cast<int>(threadIdx.x) + 256 * i, n16 - 1)];
-    }
+    for (int i = 0; i < XPT; ++i) xall[i] = global_load16(xaddr, min(static_cast<int>(threadIdx.x) + 256 * i, n16 - 1));
+    asm volatile("" ::: "memory");  // keeps these loads here, ahead of the weights
+
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- 3. weight words and row scales (raw bits, converted at the end).
     //         Loads are unconditional (no branch, so nothing waits on them
@@ -380,11 +397,18 @@ __global__ __launch_bounds__(256) void gemv_sign_kernel(const uint8_t* __restric
         graw[0] = reinterpret_cast<const uint32_t*>(blob + off_c0)[nl];  // alpha, fp32 bits
     }
 
+    __builtin_amdgcn_sched_barrier(0);
+
+    __builtin_amdgcn_sched_barrier(0);
+
     // ---- 4. tables: x~ = h x, then the 16 signed sums of each chunk
+    // No branch on the table index: a guarded build would let the compiler
+    // move the input loads into it, behind the weight stream.  Lanes past the
+    // last table rebuild that table and store the same values again.
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
-        const int tbl = threadIdx.x + 256 * i;
-        if (tbl < NT) {
+        const int tbl = min(static_cast<int>(threadIdx.x) + 256 * i, NT - 1);
+        {
             const int c = tbl / P;
             float xv[4], hv[4] = {1.0f, 1.0f, 1.0f, 1.0f};
             if (DT == BITQ_DT_F32) {
@@ -409,12 +433,15 @@ __global__ __launch_bounds__(256) void gemv_sign_kernel(const uint8_t* __restric
                 dst[q4] = make_float4(lo[0] + hi[q4], lo[1] + hi[q4], lo[2] + hi[q4], lo[3] + hi[q4]);
         }
     }
-    if (splits > 1) {  // sum |x| of this thread's inputs, then of the wave's
+    {  // sum |x|: this thread's inputs (clamped duplicates masked to zero
+       // bits, no branch), the wave's, then the workgroup's after the barrier
         float xs = 0.0f;
 #pragma unroll
-        for (int i = 0; i < XPT; ++i)
-            if (static_cast<int>(threadIdx.x) + 256 * i < n16) xs += abs_sum8<DT>(xall[i]);
-        for (int i = threadIdx.x + 256 * XPT; i < n16; i += 256) xs += abs_sum8<DT>(x16[i]);  // K > 16384 (bf16)
+        for (int i = 0; i < XPT; ++i) {
+            const uint32_t keep = static_cast<int>(threadIdx.x) + 256 * i < n16 ? 0xFFFFFFFFu : 0u;
+            xs += abs_sum8<DT>(make_uint4(xall[i].x & keep, xall[i].y & keep, xall[i].z & keep, xall[i].w & keep));
+        }
+        for (int i = threadIdx.x + 256 * XPT; i < n16; i += 256) xs += abs_sum8<DT>(global_load16(xaddr, i));  // K > 16384 (bf16)
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) xs += __shfl_xor(xs, o, 64);
         if (lane == 0) s_xsum[wave] = xs;
@@ -432,7 +459,10 @@ __global__ __launch_bounds__(256) void gemv_sign_kernel(const uint8_t* __restric
         for (int bb = 0; bb < KB; ++bb)
 #pragma unroll
             for (int p = 0; p < P; ++p) {
-                const uint32_t words[4] = {wv[bb][p].x, wv[bb][p].y, wv[bb][p].z, wv[bb][p].w};
+                // the empty asm keeps every use of this block's words (and the
+                // wait for them) after the barrier, in block order
+                uint32_t words[4] = {wv[bb][p].x, wv[bb][p].y, wv[bb][p].z, wv[bb][p].w};
+                asm volatile("" : "+v"(words[0]), "+v"(words[1]), "+v"(words[2]), "+v"(words[3]));
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
                     const uint32_t w4 = words[w] << 2;   // nibble 2j in bits 2..5 of byte j
