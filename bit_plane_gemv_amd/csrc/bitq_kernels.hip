@@ -44,81 +44,6 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
-// Uniform value in a scalar register (all lanes hold the same value).
-__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
-
-// ------------------------------------------------- split-k reduction helper
-// When a row's k range is split over several workgroups, each split stores
-// its partial output with a device-scope atomic store (written through to
-// the device-coherent level, not left in one XCD's L2), waits until the store
-// is acknowledged, then increments the row's arrival counter with a
-// device-scope atomic.  The lane that sees the counter at splits - 1 is the
-// last one for that row: it resets the counter for the next call and adds
-// the row's partials in split order (deterministic), reading them with
-// device-scope atomic loads.  Rows hand off independently: no workgroup
-// barrier and no cache-wide write-back or invalidate is involved.
-__device__ __forceinline__ void store_partial(float* p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_partial(const float* p) {
-    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_partial_i(int32_t* p, int32_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int32_t load_partial_i(const int32_t* p) {
-    return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Sum of the partials p[0], p[stride], ..., p[(count-1)*stride] in index
-// order.  Loads are issued 32 at a time (indices clamped in bounds, the
-// surplus ignored), so a batch costs one memory round trip, not 32.
-template <typename T>
-__device__ __forceinline__ T sum_partials(const T* p, size_t stride, int count) {
-    constexpr int kBatch = 32;
-    T s = 0;
-    for (int s0 = 0; s0 < count; s0 += kBatch) {
-        T v[kBatch];
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int i = min(s0 + u, count - 1);
-            if constexpr (sizeof(T) == 4 && static_cast<T>(0.5f) != 0)
-                v[u] = load_partial(reinterpret_cast<const float*>(p) + i * stride);
-            else
-                v[u] = load_partial_i(reinterpret_cast<const int32_t*>(p) + i * stride);
-        }
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u)
-            if (s0 + u < count) s += v[u];
-    }
-    return s;
-}
-
-// Per-wave arrival after the wave's partial stores (one atomic per wave on
-// the counter of its 64-row tile): true, in every lane, for the wave of the
-// last split to arrive, which then resets the counter to zero.
-__device__ __forceinline__ bool arrive_last_wave(uint32_t* tile_counter, int splits) {
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are complete
-    uint32_t prev = 0;
-    if ((threadIdx.x & 63) == 0)
-        prev = __hip_atomic_fetch_add(tile_counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    prev = __builtin_amdgcn_readfirstlane(prev);
-    const bool last = prev == static_cast<uint32_t>(splits - 1);
-    if (last && (threadIdx.x & 63) == 0)
-        __hip_atomic_store(tile_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return last;
-}
-
-// Per-lane arrival after this lane's partial stores: true for the last split
-// of the lane's row (whose counter is then reset to zero).
-__device__ __forceinline__ bool arrive_last_row(uint32_t* row_counter, int splits) {
-    __builtin_amdgcn_s_waitcnt(0);  // this lane's partial stores are complete
-    const uint32_t prev = __hip_atomic_fetch_add(row_counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (prev != static_cast<uint32_t>(splits - 1)) return false;
-    __hip_atomic_store(row_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return true;
-}
-
 // ======================================================= activation quantizer
 // [HGF] §1.2: int8 activations with a per-token absmax scale, dequantized
 // with amax/127; [BVSR] intro: online conversion of activations to the bit
@@ -508,11 +433,9 @@ __global__ __launch_bounds__(256) void gemv_sign_kernel(const uint8_t* __restric
 //   sum_k qw_k q_k = sum_i sum_j u_i c_j popcount(W_i AND X_j)
 // ([ABQ] abstract and §1: arbitrary-bit products rebuilt from binary
 // operations instead of INT4/INT8 units; [BVSR] intro: AND and population
-// count directly on the bitvectors, without dequantization).  The activation
-// plane words are the same for all 64 rows of a wave, so they are read with
-// scalar loads and enter the AND as scalar operands; each weight word costs
-// one AND and one popcount-accumulate (v_bcnt_u32_b32) per activation plane.
-// All weight loads of the workgroup's k slice are issued before any compute.
+// count directly on the bitvectors, without dequantization).  Each weight
+// word costs one AND and one popcount-accumulate (v_bcnt_u32_b32) per
+// activation plane; the activation plane words come from LDS.
 //
 // Per-token epilogues (y before the per-token factor d, applied at the end):
 //   TERNARY ([HGF] §1.2): Y = sum_j c_j (popc(P & X_j) - popc(M & X_j)),
@@ -559,196 +482,15 @@ __device__ __forceinline__ int combine_planes(const int (&a)[8]) {
     return r;
 }
 
-template <int FMT, bool ACC, int KB>
-__global__ __launch_bounds__(64) void gemv_bits_kernel(const uint8_t* __restrict__ blob, size_t off_c0,
-                                                       size_t off_c1, const uint8_t* __restrict__ act,
-                                                       size_t act_off_S, size_t act_off_d, int M, int N,
-                                                       int K, int Np, int Tn, int Tb, int splits,
-                                                       float* __restrict__ y, float* __restrict__ ws_part,
-                                                       uint32_t* __restrict__ ws_cnt) {
-    constexpr int P = IntCfg<FMT>::P;
-    __shared__ float4 s_cache[FMT == BITQ_BVSR4 ? 256 * 2 : 1];
-    const int lane = threadIdx.x;
-    const int t = blockIdx.x;
-    const int n = t * kRowTile + lane;
-    const int split = blockIdx.y;
-    const int b0 = split * KB;
-    const int Kw = Tb * 4;
-    const uint32_t* __restrict__ aplanes = reinterpret_cast<const uint32_t*>(act);
-    const int32_t* __restrict__ aS = reinterpret_cast<const int32_t*>(act + act_off_S);
-    const float* __restrict__ ad = reinterpret_cast<const float*>(act + act_off_d);
-
-    // ---- all weight words and coefficients of the k slice, issued up front
-    //      and unconditionally (a block beyond K re-reads the last block and
-    //      is skipped below)
-    uint4 wv[KB][P];
-    uint32_t coef[KB];
-#pragma unroll
-    for (int bb = 0; bb < KB; ++bb) {
-        const int b = min(b0 + bb, Tb - 1);
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-            const size_t off = (static_cast<size_t>(t) * Tb + b) * P + p;
-            wv[bb][p] = *reinterpret_cast<const uint4*>(blob + kHeaderBytes + off * 1024 + lane * 16);
-        }
-        coef[bb] = 0;
-        if (FMT == BITQ_W2A8 || FMT == BITQ_BVSR4)
-            coef[bb] = reinterpret_cast<const uint32_t*>(blob + off_c0)[(static_cast<size_t>(t) * Tb + b) * 64 + lane];
-    }
-
-    if (FMT == BITQ_BVSR4 && !ACC) {
-        const float* cache = reinterpret_cast<const float*>(blob + off_c1);
-        for (int e = lane; e < 256; e += 64) {
-            const float* c = cache + 5 * e;
-            s_cache[2 * e] = make_float4(c[0], c[1], c[2], c[3]);
-            s_cache[2 * e + 1] = make_float4(c[4], 0.0f, 0.0f, 0.0f);
-        }
-        __syncthreads();
-    }
-
-    for (int m = 0; m < M; ++m) {
-        const uint32_t* __restrict__ xp = aplanes + static_cast<size_t>(m) * Kw * 8;
-        const int32_t* __restrict__ xS = aS + static_cast<size_t>(m) * Kw;
-        float yacc = 0.0f;
-        int tacc[2][8];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) tacc[i][j] = 0;
-
-#pragma unroll
-        for (int bb = 0; bb < KB; ++bb) {
-            const int bu = uniform(b0 + bb);
-            if (bu >= Tb) break;
-            if (FMT == BITQ_TERNARY) {
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const uint32_t* xw = xp + static_cast<size_t>(bu * 4 + w) * 8;
-                    const uint32_t wp = (&wv[bb][0].x)[w], wm = (&wv[bb][1].x)[w];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const uint32_t xj = xw[j];
-                        tacc[0][j] += __builtin_popcount(wp & xj);
-                        tacc[1][j] += __builtin_popcount(wm & xj);
-                    }
-                }
-            } else if (FMT == BITQ_W2A8) {
-                int a[2][8];
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) a[i][j] = 0;
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const uint32_t* xw = xp + static_cast<size_t>(bu * 4 + w) * 8;
-                    const uint32_t w0 = (&wv[bb][0].x)[w], w1 = (&wv[bb][1].x)[w];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const uint32_t xj = xw[j];
-                        a[0][j] += __builtin_popcount(w0 & xj);
-                        a[1][j] += __builtin_popcount(w1 & xj);
-                    }
-                }
-                int t8[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) t8[j] = a[0][j] + 2 * a[1][j];
-                const int A = combine_planes(t8);
-                if (ACC) {
-                    const size_t G = Tb;  // K is a multiple of 128 for W2A8
-                    if (n < N) reinterpret_cast<int32_t*>(y)[(static_cast<size_t>(m) * N + n) * G + bu] = A;
-                } else {
-                    const int S128 = xS[bu * 4] + xS[bu * 4 + 1] + xS[bu * 4 + 2] + xS[bu * 4 + 3];
-                    const float delta = f16_bits_to_f32(coef[bb]);
-                    const float z = f16_bits_to_f32(coef[bb] >> 16);
-                    yacc += delta * (static_cast<float>(A) - z * static_cast<float>(S128));
-                }
-            } else {  // BVSR4
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const uint32_t* xw = xp + static_cast<size_t>(bu * 4 + w) * 8;
-                    int a[4][8];
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const uint32_t bk = (&wv[bb][k].x)[w];
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) a[k][j] = __builtin_popcount(bk & xw[j]);
-                    }
-                    int Pk[4];
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) Pk[k] = combine_planes(a[k]);
-                    if (ACC) {
-                        const int G = K / 32;  // groups of the real (unpadded) K
-                        const int g = bu * 4 + w;
-                        int4* dst = reinterpret_cast<int4*>(y) + (static_cast<size_t>(m) * N + n) * G + g;
-                        if (n < N && g < G) *dst = make_int4(Pk[0], Pk[1], Pk[2], Pk[3]);
-                    } else {
-                        const int id = (coef[bb] >> (8 * w)) & 0xFF;
-                        const float4 c = s_cache[2 * id];
-                        const float bb5 = s_cache[2 * id + 1].x;
-                        const float S32 = static_cast<float>(xS[bu * 4 + w]);
-                        yacc += bb5 * S32 + c.x * static_cast<float>(Pk[0]) + c.y * static_cast<float>(Pk[1]) +
-                                c.z * static_cast<float>(Pk[2]) + c.w * static_cast<float>(Pk[3]);
-                    }
-                }
-            }
-        }
-
-        // ---- per-token result of this split
-        float part = 0.0f;
-        int ipart = 0;
-        if (FMT == BITQ_TERNARY) {
-            int Y[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) Y[j] = tacc[0][j] - tacc[1][j];
-            ipart = combine_planes(Y);
-            const float gamma = *reinterpret_cast<const float*>(blob + off_c0);
-            part = gamma * ad[m] * static_cast<float>(ipart);
-        } else {
-            part = ad[m] * yacc;
-        }
-        if (ACC && FMT != BITQ_TERNARY) continue;  // partials already written per group
-
-        const bool int_out = ACC;  // TERNARY with ACC: reduce the exact integer Y
-        if (splits == 1) {
-            if (n < N) {
-                if (int_out)
-                    reinterpret_cast<int32_t*>(y)[static_cast<size_t>(m) * N + n] = ipart;
-                else
-                    y[static_cast<size_t>(m) * N + n] = part;
-            }
-            continue;
-        }
-        float* slot = ws_part + (static_cast<size_t>(split) * M + m) * Np + n;
-        if (int_out)
-            store_partial_i(reinterpret_cast<int32_t*>(slot), ipart);
-        else
-            store_partial(slot, part);
-    }
-    if (ACC && FMT != BITQ_TERNARY) return;
-    if (splits == 1) return;
-    // ---- all tokens of this split are stored: arrive once, the last sums
-    if (arrive_last_row(&ws_cnt[n], splits) && n < N) {
-        const size_t stride = static_cast<size_t>(M) * Np;
-        for (int mm = 0; mm < M; ++mm) {
-            const size_t off = static_cast<size_t>(mm) * Np + n;
-            if (ACC)
-                reinterpret_cast<int32_t*>(y)[static_cast<size_t>(mm) * N + n] =
-                    sum_partials<int32_t>(reinterpret_cast<const int32_t*>(ws_part) + off, stride, splits);
-            else
-                y[static_cast<size_t>(mm) * N + n] = sum_partials<float>(ws_part + off, stride, splits);
-        }
-    }
-}
-
 // ================================= AND+popcount GEMV, whole k per workgroup
-// Same arithmetic as gemv_bits_kernel, with a decomposition that needs no
-// hand-off between workgroups: a workgroup (256 threads) owns 16 rows and the
-// whole k range.  Thread (g, r) = (tid / 16, tid % 16) takes row r of the
-// group and the k blocks b = g + 16 j (j < BPL) of each round of 16 BPL
-// blocks; the 16 lanes of a k-group read 16 adjacent rows of a tile (256
-// contiguous bytes per load).  Activation planes and group sums of the round
-// are staged once in LDS; the 16 k-groups' results for a row are added in a
-// fixed order (two lane exchanges, then four waves through LDS).
+// No hand-off between workgroups: a workgroup (256 threads) owns RG rows
+// (16 or 8) and the whole k range.  Thread (g, r) = (tid / RG, tid % RG)
+// takes row r of the group and the k blocks b = g + G j (j < BPL, G = 256/RG
+// k-groups) of each round of G BPL blocks; the RG lanes of a k-group read RG
+// adjacent rows of a tile (16 RG contiguous bytes per load).  Activation
+// planes and group sums of the round are staged once in LDS; the G k-groups'
+// results for a row are added in a fixed order (lane exchanges, then four
+// waves through LDS).
 template <int FMT, bool ACC, int BPL, int RG, bool ONE>
 __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __restrict__ blob, size_t off_c0,
                                                            size_t off_c1, const uint8_t* __restrict__ act,
@@ -1094,29 +836,6 @@ int launch_gemv_float(const bitq_wdesc& d, const Plan& pl, const void* w, const 
     else
         launch_sign_fmt<BITQ_DT_BF16>(d, pl, L, w, x, y, ws, st);
     return static_cast<int>(hipGetLastError());
-}
-
-template <int FMT, bool ACC, int KB>
-static void launch_bits_kb(const bitq_wdesc& d, const Plan& pl, const BlobLayout& L, const void* w,
-                           const void* act, int M, float* y, void* ws, hipStream_t st) {
-    ActLayout A = act_layout(M, d.K);
-    uint8_t* wsb = static_cast<uint8_t*>(ws);
-    hipLaunchKernelGGL((gemv_bits_kernel<FMT, ACC, KB>), dim3(pl.row_groups, pl.splits), dim3(64), 0, st,
-                       static_cast<const uint8_t*>(w), L.off_c0, L.off_c1, static_cast<const uint8_t*>(act),
-                       A.off_S, A.off_d, M, d.N, d.K, static_cast<int>(L.Np), static_cast<int>(L.Tn),
-                       static_cast<int>(L.Tb), pl.splits, y, reinterpret_cast<float*>(wsb + pl.off_partials),
-                       reinterpret_cast<uint32_t*>(wsb + pl.off_counters));
-}
-
-template <int FMT, bool ACC>
-static void launch_bits(const bitq_wdesc& d, const Plan& pl, const BlobLayout& L, const void* w, const void* act,
-                        int M, float* y, void* ws, hipStream_t st) {
-    switch (pl.blocks_per_split) {
-        case 1: launch_bits_kb<FMT, ACC, 1>(d, pl, L, w, act, M, y, ws, st); break;
-        case 2: launch_bits_kb<FMT, ACC, 2>(d, pl, L, w, act, M, y, ws, st); break;
-        case 4: launch_bits_kb<FMT, ACC, 4>(d, pl, L, w, act, M, y, ws, st); break;
-        default: launch_bits_kb<FMT, ACC, 8>(d, pl, L, w, act, M, y, ws, st); break;
-    }
 }
 
 template <int FMT, bool ACC, int BPL, int RG>
