@@ -17,6 +17,13 @@ and a float32 GPU kernel agree bit for bit:
 
 Then x_hat_k = q_k * d is the activation the integer paths multiply.
 Group sums S[g] = sum_{k in g} q_k feed the zero-point and offset terms.
+
+Arbitrary activation bit widths ([ABQ] §1: any WnAm, e.g. W4A4, W6A6): with
+m bits the symmetric range is [-Qm, Qm], Qm = 2^(m-1) - 1, and the same steps
+run with Qm in place of 127 (m = 8 is the int8 quantizer above).  The
+codes still fit a two's-complement byte whose bits m-1..7 all equal the
+sign, so the m-bit product needs only planes 0..m-2 and the sign plane 7
+(weight -2^(m-1)).
 """
 from __future__ import annotations
 
@@ -25,10 +32,19 @@ import numpy as np
 from . import bitserial
 
 
-def quantize(x_f32: np.ndarray):
-    """x_f32: [M, K] float32.  Returns (q int8 [M,K], d float32 [M])."""
+def qmax(bits: int) -> int:
+    """Largest code of the symmetric m-bit range: 2^(m-1) - 1."""
+    assert 2 <= bits <= 8
+    return (1 << (bits - 1)) - 1
+
+
+def quantize(x_f32: np.ndarray, bits: int = 8):
+    """x_f32: [M, K] float32.  Returns (q int8 [M,K], d float32 [M]) with
+    q in [-Qm, Qm], Qm = 2^(bits-1) - 1 (127 for the default 8 bits)."""
     x = np.asarray(x_f32, dtype=np.float32)
     assert x.ndim == 2
+    Q = qmax(bits)
+    Qf = np.float32(Q)
     amax = np.max(np.abs(x), axis=1)                       # float32, exact
     M, K = x.shape
     q = np.zeros((M, K), dtype=np.int8)
@@ -37,10 +53,10 @@ def quantize(x_f32: np.ndarray):
         a = amax[m]
         if a == 0:
             continue
-        s = np.float32(127.0) / a                          # fl32 division
+        s = Qf / a                                         # fl32 division
         prod = x[m] * s                                    # fl32 multiply
-        q[m] = np.clip(np.rint(prod), -127, 127).astype(np.int8)
-        d[m] = a / np.float32(127.0)
+        q[m] = np.clip(np.rint(prod), -Q, Q).astype(np.int8)
+        d[m] = a / Qf
     return q, d
 
 

@@ -25,6 +25,19 @@ import numpy as np
 ACT_PLANE_WEIGHTS = np.array([1, 2, 4, 8, 16, 32, 64, -128], dtype=np.int64)
 
 
+def act_plane_weights(bits: int) -> np.ndarray:
+    """Plane weights for m-bit codes q in [-(2^(m-1)-1), 2^(m-1)-1] stored as
+    int8: bits m-1..7 of the byte all equal the sign, so q is planes 0..m-2
+    with weights 2^j plus the sign plane 7 with weight -2^(m-1); planes
+    m-1..6 get weight 0.  bits = 8 gives ACT_PLANE_WEIGHTS."""
+    assert 2 <= bits <= 8
+    w = np.zeros(8, dtype=np.int64)
+    for j in range(bits - 1):
+        w[j] = 1 << j
+    w[7] = -(1 << (bits - 1))
+    return w
+
+
 def act_planes(q: np.ndarray) -> np.ndarray:
     """Two's-complement bit-planes of int8 values: out[j] = bit j of uint8(q)."""
     u = np.asarray(q, dtype=np.int8).view(np.uint8).astype(np.int64)

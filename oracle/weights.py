@@ -142,6 +142,41 @@ def quantize_w2a8(W: np.ndarray, group: int = 128):
     return (q.reshape(N, K).astype(np.uint8), delta16, z.astype(np.float16))
 
 
+def quantize_wnam(W: np.ndarray, bits: int, group: int = 128):
+    """Arbitrary weight bit width n = `bits` (1..4) for the WnAm bit-plane
+    GEMV ([ABQ] §1 quantization freedom; §3.2 Eq. (3) with gamma = 0 and the
+    clipping factors of Eq. (1) at 1): the same asymmetric min/max
+    round-to-nearest as W2A8, on L = 2^n - 1 steps per group:
+
+        delta = fl16((hi - lo) / L)
+        z     = clamp(rint(-lo / delta), 0, L)           (integer zero point)
+        q     = clamp(rint(W / delta) + z, 0, L)          (n bit-planes)
+        W^    = delta * (q - z)
+
+    A group whose step is zero gets delta = 1, z = 0, q = 0.  With n = 2 this
+    is quantize_w2a8.
+    """
+    assert 1 <= bits <= 4
+    L = float((1 << bits) - 1)
+    W = np.asarray(W, dtype=np.float32)
+    N, K = W.shape
+    assert K % group == 0
+    G = K // group
+    Wg = W.reshape(N, G, group).astype(np.float64)
+    lo = Wg.min(axis=-1)
+    hi = Wg.max(axis=-1)
+    step16 = to_f16((hi - lo) / L)
+    step = step16.astype(np.float64)
+    flat = step == 0.0
+    div = np.where(flat, 1.0, step)
+    zp = np.clip(np.rint(-lo / div), 0, L)
+    codes = np.clip(np.rint(Wg / div[..., None]) + zp[..., None], 0, L)
+    zp = np.where(flat, 0.0, zp)
+    codes = np.where(flat[..., None], 0.0, codes)
+    step16 = np.where(flat, np.float16(1.0), step16).astype(np.float16)
+    return codes.reshape(N, K).astype(np.uint8), step16, zp.astype(np.float16)
+
+
 # ---------------------------------------------------------------------- BVSR
 BVSR_GROUP = 32
 BVSR_NBITS = 4
