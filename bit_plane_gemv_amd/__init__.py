@@ -47,14 +47,16 @@ if len(_hip_runtimes()) > 1:
 
 # ------------------------------------------------------------------ enums
 OK, E_ARG, E_SHAPE, E_ALIGN, E_UNSUPPORTED, E_CAPACITY, E_DEVICE = 0, -1, -2, -3, -4, -5, -6
-SIGN1, RABIT, TERNARY, W2A8, BVSR4 = 1, 2, 3, 4, 5
+SIGN1, RABIT, TERNARY, W2A8, BVSR4, WNAM = 1, 2, 3, 4, 5, 6
 DT_F32, DT_BF16, DT_ACT = 0, 1, 2
 F_ACC_INT32 = 1
 
-FORMAT_NAMES = {SIGN1: "sign", RABIT: "rabit", TERNARY: "ternary", W2A8: "w2a8", BVSR4: "bvsr"}
+FORMAT_NAMES = {SIGN1: "sign", RABIT: "rabit", TERNARY: "ternary", W2A8: "w2a8", BVSR4: "bvsr",
+                WNAM: "wnam"}
 FORMATS = {v: k for k, v in FORMAT_NAMES.items()}
-DEFAULT_PLANES = {SIGN1: 1, RABIT: 2, TERNARY: 2, W2A8: 2, BVSR4: 4}
-DEFAULT_GROUP = {SIGN1: 0, RABIT: 0, TERNARY: 0, W2A8: 128, BVSR4: 32}
+DEFAULT_PLANES = {SIGN1: 1, RABIT: 2, TERNARY: 2, W2A8: 2, BVSR4: 4, WNAM: 4}
+DEFAULT_GROUP = {SIGN1: 0, RABIT: 0, TERNARY: 0, W2A8: 128, BVSR4: 32, WNAM: 128}
+DEFAULT_ABITS = {SIGN1: 0, RABIT: 0, TERNARY: 8, W2A8: 8, BVSR4: 8, WNAM: 4}
 
 
 class BitqError(RuntimeError):
@@ -65,7 +67,7 @@ class BitqError(RuntimeError):
 
 class WDesc(ctypes.Structure):
     _fields_ = [("fmt", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
-                ("planes", ctypes.c_int32), ("group", ctypes.c_int32)]
+                ("planes", ctypes.c_int32), ("group", ctypes.c_int32), ("abits", ctypes.c_int32)]
 
 
 class Logical(ctypes.Structure):
@@ -87,6 +89,7 @@ _sigs = {
     "bitq_quantize_weights": ([ctypes.POINTER(WDesc), _P, _P, _SZ, _I32], _I32),
     "bitq_act_size": ([_I32, _I32, ctypes.POINTER(_SZ)], _I32),
     "bitq_quantize_act": ([_P, _I32, _I32, _I32, _P, _SZ, _P], _I32),
+    "bitq_quantize_act_bits": ([_P, _I32, _I32, _I32, _I32, _P, _SZ, _P], _I32),
     "bitq_workspace_size": ([ctypes.POINTER(WDesc), _I32, ctypes.POINTER(_SZ)], _I32),
     "bitq_gemv": ([ctypes.POINTER(WDesc), _P, _P, _I32, _P, _P, _SZ, _U32, _P], _I32),
     "bitq_gemm_smallM": ([ctypes.POINTER(WDesc), _P, _P, _I32, _P, _P, _SZ, _U32, _P], _I32),
@@ -126,11 +129,13 @@ def _stream(stream) -> int | None:
     return int(stream)
 
 
-def wdesc(fmt, N: int, K: int, planes: int | None = None, group: int | None = None) -> WDesc:
+def wdesc(fmt, N: int, K: int, planes: int | None = None, group: int | None = None,
+          abits: int | None = None) -> WDesc:
     if isinstance(fmt, str):
         fmt = FORMATS[fmt]
     return WDesc(fmt, N, K, DEFAULT_PLANES[fmt] if planes is None else planes,
-                 DEFAULT_GROUP[fmt] if group is None else group)
+                 DEFAULT_GROUP[fmt] if group is None else group,
+                 DEFAULT_ABITS[fmt] if abits is None else abits)
 
 
 # -------------------------------------------------------------- host calls
@@ -194,9 +199,14 @@ def workspace_size(desc: WDesc, M: int = 1) -> int:
 
 
 # ------------------------------------------------------------ device calls
-def quantize_act(x, x_dtype: int, M: int, K: int, act, act_bytes: int | None = None, stream=None):
+def quantize_act(x, x_dtype: int, M: int, K: int, act, act_bytes: int | None = None, stream=None,
+                 abits: int = 8):
     nbytes = act.numel() * act.element_size() if act_bytes is None else act_bytes
-    _check(_lib.bitq_quantize_act(_ptr(x), x_dtype, M, K, _ptr(act), nbytes, _stream(stream)))
+    if abits == 8:
+        _check(_lib.bitq_quantize_act(_ptr(x), x_dtype, M, K, _ptr(act), nbytes, _stream(stream)))
+    else:
+        _check(_lib.bitq_quantize_act_bits(_ptr(x), x_dtype, M, K, abits, _ptr(act), nbytes,
+                                           _stream(stream)))
 
 
 def gemv(desc: WDesc, w, x, x_dtype: int, y, ws, ws_bytes: int | None = None, flags: int = 0,

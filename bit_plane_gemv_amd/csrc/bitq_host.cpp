@@ -99,7 +99,7 @@ void parallel_for(int64_t n, int nthreads, F&& body) {
 // ------------------------------------------------------------- validation
 bitq_status check_desc(const bitq_wdesc* d) {
     if (!d) return fail(BITQ_E_ARG, "desc is NULL");
-    if (d->fmt < BITQ_SIGN1 || d->fmt > BITQ_BVSR4) return fail(BITQ_E_ARG, "unknown format %d", d->fmt);
+    if (d->fmt < BITQ_SIGN1 || d->fmt > BITQ_WNAM) return fail(BITQ_E_ARG, "unknown format %d", d->fmt);
     if (d->N < 1 || d->N > (1 << 24)) return fail(BITQ_E_SHAPE, "N=%d out of range [1, 2^24]", d->N);
     if (d->K < 32 || d->K > (1 << 20)) return fail(BITQ_E_SHAPE, "K=%d out of range [32, 2^20]", d->K);
     if (d->K % 32) return fail(BITQ_E_SHAPE, "K=%d is not a multiple of 32", d->K);
@@ -127,7 +127,18 @@ bitq_status check_desc(const bitq_wdesc* d) {
             if (d->planes != 4 || d->group != 32)
                 return fail(BITQ_E_SHAPE, "BVSR4 needs planes=4, group=32");
             break;
+        case BITQ_WNAM:
+            if (d->planes < 1 || d->planes > 4 || d->group != 128)
+                return fail(BITQ_E_SHAPE, "WNAM needs planes in 1..4, group=128");
+            if (d->K % 128) return fail(BITQ_E_SHAPE, "WNAM needs K %% 128 == 0 (K=%d)", d->K);
+            if (d->abits < 2 || d->abits > 8) return fail(BITQ_E_SHAPE, "WNAM needs abits in 2..8 (abits=%d)", d->abits);
+            break;
     }
+    const bool intfmt = d->fmt == BITQ_TERNARY || d->fmt == BITQ_W2A8 || d->fmt == BITQ_BVSR4;
+    if (intfmt && d->abits != 0 && d->abits != 8)
+        return fail(BITQ_E_SHAPE, "abits=%d: TERNARY/W2A8/BVSR4 use 8-bit activations (abits 0 or 8)", d->abits);
+    if ((d->fmt == BITQ_SIGN1 || d->fmt == BITQ_RABIT) && d->abits != 0)
+        return fail(BITQ_E_SHAPE, "abits=%d: SIGN1/RABIT take raw activations (abits 0)", d->abits);
     return BITQ_OK;
 }
 
@@ -198,16 +209,20 @@ bitq_status check_logical(const bitq_wdesc& d, const bitq_logical* s) {
                     return fail(BITQ_E_ARG, "tern[%lld]=%d not in {-1,0,1}", (long long)i, s->tern[i]);
             break;
         case BITQ_W2A8:
+        case BITQ_WNAM: {
             if ((st = need(s->code, "code")) || (st = need(s->delta, "delta")) || (st = need(s->zero, "zero")))
                 return st;
+            const int top = (1 << d.planes) - 1;  // W2A8: planes = 2
             for (int64_t i = 0; i < N * K; ++i)
-                if (s->code[i] > 3) return fail(BITQ_E_ARG, "code[%lld]=%d > 3", (long long)i, s->code[i]);
+                if (s->code[i] > top)
+                    return fail(BITQ_E_ARG, "code[%lld]=%d > %d", (long long)i, s->code[i], top);
             for (int64_t i = 0; i < N * (K / 128); ++i) {
-                double z = f16_to_f64(s->zero[i]);
-                if (!(z == 0 || z == 1 || z == 2 || z == 3))
-                    return fail(BITQ_E_ARG, "zero[%lld] is not an integer in 0..3", (long long)i);
+                const double z = f16_to_f64(s->zero[i]);
+                if (!(z >= 0 && z <= top && z == std::floor(z)))
+                    return fail(BITQ_E_ARG, "zero[%lld] is not an integer in 0..%d", (long long)i, top);
             }
             break;
+        }
         case BITQ_BVSR4:
             if ((st = need(s->code, "code")) || (st = need(s->idx, "idx")) || (st = need(s->cache, "cache")))
                 return st;
@@ -235,7 +250,8 @@ void pack_coefficients(const bitq_wdesc& d, const BlobLayout& L, const bitq_logi
             std::memcpy(dst + L.off_c0, &gmm, 4);
             break;
         }
-        case BITQ_W2A8: {
+        case BITQ_W2A8:
+        case BITQ_WNAM: {
             const int64_t G = K / 128;
             for (int64_t n = 0; n < N; ++n)
                 for (int64_t g = 0; g < G; ++g) {
@@ -281,6 +297,7 @@ bitq_status pack_impl(const bitq_wdesc& d, const bitq_logical* s, void* dstv, si
             break;
         case BITQ_W2A8:
         case BITQ_BVSR4:
+        case BITQ_WNAM:
             pack_planes(d, L, dst, nthreads,
                         [&](int64_t p, int64_t n, int64_t k) { return (s->code[n * K + k] >> p) & 1; });
             break;
@@ -396,9 +413,15 @@ bitq_status quantize_rabit(const bitq_wdesc& d, const float* W, std::vector<int8
     return BITQ_OK;
 }
 
+// [ABQ] §3.2 Eq. (3) with gamma = 0 and clip factors 1: asymmetric min/max
+// round-to-nearest per group of 128 inputs on L = 2^planes - 1 steps (W2A8:
+// 2 planes, L = 3; WNAM: 1..4 planes).  delta = fl16((hi - lo)/L),
+// z = clamp(rint(-lo/delta), 0, L), q = clamp(rint(W/delta) + z, 0, L); a
+// group with a zero step gets delta = 1, z = 0, q = 0.
 void quantize_w2a8(const bitq_wdesc& d, const float* W, std::vector<uint8_t>& q, std::vector<uint16_t>& delta,
                    std::vector<uint16_t>& zero, int nthreads) {
     const int64_t N = d.N, K = d.K, G = K / 128;
+    const double L = static_cast<double>((1 << d.planes) - 1);
     q.assign(N * K, 0);
     delta.assign(N * G, 0);
     zero.assign(N * G, 0);
@@ -410,19 +433,19 @@ void quantize_w2a8(const bitq_wdesc& d, const float* W, std::vector<uint8_t>& q,
                 lo = std::min(lo, static_cast<double>(w[i]));
                 hi = std::max(hi, static_cast<double>(w[i]));
             }
-            uint16_t d16 = f64_to_f16((hi - lo) / 3.0);
+            uint16_t d16 = f64_to_f16((hi - lo) / L);
             double dl = f16_to_f64(d16);
             if (dl == 0.0) {  // degenerate group: delta = 1, z = 0, q = 0
                 delta[n * G + gi] = 0x3C00;
                 zero[n * G + gi] = 0;
                 continue;
             }
-            double z = std::min(3.0, std::max(0.0, std::nearbyint(-lo / dl)));
+            double z = std::min(L, std::max(0.0, std::nearbyint(-lo / dl)));
             delta[n * G + gi] = d16;
             zero[n * G + gi] = f64_to_f16(z);
             for (int i = 0; i < 128; ++i) {
                 double t = std::nearbyint(static_cast<double>(w[i]) / dl) + z;
-                q[n * K + gi * 128 + i] = static_cast<uint8_t>(std::min(3.0, std::max(0.0, t)));
+                q[n * K + gi * 128 + i] = static_cast<uint8_t>(std::min(L, std::max(0.0, t)));
             }
         }
     });
@@ -570,7 +593,8 @@ BlobLayout blob_layout(const bitq_wdesc& d) {
         case BITQ_SIGN1: L.c0_bytes = 4 * L.Np; L.c1_bytes = 0; break;
         case BITQ_RABIT: L.c0_bytes = 2 * L.P * L.Np; L.c1_bytes = 2 * L.P * L.Kp; break;
         case BITQ_TERNARY: L.c0_bytes = 4; L.c1_bytes = 0; break;
-        case BITQ_W2A8: L.c0_bytes = 4 * L.Np * L.Tb; L.c1_bytes = 0; break;
+        case BITQ_W2A8:
+        case BITQ_WNAM: L.c0_bytes = 4 * L.Np * L.Tb; L.c1_bytes = 0; break;
         case BITQ_BVSR4: L.c0_bytes = L.Np * (L.Kp / 32); L.c1_bytes = 256 * 5 * 4; break;
         default: L.c0_bytes = L.c1_bytes = 0;
     }
@@ -606,13 +630,15 @@ Plan make_plan(const bitq_wdesc& d, int M) {
         // Rows per workgroup (16 or 8): 8 rows double the waves of layers
         // with fewer than 16384 rows, which keeps more waves per SIMD to hide
         // the popcount chains (measured faster on every such layer shape).
-        const int rg = d.N >= 16384 ? 16 : 8;
+        // WNAM is built for 8 rows and 1, 2, 4 or 8 blocks per lane only.
+        const bool wnam = d.fmt == BITQ_WNAM;
+        const int rg = (d.N >= 16384 && !wnam) ? 16 : 8;
         const int64_t kgroups = 256 / rg;
         const int64_t need = (NB + kgroups - 1) / kgroups;
         const int sizes[6] = {1, 2, 3, 4, 6, 8};
         p.blocks_per_split = 8;
         for (int sz : sizes)
-            if (sz >= need) {
+            if (sz >= need && !(wnam && (sz == 3 || sz == 6))) {
                 p.blocks_per_split = sz;
                 break;
             }
@@ -733,6 +759,7 @@ bitq_status bitq_quantize_weights(const bitq_wdesc* desc, const float* W, void* 
                 break;
             }
             case BITQ_W2A8:
+            case BITQ_WNAM:
                 quantize_w2a8(d, W, u8, delta, zero, nthreads);
                 lg.code = u8.data();
                 lg.delta = delta.data();
@@ -763,9 +790,15 @@ bitq_status bitq_act_size(int32_t M, int32_t K, size_t* bytes) {
 
 bitq_status bitq_quantize_act(const void* x_dev, int32_t x_dtype, int32_t M, int32_t K, void* act_dev,
                               size_t act_bytes, void* stream) {
+    return bitq_quantize_act_bits(x_dev, x_dtype, M, K, 8, act_dev, act_bytes, stream);
+}
+
+bitq_status bitq_quantize_act_bits(const void* x_dev, int32_t x_dtype, int32_t M, int32_t K, int32_t abits,
+                                   void* act_dev, size_t act_bytes, void* stream) {
     size_t need = 0;
     bitq_status s = bitq_act_size(M, K, &need);
     if (s) return s;
+    if (abits < 2 || abits > 8) return fail(BITQ_E_SHAPE, "abits=%d out of range [2, 8]", abits);
     if (!x_dev || !act_dev) return fail(BITQ_E_ARG, "x_dev/act_dev is NULL");
     if (x_dtype != BITQ_DT_F32 && x_dtype != BITQ_DT_BF16)
         return fail(BITQ_E_ARG, "x_dtype must be BITQ_DT_F32 or BITQ_DT_BF16");
@@ -776,7 +809,7 @@ bitq_status bitq_quantize_act(const void* x_dev, int32_t x_dtype, int32_t M, int
     int e = current_device_is_gfx950(&is950);
     if (e) return fail(BITQ_E_DEVICE, "HIP error %d while querying the device", e);
     if (!is950) return fail(BITQ_E_UNSUPPORTED, "current device is not gfx950");
-    e = launch_quantize_act(x_dev, x_dtype, M, K, act_dev, stream);
+    e = launch_quantize_act(x_dev, x_dtype, M, K, abits, act_dev, stream);
     if (e) return fail(BITQ_E_DEVICE, "HIP launch error %d", e);
     return ok();
 }
@@ -807,7 +840,7 @@ static bitq_status gemv_common(const bitq_wdesc* desc, const void* w_dev, const 
         if (!aligned(x_dev, 16)) return fail(BITQ_E_ALIGN, "x_dev must be 16-byte aligned");
     } else {
         if (x_dtype != BITQ_DT_ACT)
-            return fail(BITQ_E_ARG, "TERNARY/W2A8/BVSR4 take an activation buffer (BITQ_DT_ACT)");
+            return fail(BITQ_E_ARG, "TERNARY/W2A8/BVSR4/WNAM take an activation buffer (BITQ_DT_ACT)");
         if (!aligned(x_dev, 256)) return fail(BITQ_E_ALIGN, "activation buffer must be 256-byte aligned");
     }
     if (!aligned(w_dev, 256)) return fail(BITQ_E_ALIGN, "w_dev must be 256-byte aligned");
@@ -841,7 +874,7 @@ bitq_status bitq_gemm_smallM(const bitq_wdesc* desc, const void* w_dev, const vo
     bitq_status s = check_desc(desc);
     if (s) return s;
     if (desc->fmt == BITQ_SIGN1 || desc->fmt == BITQ_RABIT)
-        return fail(BITQ_E_UNSUPPORTED, "bitq_gemm_smallM supports TERNARY, W2A8 and BVSR4");
+        return fail(BITQ_E_UNSUPPORTED, "bitq_gemm_smallM supports TERNARY, W2A8, BVSR4 and WNAM");
     if (M < 2 || M > 64) return fail(BITQ_E_SHAPE, "M=%d out of range [2, 64]", M);
     return gemv_common(desc, w_dev, act_dev, BITQ_DT_ACT, M, y_dev, ws_dev, ws_bytes, flags, stream);
 }

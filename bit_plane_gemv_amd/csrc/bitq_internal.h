@@ -52,7 +52,7 @@ Plan make_plan(const bitq_wdesc& d, int M);
 
 // Kernel launchers (bitq_kernels.hip).  Arguments are already validated.
 // Each returns hipSuccess or the HIP error code of the launch.
-int launch_quantize_act(const void* x, int x_dtype, int M, int K, void* act, void* stream);
+int launch_quantize_act(const void* x, int x_dtype, int M, int K, int abits, void* act, void* stream);
 int launch_gemv_float(const bitq_wdesc& d, const Plan& plan, const void* w, const void* x,
                       int x_dtype, float* y, void* ws, void* stream);
 int launch_gemv_int(const bitq_wdesc& d, const Plan& plan, const void* w, const void* act,

@@ -49,6 +49,7 @@ __device__ __forceinline__ float wave_max(float v) {
 // with amax/127; [BVSR] intro: online conversion of activations to the bit
 // format.  Arithmetic order fixed for bit-exactness: s = fl32(127/amax)
 // correctly rounded, q = clamp(rint(fl32(x*s)), -127, 127), d = fl32(amax/127).
+// m-bit activations ([ABQ] §1) use Qm = 2^(m-1) - 1 in place of 127.
 //
 // Grid (words / 8, M): each workgroup (4 waves) owns 8 consecutive 32-input
 // words of one token.  It first reduces amax over the token's whole row (the
@@ -64,7 +65,7 @@ __device__ __forceinline__ float act_at(const void* x, size_t i) {
 }
 
 template <int DT>
-__global__ __launch_bounds__(256) void quant_act_kernel(const void* __restrict__ x, int K, int Kw,
+__global__ __launch_bounds__(256) void quant_act_kernel(const void* __restrict__ x, int K, int Kw, float qmax,
                                                         uint32_t* __restrict__ planes, int32_t* __restrict__ S,
                                                         int8_t* __restrict__ q, float* __restrict__ dq) {
     constexpr int VEC = (DT == BITQ_DT_F32) ? 4 : 8;  // inputs per 16-byte load
@@ -120,8 +121,8 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const void* __restrict__
     __syncthreads();
     amax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
     float s = 0.0f;
-    if (amax > 0.0f) s = __fdiv_rn(127.0f, amax);
-    if (blockIdx.x == 0 && tid == 0) dq[m] = (amax > 0.0f) ? __fdiv_rn(amax, 127.0f) : 0.0f;
+    if (amax > 0.0f) s = __fdiv_rn(qmax, amax);
+    if (blockIdx.x == 0 && tid == 0) dq[m] = (amax > 0.0f) ? __fdiv_rn(amax, qmax) : 0.0f;
 
     // ---- this wave's 64 inputs = words w0 and w0 + 1
     const int w0 = 8 * blockIdx.x + 2 * wave;
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const void* __restrict__
     int qi = 0;
     if (k < K && amax > 0.0f) {
         const float r = rintf(__fmul_rn(s_slice[k - lo], s));
-        qi = static_cast<int>(fminf(fmaxf(r, -127.0f), 127.0f));
+        qi = static_cast<int>(fminf(fmaxf(r, -qmax), qmax));
     }
     q[static_cast<size_t>(m) * (Kw * 32) + k] = static_cast<int8_t>(qi);
     // planes: lane j (< 8) keeps plane j of word w0, lane 8 + j of word w0 + 1
@@ -444,14 +445,6 @@ __global__ __launch_bounds__(256) void gemv_sign_kernel(const uint8_t* __restric
 //           y += delta (A - z S128)
 //   BVSR4 ([BVSR]): per 32-group P_k = sum_j c_j popc(beta_k & X_j),
 //           y += b S32 + sum_k c_k P_k with (c, b) = cache[idx]
-template <int FMT>
-struct IntCfg;
-template <>
-struct IntCfg<BITQ_TERNARY> { static constexpr int P = 2; };
-template <>
-struct IntCfg<BITQ_W2A8> { static constexpr int P = 2; };
-template <>
-struct IntCfg<BITQ_BVSR4> { static constexpr int P = 4; };
 
 // popcount(v) + acc as one v_bcnt_u32_b32 (keeps the accumulation a chain
 // of accumulating popcounts instead of separate popcounts plus adds).
@@ -491,12 +484,11 @@ __device__ __forceinline__ int combine_planes(const int (&a)[8]) {
 // planes and group sums of the round are staged once in LDS; the G k-groups'
 // results for a row are added in a fixed order (lane exchanges, then four
 // waves through LDS).
-template <int FMT, bool ACC, int BPL, int RG, bool ONE>
+template <int FMT, int P, bool ACC, int BPL, int RG, bool ONE>
 __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __restrict__ blob, size_t off_c0,
                                                            size_t off_c1, const uint8_t* __restrict__ act,
                                                            size_t act_off_S, size_t act_off_d, int M, int N, int K,
-                                                           int Tb, float* __restrict__ y) {
-    constexpr int P = IntCfg<FMT>::P;
+                                                           int Tb, int abits, float* __restrict__ y) {
     constexpr int G = 256 / RG;    // k-groups: lanes that share a row
     constexpr int Q = 64 / RG;     // row groups per 64-row tile
     constexpr int NBW = G * BPL;   // k blocks per round
@@ -547,7 +539,8 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
                 wv[j][p] = *reinterpret_cast<const uint4*>(tile_planes + off);
             }
             coef[j] = 0;
-            if (FMT == BITQ_W2A8 || FMT == BITQ_BVSR4) coef[j] = tile_coef[static_cast<uint32_t>(b * 64 + rowin)];
+            if (FMT == BITQ_W2A8 || FMT == BITQ_BVSR4 || FMT == BITQ_WNAM)
+                coef[j] = tile_coef[static_cast<uint32_t>(b * 64 + rowin)];
         }
     };
     // Staging of the activation planes and sums of blocks [b_base, b_base +
@@ -575,7 +568,7 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
     // Issue order: coefficient cache (BVSR), activation copies, then the
     // weight stream; kWeightLoads loads follow the copies, so the barrier
     // below waits for the copies without waiting for the weights.
-    constexpr int kWeightLoads = BPL * P + ((FMT == BITQ_W2A8 || FMT == BITQ_BVSR4) ? BPL : 0);
+    constexpr int kWeightLoads = BPL * P + ((FMT == BITQ_W2A8 || FMT == BITQ_BVSR4 || FMT == BITQ_WNAM) ? BPL : 0);
     if (FMT == BITQ_BVSR4 && !ACC) {
         // cache entry e (c0..c3, b; 5 floats) -> LDS floats 8e..8e+4 by 4-byte
         // copies; floats 8e+5..8e+7 are never read (they get copies of b)
@@ -668,6 +661,49 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
 #pragma unroll
                     for (int jj = 0; jj < 8; ++jj) t8[jj] = a[0][jj] + 2 * a[1][jj];
                     const int A = combine_planes(t8);
+                    if (ACC) {
+                        if (n < N) reinterpret_cast<int32_t*>(y)[(static_cast<size_t>(m) * N + n) * NB + b] = A;
+                    } else {
+                        const int4 S4 = *reinterpret_cast<const int4*>(&s_S[4 * bl]);
+                        const int S128 = S4.x + S4.y + S4.z + S4.w;
+                        const float delta = f16_bits_to_f32(cw);
+                        const float z = f16_bits_to_f32(cw >> 16);
+                        yacc += delta * (static_cast<float>(A) - z * static_cast<float>(S128));
+                    }
+                } else if (FMT == BITQ_WNAM) {
+                    // n = P weight planes, m = abits activation planes: planes
+                    // 0..m-2 with weights 2^j and the sign plane 7 with weight
+                    // -2^(m-1) (bits m-1..6 of an m-bit code are sign copies)
+                    int a[P][8];
+#pragma unroll
+                    for (int i = 0; i < P; ++i)
+#pragma unroll
+                        for (int jj = 0; jj < 8; ++jj) a[i][jj] = 0;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const uint4 x0 = *reinterpret_cast<const uint4*>(xa + 8 * w);
+                        const uint4 x1 = *reinterpret_cast<const uint4*>(xa + 8 * w + 4);
+                        const uint32_t xj[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+                        uint32_t wi[P];
+#pragma unroll
+                        for (int i = 0; i < P; ++i) wi[i] = (&wv[j][i].x)[w];
+#pragma unroll
+                        for (int jj = 0; jj < 7; ++jj)
+                            if (jj < abits - 1)  // uniform
+#pragma unroll
+                                for (int i = 0; i < P; ++i) a[i][jj] = bcnt_acc(wi[i] & xj[jj], a[i][jj]);
+#pragma unroll
+                        for (int i = 0; i < P; ++i) a[i][7] = bcnt_acc(wi[i] & xj[7], a[i][7]);
+                    }
+                    int A = 0;
+#pragma unroll
+                    for (int i = P - 1; i >= 0; --i) {
+                        int r = -a[i][7];
+#pragma unroll
+                        for (int jj = 6; jj >= 0; --jj)
+                            if (jj < abits - 1) r = 2 * r + a[i][jj];
+                        A = 2 * A + r;
+                    }
                     if (ACC) {
                         if (n < N) reinterpret_cast<int32_t*>(y)[(static_cast<size_t>(m) * N + n) * NB + b] = A;
                     } else {
@@ -774,7 +810,7 @@ int current_device_is_gfx950(int* is_gfx950) {
     return 0;
 }
 
-int launch_quantize_act(const void* x, int x_dtype, int M, int K, void* act, void* stream) {
+int launch_quantize_act(const void* x, int x_dtype, int M, int K, int abits, void* act, void* stream) {
     ActLayout A = act_layout(M, K);
     uint8_t* base = static_cast<uint8_t*>(act);
     auto* planes = reinterpret_cast<uint32_t*>(base + A.off_planes);
@@ -783,12 +819,13 @@ int launch_quantize_act(const void* x, int x_dtype, int M, int K, void* act, voi
     auto* d = reinterpret_cast<float*>(base + A.off_d);
     const int Kw = static_cast<int>(A.Kw);
     const dim3 grid((Kw + 7) / 8, M);
+    const float qmax = static_cast<float>((1 << (abits - 1)) - 1);  // 127 for int8
     if (x_dtype == BITQ_DT_F32)
         hipLaunchKernelGGL(quant_act_kernel<BITQ_DT_F32>, grid, dim3(256), 0, static_cast<hipStream_t>(stream), x,
-                           K, Kw, planes, S, q, d);
+                           K, Kw, qmax, planes, S, q, d);
     else
         hipLaunchKernelGGL(quant_act_kernel<BITQ_DT_BF16>, grid, dim3(256), 0, static_cast<hipStream_t>(stream), x,
-                           K, Kw, planes, S, q, d);
+                           K, Kw, qmax, planes, S, q, d);
     return static_cast<int>(hipGetLastError());
 }
 
@@ -838,7 +875,7 @@ int launch_gemv_float(const bitq_wdesc& d, const Plan& pl, const void* w, const 
     return static_cast<int>(hipGetLastError());
 }
 
-template <int FMT, bool ACC, int BPL, int RG>
+template <int FMT, int P, bool ACC, int BPL, int RG>
 static void launch_nr_bpl(const bitq_wdesc& d, const BlobLayout& L, const void* w, const void* act, int M,
                           float* y, hipStream_t st) {
     ActLayout A = act_layout(M, d.K);
@@ -847,31 +884,56 @@ static void launch_nr_bpl(const bitq_wdesc& d, const BlobLayout& L, const void* 
     const int tiles = static_cast<int>(L.Tn);
     const int groups = 8 * (64 / RG) * ((tiles + 7) / 8);
     const bool one = L.Tb <= (256 / RG) * BPL;  // the whole k range in one round
-    auto kern = one ? gemv_bits_nr_kernel<FMT, ACC, BPL, RG, true> : gemv_bits_nr_kernel<FMT, ACC, BPL, RG, false>;
+    auto kern = one ? gemv_bits_nr_kernel<FMT, P, ACC, BPL, RG, true> : gemv_bits_nr_kernel<FMT, P, ACC, BPL, RG, false>;
+    const int abits = d.fmt == BITQ_WNAM ? d.abits : 8;
     hipLaunchKernelGGL(kern, dim3(groups), dim3(256), 0, st, static_cast<const uint8_t*>(w), L.off_c0, L.off_c1,
-                       static_cast<const uint8_t*>(act), A.off_S, A.off_d, M, d.N, d.K, static_cast<int>(L.Tb), y);
+                       static_cast<const uint8_t*>(act), A.off_S, A.off_d, M, d.N, d.K, static_cast<int>(L.Tb),
+                       abits, y);
 }
 
-template <int FMT, bool ACC, int RG>
+template <int FMT, int P, bool ACC, int RG>
 static void launch_nr_rg(const bitq_wdesc& d, const Plan& pl, const BlobLayout& L, const void* w,
                          const void* act, int M, float* y, hipStream_t st) {
-    switch (pl.blocks_per_split) {  // blocks per lane
-        case 1: launch_nr_bpl<FMT, ACC, 1, RG>(d, L, w, act, M, y, st); break;
-        case 2: launch_nr_bpl<FMT, ACC, 2, RG>(d, L, w, act, M, y, st); break;
-        case 3: launch_nr_bpl<FMT, ACC, 3, RG>(d, L, w, act, M, y, st); break;
-        case 4: launch_nr_bpl<FMT, ACC, 4, RG>(d, L, w, act, M, y, st); break;
-        case 6: launch_nr_bpl<FMT, ACC, 6, RG>(d, L, w, act, M, y, st); break;
-        default: launch_nr_bpl<FMT, ACC, 8, RG>(d, L, w, act, M, y, st); break;
+    if constexpr (FMT == BITQ_WNAM) {  // blocks per lane 1, 2, 4 or 8 (the plan rounds up)
+        switch (pl.blocks_per_split) {
+            case 1: launch_nr_bpl<FMT, P, ACC, 1, RG>(d, L, w, act, M, y, st); break;
+            case 2: launch_nr_bpl<FMT, P, ACC, 2, RG>(d, L, w, act, M, y, st); break;
+            case 4: launch_nr_bpl<FMT, P, ACC, 4, RG>(d, L, w, act, M, y, st); break;
+            default: launch_nr_bpl<FMT, P, ACC, 8, RG>(d, L, w, act, M, y, st); break;
+        }
+    } else {
+        switch (pl.blocks_per_split) {  // blocks per lane
+            case 1: launch_nr_bpl<FMT, P, ACC, 1, RG>(d, L, w, act, M, y, st); break;
+            case 2: launch_nr_bpl<FMT, P, ACC, 2, RG>(d, L, w, act, M, y, st); break;
+            case 3: launch_nr_bpl<FMT, P, ACC, 3, RG>(d, L, w, act, M, y, st); break;
+            case 4: launch_nr_bpl<FMT, P, ACC, 4, RG>(d, L, w, act, M, y, st); break;
+            case 6: launch_nr_bpl<FMT, P, ACC, 6, RG>(d, L, w, act, M, y, st); break;
+            default: launch_nr_bpl<FMT, P, ACC, 8, RG>(d, L, w, act, M, y, st); break;
+        }
     }
 }
 
-template <int FMT, bool ACC>
+template <int FMT, int P, bool ACC>
 static void launch_nr(const bitq_wdesc& d, const Plan& pl, const BlobLayout& L, const void* w, const void* act,
                       int M, float* y, hipStream_t st) {
-    switch (pl.rows_per_wg) {  // rows per workgroup
-        case 4: launch_nr_rg<FMT, ACC, 4>(d, pl, L, w, act, M, y, st); break;
-        case 8: launch_nr_rg<FMT, ACC, 8>(d, pl, L, w, act, M, y, st); break;
-        default: launch_nr_rg<FMT, ACC, 16>(d, pl, L, w, act, M, y, st); break;
+    if constexpr (FMT == BITQ_WNAM) {  // 8 rows per workgroup only
+        launch_nr_rg<FMT, P, ACC, 8>(d, pl, L, w, act, M, y, st);
+    } else {
+        switch (pl.rows_per_wg) {  // rows per workgroup
+            case 8: launch_nr_rg<FMT, P, ACC, 8>(d, pl, L, w, act, M, y, st); break;
+            default: launch_nr_rg<FMT, P, ACC, 16>(d, pl, L, w, act, M, y, st); break;
+        }
+    }
+}
+
+template <bool ACC>
+static void launch_wnam(const bitq_wdesc& d, const Plan& pl, const BlobLayout& L, const void* w, const void* act,
+                        int M, float* y, hipStream_t st) {
+    switch (d.planes) {
+        case 1: launch_nr<BITQ_WNAM, 1, ACC>(d, pl, L, w, act, M, y, st); break;
+        case 2: launch_nr<BITQ_WNAM, 2, ACC>(d, pl, L, w, act, M, y, st); break;
+        case 3: launch_nr<BITQ_WNAM, 3, ACC>(d, pl, L, w, act, M, y, st); break;
+        default: launch_nr<BITQ_WNAM, 4, ACC>(d, pl, L, w, act, M, y, st); break;
     }
 }
 
@@ -883,16 +945,19 @@ int launch_gemv_int(const bitq_wdesc& d, const Plan& pl, const void* w, const vo
     (void)ws;
     switch (d.fmt) {
         case BITQ_TERNARY:
-            acc ? launch_nr<BITQ_TERNARY, true>(d, pl, L, w, act, M, y, st)
-                : launch_nr<BITQ_TERNARY, false>(d, pl, L, w, act, M, y, st);
+            acc ? launch_nr<BITQ_TERNARY, 2, true>(d, pl, L, w, act, M, y, st)
+                : launch_nr<BITQ_TERNARY, 2, false>(d, pl, L, w, act, M, y, st);
             break;
         case BITQ_W2A8:
-            acc ? launch_nr<BITQ_W2A8, true>(d, pl, L, w, act, M, y, st)
-                : launch_nr<BITQ_W2A8, false>(d, pl, L, w, act, M, y, st);
+            acc ? launch_nr<BITQ_W2A8, 2, true>(d, pl, L, w, act, M, y, st)
+                : launch_nr<BITQ_W2A8, 2, false>(d, pl, L, w, act, M, y, st);
+            break;
+        case BITQ_WNAM:
+            acc ? launch_wnam<true>(d, pl, L, w, act, M, y, st) : launch_wnam<false>(d, pl, L, w, act, M, y, st);
             break;
         default:
-            acc ? launch_nr<BITQ_BVSR4, true>(d, pl, L, w, act, M, y, st)
-                : launch_nr<BITQ_BVSR4, false>(d, pl, L, w, act, M, y, st);
+            acc ? launch_nr<BITQ_BVSR4, 4, true>(d, pl, L, w, act, M, y, st)
+                : launch_nr<BITQ_BVSR4, 4, false>(d, pl, L, w, act, M, y, st);
             break;
     }
     return static_cast<int>(hipGetLastError());

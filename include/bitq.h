@@ -68,11 +68,16 @@ typedef enum {
                           W^ = delta * (q - z) per group of 128 consecutive inputs,
                           delta and z fp16; the two bits are two binary planes.
                           planes = 2, group = 128. */
-    BITQ_BVSR4 = 5     /* [BVSR] introduction: per group of 32 consecutive inputs,
+    BITQ_BVSR4 = 5,    /* [BVSR] introduction: per group of 32 consecutive inputs,
                           W^ = b + sum_k c_k beta_k with 4 {0,1} bitvectors
                           beta_0..3 and a coefficient set (c_0..c_3, b) picked by
                           a u8 index from a shared 256-entry cache of fp32 sets.
                           planes = 4, group = 32. */
+    BITQ_WNAM = 6      /* [ABQ] §1 arbitrary-bit WnAm: n-bit asymmetric codes
+                          q in 0..2^n-1, W^ = delta * (q - z) per group of 128
+                          inputs (delta, z fp16; the W2A8 arithmetic with
+                          2^n - 1 steps), times m-bit symmetric activations.
+                          planes = n (1..4), group = 128, abits = m (2..8). */
 } bitq_format;
 
 /* Activation dtypes accepted by bitq_quantize_act / bitq_gemv. */
@@ -91,10 +96,14 @@ typedef enum {
 typedef struct {
     int32_t fmt;      /* bitq_format */
     int32_t N;        /* outputs, 1 .. 2^24 */
-    int32_t K;        /* inputs, multiple of 32 (of 128 for BITQ_W2A8), <= 2^20
-                         (SIGN1/RABIT: <= 64512) */
+    int32_t K;        /* inputs, multiple of 32 (of 128 for BITQ_W2A8/WNAM),
+                         <= 2^20 (SIGN1/RABIT: <= 64512) */
     int32_t planes;   /* see bitq_format */
     int32_t group;    /* see bitq_format */
+    int32_t abits;    /* activation bits of the integer GEMV: WNAM 2..8; the
+                         other integer formats 0 or 8 (int8); float formats 0.
+                         Activation buffers passed to the GEMV must have been
+                         written with the same bit count. */
 } bitq_wdesc;
 
 /*
@@ -109,9 +118,11 @@ typedef struct {
  *                (zero must hold an integer 0..3)
  *   BITQ_BVSR4   code [N][K] (0..15, bit k = bitvector beta_k), idx [N][K/32],
  *                cache [256][5] as (c0, c1, c2, c3, b)
+ *   BITQ_WNAM    code [N][K] (0..2^n-1), delta [N][K/128], zero [N][K/128]
+ *                (zero must hold an integer 0..2^n-1)
  *
  * This mirrors the weight-parameter struct of [BitNet] §3.2 (binary weights,
- * scales, optional zero points) generalized to the five formats.
+ * scales, optional zero points) generalized to the six formats.
  */
 typedef struct {
     const int8_t*   sign;
@@ -195,7 +206,10 @@ bitq_status bitq_quantize_weights(const bitq_wdesc* desc, const float* W, void* 
  *                          byte of q[m][32w + i] at bit i
  *   S      i32 [M][Kw]     sum of q over each run of 32 inputs
  *   q      i8  [M][Kp]     quantized activations (0 beyond K)
- *   d      f32 [M]         dequantization step amax/127
+ *   d      f32 [M]         dequantization step amax/Qm (Qm = 127 for int8)
+ * With m-bit activations (bitq_quantize_act_bits) q lies in [-Qm, Qm],
+ * Qm = 2^(m-1) - 1; the byte's bits m-1..7 then all equal the sign, and the
+ * GEMV uses planes 0..m-2 and plane 7 (weight -2^(m-1)).
  */
 bitq_status bitq_act_size(int32_t M, int32_t K, size_t* bytes);
 
@@ -212,6 +226,15 @@ bitq_status bitq_act_size(int32_t M, int32_t K, size_t* bytes);
  */
 bitq_status bitq_quantize_act(const void* x_dev, int32_t x_dtype, int32_t M, int32_t K,
                               void* act_dev, size_t act_bytes, void* stream);
+
+/*
+ * The same per-token quantization to m = abits bits ([ABQ] §1: arbitrary
+ * activation precision, e.g. A4, A6): Qm = 2^(m-1) - 1 replaces 127, i.e.
+ * s = fl32(Qm/amax), q = clamp(rint(fl32(x*s)), -Qm, Qm), d = fl32(amax/Qm).
+ * abits 2..8; abits = 8 is bitq_quantize_act.  Same buffer layout.
+ */
+bitq_status bitq_quantize_act_bits(const void* x_dev, int32_t x_dtype, int32_t M, int32_t K,
+                                   int32_t abits, void* act_dev, size_t act_bytes, void* stream);
 
 /*
  * Workspace for one bitq_gemv / bitq_gemm_smallM call (device memory, 256-byte
@@ -231,8 +254,9 @@ bitq_status bitq_workspace_size(const bitq_wdesc* desc, int32_t M, size_t* bytes
  * Batch-1 GEMV y[N] = W^ x.
  *   w_dev  packed blob in device memory (256-byte aligned)
  *   x_dev  SIGN1/RABIT: raw activations, BITQ_DT_F32 or BITQ_DT_BF16, 16-byte
- *          aligned.  TERNARY/W2A8/BVSR4: an activation buffer from
- *          bitq_quantize_act with M = 1 (x_dtype = BITQ_DT_ACT).
+ *          aligned.  TERNARY/W2A8/BVSR4/WNAM: an activation buffer from
+ *          bitq_quantize_act (WNAM: bitq_quantize_act_bits with desc->abits)
+ *          with M = 1 (x_dtype = BITQ_DT_ACT).
  *   y_dev  fp32 [N], 4-byte aligned.
  * Float formats ([RaBiT] §3.2 sign-apply instead of multiplies): y_n =
  *   sum_p g_p[n] sum_k B_p[n,k] h_p[k] x_k (SIGN1: alpha_n sum_k B[n,k] x_k),
@@ -247,9 +271,11 @@ bitq_status bitq_workspace_size(const bitq_wdesc* desc, int32_t M, size_t* bytes
  *           A[n,g] = sum_{k in g} q[n,k] q_k
  *   BVSR4   y_n = d sum_g (b S32[g] + sum_j c_j P[n,g,j]),
  *           P[n,g,j] = sum_{k in g} beta_j[n,k] q_k, (c, b) = cache[idx[n,g]]
+ *   WNAM    as W2A8 with n-bit codes and m-bit q: the AND+popcount runs over
+ *           n weight planes and m activation planes only
  * flags & BITQ_F_ACC_INT32 (integer formats): y_dev receives, as int32,
- *   TERNARY Y [N]; W2A8 A [N][K/128]; BVSR4 P [N][K/32][4]; the buffer must
- *   hold that many int32 values.
+ *   TERNARY Y [N]; W2A8/WNAM A [N][K/128]; BVSR4 P [N][K/32][4]; the buffer
+ *   must hold that many int32 values.
  */
 bitq_status bitq_gemv(const bitq_wdesc* desc, const void* w_dev, const void* x_dev,
                       int32_t x_dtype, float* y_dev, void* ws_dev, size_t ws_bytes,
@@ -257,8 +283,8 @@ bitq_status bitq_gemv(const bitq_wdesc* desc, const void* w_dev, const void* x_d
 
 /*
  * Small-batch GEMM y[M][N] = x W^T for 2 <= M <= 64, integer formats
- * (TERNARY, W2A8, BVSR4), reading every weight once for all M tokens.
- *   act_dev activation buffer from bitq_quantize_act with this M.
+ * (TERNARY, W2A8, BVSR4, WNAM), reading every weight once for all M tokens.
+ *   act_dev activation buffer from bitq_quantize_act(_bits) with this M.
  *   y_dev   fp32 [M][N].  BITQ_F_ACC_INT32 writes [M][...] int32 partials
  *           laid out as in bitq_gemv, one block per token.
  */

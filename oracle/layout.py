@@ -23,6 +23,7 @@ Specification (all little-endian):
                 high half = zero point (f16)  (plane i = bit i of q)
       5 bvsr    c0 = idx    u8  [Np/64][Kp/128][64][4] (byte j = group 4b+j),
                 c1 = cache  f32 [256][5]      (plane k = bitvector beta_k)
+      6 wnam    as w2a8 with P = n planes      (plane i = bit i of q)
   Every section starts at a multiple of 256 bytes.
 """
 from __future__ import annotations
@@ -35,7 +36,7 @@ MAGIC = 0x51544942
 HEADER_BYTES = 256
 ROW_TILE = 64
 K_BLOCK = 128
-FORMATS = {1: "sign", 2: "rabit", 3: "ternary", 4: "w2a8", 5: "bvsr"}
+FORMATS = {1: "sign", 2: "rabit", 3: "ternary", 4: "w2a8", 5: "bvsr", 6: "wnam"}
 
 
 def parse_header(blob: np.ndarray) -> dict:
@@ -93,8 +94,8 @@ def unpack(blob: np.ndarray) -> dict:
         out["both_set"] = bool(np.any(plus & minus))
         out["T"] = plus - minus
         out["gamma"] = np.float32(_section(b, h["off_c0"], 4, np.float32)[0])
-    elif fmt == 4:
-        out["q"] = (bits[0] + 2 * bits[1]).astype(np.uint8)
+    elif fmt in (4, 6):   # w2a8 (2 planes), wnam (P planes): code = sum_p 2^p plane_p
+        out["q"] = sum((bits[p].astype(np.int64) << p) for p in range(P)).astype(np.uint8)
         dz = _section(b, h["off_c0"], 4 * Np * (Kp // K_BLOCK), np.uint32)
         dz = dz.reshape(Tn, Tb, ROW_TILE).transpose(0, 2, 1).reshape(Np, Tb)
         delta = (dz & 0xFFFF).astype(np.uint16).view(np.float16)

@@ -40,13 +40,13 @@ def workspace(desc, M=1):
     return t.zeros(bq.workspace_size(desc, M), dtype=t.uint8, device="cuda")
 
 
-def quantize_act_dev(x_bits_or_f32: np.ndarray, M: int, K: int):
-    """Run bitq_quantize_act; returns (device act buffer, parsed host copy)."""
+def quantize_act_dev(x_bits_or_f32: np.ndarray, M: int, K: int, abits: int = 8):
+    """Run bitq_quantize_act(_bits); returns (device act buffer, parsed host copy)."""
     t = torch()
     x = to_dev(x_bits_or_f32)
     dt = bq.DT_F32 if x_bits_or_f32.dtype == np.float32 else bq.DT_BF16
     act = t.full((bq.act_size(M, K),), 0x5A, dtype=t.uint8, device="cuda")  # poison
-    bq.quantize_act(x, dt, M, K, act)
+    bq.quantize_act(x, dt, M, K, act, abits=abits)
     t.cuda.synchronize()
     return act, parse_act(act.cpu().numpy(), M, K)
 

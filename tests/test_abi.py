@@ -45,6 +45,15 @@ def test_version_and_error_string():
     (bq.WDesc(bq.W2A8, 64, 96, 2, 128), bq.E_SHAPE),
     (bq.WDesc(bq.W2A8, 64, 128, 2, 64), bq.E_SHAPE),
     (bq.WDesc(bq.BVSR4, 64, 128, 3, 32), bq.E_SHAPE),
+    (bq.WDesc(7, 64, 128, 1, 0), bq.E_ARG),
+    (bq.WDesc(bq.WNAM, 64, 128, 0, 128, 4), bq.E_SHAPE),
+    (bq.WDesc(bq.WNAM, 64, 128, 5, 128, 4), bq.E_SHAPE),
+    (bq.WDesc(bq.WNAM, 64, 128, 3, 32, 4), bq.E_SHAPE),
+    (bq.WDesc(bq.WNAM, 64, 96, 3, 128, 4), bq.E_SHAPE),
+    (bq.WDesc(bq.WNAM, 64, 128, 3, 128, 1), bq.E_SHAPE),
+    (bq.WDesc(bq.WNAM, 64, 128, 3, 128, 9), bq.E_SHAPE),
+    (bq.WDesc(bq.W2A8, 64, 128, 2, 128, 4), bq.E_SHAPE),
+    (bq.WDesc(bq.RABIT, 64, 128, 2, 0, 8), bq.E_SHAPE),
 ])
 def test_descriptor_validation(desc, status):
     with pytest.raises(bq.BitqError) as e:
@@ -147,6 +156,13 @@ def test_device_entry_points_validate_before_any_device_call():
     assert bq._lib.bitq_quantize_act(good, 7, 4, 256, good, n, None) == bq.E_ARG
     assert bq._lib.bitq_quantize_act(good + 2, bq.DT_BF16, 4, 256, good, n, None) == bq.E_ALIGN
     assert bq._lib.bitq_quantize_act(good, bq.DT_BF16, 4, 256, good, n - 1, None) == bq.E_CAPACITY
+    assert bq._lib.bitq_quantize_act_bits(good, bq.DT_BF16, 4, 256, 1, good, n, None) == bq.E_SHAPE
+    assert bq._lib.bitq_quantize_act_bits(good, bq.DT_BF16, 4, 256, 9, good, n, None) == bq.E_SHAPE
+    # WNAM takes an activation buffer and supports small M
+    dw = bq.wdesc(bq.WNAM, 128, 256, planes=3, abits=4)
+    assert bq.workspace_size(dw, 1) == 0
+    assert bq._lib.bitq_gemv(ctypes.byref(dw), good, good, bq.DT_BF16, good, None, 0, 0, None) == bq.E_ARG
+    assert bq._lib.bitq_gemm_smallM(ctypes.byref(dw), good, good, 65, good, None, 0, 0, None) == bq.E_SHAPE
 
 
 def test_act_size_matches_documented_layout():

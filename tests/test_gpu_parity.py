@@ -27,9 +27,9 @@ def _need_gpu():
 
 
 # ======================================================= activation quantizer
-def _check_act(x_store, x_f32, M, K):
-    act, got = quantize_act_dev(x_store, M, K)
-    q, d = oact.quantize(x_f32)
+def _check_act(x_store, x_f32, M, K, abits=8):
+    act, got = quantize_act_dev(x_store, M, K, abits)
+    q, d = oact.quantize(x_f32, abits)
     assert np.array_equal(got["q"][:, :K], q), "q"
     assert np.all(got["q"][:, K:] == 0), "q padding"
     assert np.array_equal(got["d"].view(np.uint32), d.view(np.uint32)), "d"
@@ -50,6 +50,16 @@ def test_act_quant_bitexact_bf16(M, K):
         bits[1] = 0                                           # an all-zero token
         xf[1] = 0
     _check_act(bits, xf, M, K)
+
+
+@pytest.mark.parametrize("abits", [2, 3, 4, 6, 7])
+def test_act_quant_bits_bitexact(abits):
+    say("act_quant bits", abits)
+    M, K = 5, 1056
+    bits, xf = synth.random_bf16(np.random.default_rng(abits), (M, K))
+    bits[2] = 0
+    xf[2] = 0
+    _check_act(bits, xf, M, K, abits)
 
 
 def test_act_quant_ties_and_f32():
@@ -239,6 +249,61 @@ def test_w2a8_batch_invariance_and_determinism():
         act1, _ = quantize_act_dev(xs[m:m + 1], 1, K)
         y1 = run_gemv(desc, bd, act1, bq.DT_ACT, 1, ws=ws1)
         assert np.array_equal(y1[0].view(np.uint32), y16a[m].view(np.uint32)), f"token {m}"
+
+
+# ===================================================================== WnAm
+def _wnam_case(N, K, M, n, m, W, xs, xf, rows=None):
+    """n-bit weights (oracle RTN, library packer) x m-bit activations (library
+    quantizer, checked against the oracle's): exact group partials A and the
+    float output within tolerance."""
+    q, d = oact.quantize(xf, m)
+    act, got = quantize_act_dev(xs, M, K, m)
+    assert np.array_equal(got["q"][:, :K], q) and np.array_equal(got["d"].view(np.uint32), d.view(np.uint32))
+    qw, delta, zero = ow.quantize_wnam(W, n)
+    desc = bq.wdesc(bq.WNAM, N, K, planes=n, abits=m)
+    bd = dev_blob(bq.pack_weights(desc, code=qw, delta=delta, zero=zero))
+    r = np.arange(N) if rows is None else rows
+    G = K // 128
+    A = run_gemv(desc, bd, act, bq.DT_ACT, M, bq.F_ACC_INT32, M * N * G).reshape(M, N, G)
+    assert np.array_equal(A[:, r], og.w2a8_int(qw[r], q)), f"wnam A n={n} m={m}"
+    y = run_gemv(desc, bd, act, bq.DT_ACT, M)
+    y_ref, tol = og.gemv_w2a8(qw[r], delta[r], zero[r], q, d)
+    return assert_within(y[:, r], y_ref, tol, f"wnam W{n}A{m} {N}x{K} M={M}"), y
+
+
+@pytest.mark.parametrize("n,m", [(1, 8), (2, 4), (3, 3), (4, 4), (4, 2), (3, 6), (2, 8)])
+@pytest.mark.parametrize("N,K,M", [(200, 512, 1), (70, 1152, 4), (130, 4096, 1)])
+def test_wnam_gemv(n, m, N, K, M):
+    say("wnam", n, m, N, K, M)
+    W = synth.gaussian_f32(np.random.default_rng(N + K + n), (N, K), 0.02)
+    xs, xf = synth.activations("w2a8", 0, M, K)
+    _wnam_case(N, K, M, n, m, W, xs, xf)
+
+
+def test_wnam_w2_a8_equals_w2a8():
+    """W2A8 through the WnAm kernel (n = 2, m = 8) gives the W2A8 kernel's
+    output bit for bit."""
+    N, K = 1000, 2048
+    say("wnam W2A8 vs w2a8", N, K)
+    W = synth.gaussian_f32(np.random.default_rng(11), (N, K), 0.02)
+    xs, xf = synth.activations("w2a8", 0, 1, K)
+    qw, delta, zero = ow.quantize_w2a8(W)
+    act, _ = quantize_act_dev(xs, 1, K)
+    dw = bq.wdesc(bq.W2A8, N, K)
+    dn = bq.wdesc(bq.WNAM, N, K, planes=2, abits=8)
+    y1 = run_gemv(dw, dev_blob(bq.pack_weights(dw, code=qw, delta=delta, zero=zero)), act, bq.DT_ACT)
+    y2 = run_gemv(dn, dev_blob(bq.pack_weights(dn, code=qw, delta=delta, zero=zero)), act, bq.DT_ACT)
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
+@pytest.mark.parametrize("n,m,M", [(4, 4, 1), (3, 8, 1), (2, 4, 16)])
+def test_wnam_workload(n, m, M):
+    N, K = 11008, 4096
+    say("wnam workload", n, m, N, K, M)
+    W = synth.weights("w2a8", 1, N, K)
+    xs, xf = synth.activations("w2a8", 1, M, K)
+    rows = np.sort(np.random.default_rng(n * m).choice(N, 512, replace=False))
+    _wnam_case(N, K, M, n, m, W, xs, xf, rows=rows)
 
 
 # ===================================================================== BVSR

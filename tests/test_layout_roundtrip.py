@@ -95,3 +95,27 @@ def test_sections_are_256_aligned():
         h = layout.parse_header(blob)
         for k in ("off_planes", "off_c0", "off_c1", "total"):
             assert h[k] % 256 == 0
+
+
+@pytest.mark.parametrize("N,K", [(64, 128), (130, 384)])
+@pytest.mark.parametrize("n", [1, 2, 3, 4])
+def test_roundtrip_wnam(N, K, n):
+    q, delta, zero = ow.quantize_wnam(_w(N, K), n)
+    d = bq.wdesc(bq.WNAM, N, K, planes=n, abits=4)
+    blob = bq.pack_weights(d, code=q, delta=delta, zero=zero)
+    out = layout.unpack(blob)
+    assert out["format"] == "wnam" and out["header"]["P"] == n and out["pad_ok"]
+    assert np.array_equal(out["q"], q)
+    assert np.array_equal(out["delta"].view(np.uint16), delta.view(np.uint16))
+    assert np.array_equal(out["zero"].view(np.uint16), zero.view(np.uint16))
+
+
+@pytest.mark.parametrize("n", [1, 3, 4])
+def test_library_wnam_quantizer_matches_oracle(n):
+    W = _w(96, 512, seed=5)
+    d = bq.wdesc(bq.WNAM, 96, 512, planes=n, abits=6)
+    out = layout.unpack(bq.quantize_weights(d, W))
+    q, delta, zero = ow.quantize_wnam(W, n)
+    assert np.array_equal(out["q"], q)
+    assert np.array_equal(out["delta"].view(np.uint16), delta.view(np.uint16))
+    assert np.array_equal(out["zero"].view(np.uint16), zero.view(np.uint16))
