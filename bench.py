@@ -58,7 +58,9 @@ def kernels_sha() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 # Algorithmic packed bytes of one layer (planes + coefficients), by format.
-def packed_bytes(fmt: str, N: int, K: int) -> int:
+def packed_bytes(fmt: str, N: int, K: int, planes: int = 2) -> int:
+    if fmt == "wnam":
+        return planes * N * K // 8 + 4 * N * (K // 128)
     if fmt == "rabit":
         return 2 * N * K // 8 + 2 * 2 * N + 2 * 2 * K
     if fmt == "w2a8":
@@ -79,6 +81,10 @@ WORKLOADS = {
     "w2a8_down": dict(fmt="w2a8", shape_idx=2, N=4096, K=11008),
     "bvsr": dict(fmt="bvsr", shape_idx=1, N=28672, K=8192),
     "ternary": dict(fmt="ternary", shape_idx=3, N=4096, K=4096),
+    # arbitrary-bit WnAm on the W2A8 layer's data (n weight planes, m-bit activations)
+    "w4a4": dict(fmt="wnam", planes=4, abits=4, data="w2a8", shape_idx=1, N=11008, K=4096),
+    "w2a4": dict(fmt="wnam", planes=2, abits=4, data="w2a8", shape_idx=1, N=11008, K=4096),
+    "w3a8": dict(fmt="wnam", planes=3, abits=8, data="w2a8", shape_idx=1, N=11008, K=4096),
 }
 
 
@@ -90,11 +96,12 @@ def cpu_baseline(wl: dict, budget_s: float = 12.0) -> dict:
     """The oracle as it stands, timed on the host: explicit fp64 dequantization
     and dot product for one GEMV of the workload layer, repeated until about
     `budget_s` seconds of CPU work (at least once)."""
-    from oracle import act as oact, gemv as og, weights as ow
+    from oracle import act as oact, gemv as og, layout, weights as ow
     import synth
     fmt, N, K, si = wl["fmt"], wl["N"], wl["K"], wl["shape_idx"]
-    W = synth.weights(fmt, si, N, K)
-    xs, xf = synth.activations(fmt, si, 1, K)
+    data = wl.get("data", fmt)
+    W = synth.weights(data, si, N, K)
+    xs, xf = synth.activations(data, si, 1, K)
     if fmt == "rabit":
         # the GEMV step only: the logical form is built once, outside the timing
         B, g, h = ow.quantize_rabit(W)
@@ -106,6 +113,27 @@ def cpu_baseline(wl: dict, budget_s: float = 12.0) -> dict:
             q, d = oact.quantize(xf)
             return og.gemv_w2a8(qw, delta, zero, q, d)
         what = "oracle act quantize + gemv_w2a8 (fp64 dequant + dot)"
+    elif fmt == "wnam":
+        qw, delta, zero = ow.quantize_wnam(W, wl["planes"])
+        def run():
+            q, d = oact.quantize(xf, wl["abits"])
+            return og.gemv_w2a8(qw, delta, zero, q, d)
+        what = f"oracle {wl['abits']}-bit act quantize + W{wl['planes']} gemv (fp64 dequant + dot)"
+    elif fmt == "ternary":
+        T, gamma = ow.quantize_ternary(W)
+        def run():
+            q, d = oact.quantize(xf)
+            return og.gemv_ternary(T, gamma, q, d)
+        what = "oracle act quantize + gemv_ternary (fp64 dequant + dot)"
+    elif fmt == "bvsr":
+        # logical form from the library's quantizer (the oracle's exhaustive
+        # search is far too slow at this size), read back by the oracle
+        import bit_plane_gemv_amd as bq
+        L = layout.unpack(bq.quantize_weights(bq.wdesc("bvsr", N, K), W))
+        def run():
+            q, d = oact.quantize(xf)
+            return og.gemv_bvsr(L["code"], L["idx"], L["cache"], q, d)
+        what = "oracle act quantize + gemv_bvsr (fp64 dequant + dot)"
     else:
         raise ValueError(fmt)
     try:
@@ -122,7 +150,8 @@ def cpu_baseline(wl: dict, budget_s: float = 12.0) -> dict:
         if time.perf_counter() - t_all > budget_s or len(times) >= 50:
             break
     med = float(np.median(times))
-    return {"value": packed_bytes(fmt, N, K) / med / 1e9, "unit": "GB/s", "cores": int(threads),
+    return {"value": packed_bytes(fmt, N, K, wl.get("planes", 2)) / med / 1e9, "unit": "GB/s",
+            "cores": int(threads),
             "kind": "oracle",
             "sample": f"{what}, {fmt} {N}x{K} M=1, {len(times)} runs, median {med * 1e3:.1f} ms "
                       f"per GEMV; host has {os.cpu_count()} cpus"}
@@ -153,11 +182,13 @@ def main():
 
     # ---- weights: library quantizer + packer (offline, untimed)
     t0 = time.perf_counter()
-    W = synth.weights(fmt, si, N, K)
-    desc = bq.wdesc(fmt, N, K)
+    data = wl.get("data", fmt)
+    W = synth.weights(data, si, N, K)
+    desc = bq.wdesc(fmt, N, K, planes=wl.get("planes"), abits=wl.get("abits"))
+    abits = wl.get("abits", 8)
     blob = bq.quantize_weights(desc, W)
     log(f"quantized+packed {fmt} {N}x{K} in {time.perf_counter() - t0:.1f}s, blob {blob.nbytes} B")
-    alg_bytes = packed_bytes(fmt, N, K)
+    alg_bytes = packed_bytes(fmt, N, K, wl.get("planes", 2))
     copies = max(2, math.ceil(ROTATE_BYTES / blob.nbytes))
     base = torch.empty(blob.nbytes, dtype=torch.uint8, device=dev)
     base.copy_(torch.from_numpy(blob))
@@ -169,18 +200,18 @@ def main():
     blobs = [pool[c * stride:c * stride + blob.nbytes] for c in range(copies)]
 
     # ---- activations / outputs / workspace
-    xs, xf = synth.activations(fmt, si, 1, K)
+    xs, xf = synth.activations(data, si, 1, K)
     x = torch.from_numpy(np.ascontiguousarray(xs).view(np.int16)).to(dev)
     y = torch.empty(N, dtype=torch.float32, device=dev)
     ws = torch.zeros(bq.workspace_size(desc, 1), dtype=torch.uint8, device=dev)
-    integer = fmt in ("ternary", "w2a8", "bvsr")
+    integer = fmt in ("ternary", "w2a8", "bvsr", "wnam")
     act = torch.zeros(bq.act_size(1, K), dtype=torch.uint8, device=dev) if integer else None
     stream = torch.cuda.current_stream()
 
     def step(i):
         w = blobs[i % copies]
         if integer:
-            bq.quantize_act(x, bq.DT_BF16, 1, K, act, stream=stream)
+            bq.quantize_act(x, bq.DT_BF16, 1, K, act, stream=stream, abits=abits)
             bq.gemv(desc, w, act, bq.DT_ACT, y, ws, stream=stream)
         else:
             bq.gemv(desc, w, x, bq.DT_BF16, y, ws, stream=stream)
@@ -265,10 +296,11 @@ def main():
         "vs_baseline": None,
         "dtype": "f32" if fmt in ("rabit", "sign") else "int32",
         "data": "synthetic",
-        "config": {"workload": f"{fmt} {N}x{K} M=1 ({'RaBiT 2-path residual binary, bf16 x' if fmt == 'rabit' else fmt})",
+        "config": {"workload": f"{args.workload} {N}x{K} M=1 ({'RaBiT 2-path residual binary, bf16 x' if fmt == 'rabit' else fmt})",
                    "N": N, "K": K, "M": 1, "format": fmt, "packed_bytes": alg_bytes,
                    "rotating_copies": copies, "rotating_bytes": copies * stride,
-                   "graph_replay": graph is not None, "host_wall_s": round(wall, 4)},
+                   "graph_replay": graph is not None, "host_wall_s": round(wall, 4),
+                   **({"weight_bits": wl["planes"], "act_bits": abits} if fmt == "wnam" else {})},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "traffic_bytes_per_launch": mt["bytes_per_launch"] if traffic is not None else None,

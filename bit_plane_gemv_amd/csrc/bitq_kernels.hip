@@ -671,39 +671,39 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
                         yacc += delta * (static_cast<float>(A) - z * static_cast<float>(S128));
                     }
                 } else if (FMT == BITQ_WNAM) {
-                    // n = P weight planes, m = abits activation planes: planes
-                    // 0..m-2 with weights 2^j and the sign plane 7 with weight
-                    // -2^(m-1) (bits m-1..6 of an m-bit code are sign copies)
-                    int a[P][8];
+                    // n = P weight planes, m = abits activation planes: the sign
+                    // plane 7 (weight -2^(m-1)), then planes m-2 .. 0 in a loop
+                    // of m - 1 steps (bits m-1..6 of an m-bit code are sign
+                    // copies), Horner-accumulated per weight plane:
+                    //   r_i = -c_i7, then r_i = 2 r_i + c_ij,  c_ij = sum_w popc(W_i & X_j)
+                    uint32_t wi[P][4];
 #pragma unroll
-                    for (int i = 0; i < P; ++i)
-#pragma unroll
-                        for (int jj = 0; jj < 8; ++jj) a[i][jj] = 0;
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) {
-                        const uint4 x0 = *reinterpret_cast<const uint4*>(xa + 8 * w);
-                        const uint4 x1 = *reinterpret_cast<const uint4*>(xa + 8 * w + 4);
-                        const uint32_t xj[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-                        uint32_t wi[P];
-#pragma unroll
-                        for (int i = 0; i < P; ++i) wi[i] = (&wv[j][i].x)[w];
-#pragma unroll
-                        for (int jj = 0; jj < 7; ++jj)
-                            if (jj < abits - 1)  // uniform
-#pragma unroll
-                                for (int i = 0; i < P; ++i) a[i][jj] = bcnt_acc(wi[i] & xj[jj], a[i][jj]);
-#pragma unroll
-                        for (int i = 0; i < P; ++i) a[i][7] = bcnt_acc(wi[i] & xj[7], a[i][7]);
+                    for (int i = 0; i < P; ++i) {
+                        wi[i][0] = wv[j][i].x; wi[i][1] = wv[j][i].y; wi[i][2] = wv[j][i].z; wi[i][3] = wv[j][i].w;
                     }
-                    int A = 0;
+                    int r[P];
 #pragma unroll
-                    for (int i = P - 1; i >= 0; --i) {
-                        int r = -a[i][7];
+                    for (int i = 0; i < P; ++i) {
+                        int c = 0;
 #pragma unroll
-                        for (int jj = 6; jj >= 0; --jj)
-                            if (jj < abits - 1) r = 2 * r + a[i][jj];
-                        A = 2 * A + r;
+                        for (int w = 0; w < 4; ++w) c = bcnt_acc(wi[i][w] & xa[8 * w + 7], c);
+                        r[i] = -c;
                     }
+                    for (int jj = abits - 2; jj >= 0; --jj) {
+                        uint32_t xw[4];
+#pragma unroll
+                        for (int w = 0; w < 4; ++w) xw[w] = xa[8 * w + jj];
+#pragma unroll
+                        for (int i = 0; i < P; ++i) {
+                            int c = 0;
+#pragma unroll
+                            for (int w = 0; w < 4; ++w) c = bcnt_acc(wi[i][w] & xw[w], c);
+                            r[i] = 2 * r[i] + c;
+                        }
+                    }
+                    int A = r[P - 1];
+#pragma unroll
+                    for (int i = P - 2; i >= 0; --i) A = 2 * A + r[i];
                     if (ACC) {
                         if (n < N) reinterpret_cast<int32_t*>(y)[(static_cast<size_t>(m) * N + n) * NB + b] = A;
                     } else {
