@@ -72,3 +72,26 @@ def planes(q: np.ndarray) -> np.ndarray:
     """Activation bit-planes packed as words: [8, M, K/32] uint32 (plane j =
     bit j of the two's-complement byte, bit i of word w <-> channel 32w+i)."""
     return bitserial.pack_bits(bitserial.act_planes(q))
+
+
+def binarize(x_f32: np.ndarray):
+    """Binary activations of the fully binary path ([BitNet] §2.1 sign with
+    the tie at 0 going to +1; §2.3 XNOR+popcount product): x_b = sign(x) in
+    {-1, +1} and a per-token scale beta = mean_k |x_k| (fp64; the page gives
+    only the weight scale, beta is the reading taken so that beta * x_b
+    approximates x).  Returns (x_b int8 [M, K], beta float64 [M])."""
+    x = np.asarray(x_f32, dtype=np.float32)
+    assert x.ndim == 2
+    xb = np.where(x >= 0, 1, -1).astype(np.int8)           # -0.0 >= 0: +1
+    beta = np.abs(x.astype(np.float64)).mean(axis=1)
+    return xb, beta
+
+
+def binary_words(xb: np.ndarray, Kp: int | None = None) -> np.ndarray:
+    """Sign bits packed LSB first (1 <-> +1), zero bits past K up to Kp:
+    [M, Kp/32] uint32."""
+    M, K = xb.shape
+    Kp = K if Kp is None else Kp
+    bits = np.zeros((M, Kp), dtype=np.uint8)
+    bits[:, :K] = (np.asarray(xb) > 0)
+    return bitserial.pack_bits(bits)

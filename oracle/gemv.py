@@ -89,6 +89,19 @@ def gemv_rabit(B, g, h, x):
     return _chunked_matmul(lambda a, b: deq_rabit(B, g, h, a, b), B.shape[1], x)
 
 
+def gemv_xnor(B, alpha, xb, beta):
+    """Fully binary product ([BitNet] §2.3): y = alpha (.) beta (B x_b) with
+    x_b in {-1,+1}; returns (y, tol).  The dequantized operands are alpha B and
+    beta x_b."""
+    xhat = np.asarray(xb, dtype=np.float64) * np.asarray(beta, dtype=np.float64)[:, None]
+    return _chunked_matmul(lambda a, b: deq_sign(B, alpha, a, b), B.shape[0], xhat)
+
+
+def xnor_int(B, xb):
+    """Y[m, n] = sum_k B[n,k] x_b[m,k] (int64, exact)."""
+    return np.asarray(xb, dtype=np.int64) @ np.asarray(B, dtype=np.int64).T
+
+
 def act_hat(q, d):
     """x^ = q * d, the activation the integer paths multiply."""
     return q.astype(np.float64) * np.asarray(d, dtype=np.float64)[:, None]
