@@ -48,7 +48,7 @@ if len(_hip_runtimes()) > 1:
 # ------------------------------------------------------------------ enums
 OK, E_ARG, E_SHAPE, E_ALIGN, E_UNSUPPORTED, E_CAPACITY, E_DEVICE = 0, -1, -2, -3, -4, -5, -6
 SIGN1, RABIT, TERNARY, W2A8, BVSR4, WNAM = 1, 2, 3, 4, 5, 6
-DT_F32, DT_BF16, DT_ACT = 0, 1, 2
+DT_F32, DT_BF16, DT_ACT, DT_BINARY = 0, 1, 2, 3
 F_ACC_INT32 = 1
 
 FORMAT_NAMES = {SIGN1: "sign", RABIT: "rabit", TERNARY: "ternary", W2A8: "w2a8", BVSR4: "bvsr",
@@ -90,6 +90,8 @@ _sigs = {
     "bitq_act_size": ([_I32, _I32, ctypes.POINTER(_SZ)], _I32),
     "bitq_quantize_act": ([_P, _I32, _I32, _I32, _P, _SZ, _P], _I32),
     "bitq_quantize_act_bits": ([_P, _I32, _I32, _I32, _I32, _P, _SZ, _P], _I32),
+    "bitq_binact_size": ([_I32, _I32, ctypes.POINTER(_SZ)], _I32),
+    "bitq_binarize_act": ([_P, _I32, _I32, _I32, _P, _SZ, _P], _I32),
     "bitq_workspace_size": ([ctypes.POINTER(WDesc), _I32, ctypes.POINTER(_SZ)], _I32),
     "bitq_gemv": ([ctypes.POINTER(WDesc), _P, _P, _I32, _P, _P, _SZ, _U32, _P], _I32),
     "bitq_gemm_smallM": ([ctypes.POINTER(WDesc), _P, _P, _I32, _P, _P, _SZ, _U32, _P], _I32),
@@ -192,6 +194,21 @@ def act_size(M: int, K: int) -> int:
     return n.value
 
 
+def binact_size(M: int, K: int) -> int:
+    n = _SZ(0)
+    _check(_lib.bitq_binact_size(M, K, ctypes.byref(n)))
+    return n.value
+
+
+def binact_layout(M: int, K: int) -> dict:
+    """Section offsets of a binary activation buffer (as include/bitq.h)."""
+    Kp = (K + 127) // 128 * 128
+    Kw = Kp // 32
+    a = lambda v: (v + 255) // 256 * 256
+    off_beta = a(4 * M * Kw)
+    return dict(Kp=Kp, Kw=Kw, off_bits=0, off_beta=off_beta, total=a(off_beta + 4 * M))
+
+
 def workspace_size(desc: WDesc, M: int = 1) -> int:
     n = _SZ(0)
     _check(_lib.bitq_workspace_size(ctypes.byref(desc), M, ctypes.byref(n)))
@@ -199,6 +216,11 @@ def workspace_size(desc: WDesc, M: int = 1) -> int:
 
 
 # ------------------------------------------------------------ device calls
+def binarize_act(x, x_dtype: int, M: int, K: int, act, act_bytes: int | None = None, stream=None):
+    nbytes = act.numel() * act.element_size() if act_bytes is None else act_bytes
+    _check(_lib.bitq_binarize_act(_ptr(x), x_dtype, M, K, _ptr(act), nbytes, _stream(stream)))
+
+
 def quantize_act(x, x_dtype: int, M: int, K: int, act, act_bytes: int | None = None, stream=None,
                  abits: int = 8):
     nbytes = act.numel() * act.element_size() if act_bytes is None else act_bytes
@@ -209,16 +231,21 @@ def quantize_act(x, x_dtype: int, M: int, K: int, act, act_bytes: int | None = N
                                            _stream(stream)))
 
 
+def _nbytes(buf) -> int:
+    """Size of a device buffer (0 for None: calls that need no workspace)."""
+    return 0 if buf is None else buf.numel() * buf.element_size()
+
+
 def gemv(desc: WDesc, w, x, x_dtype: int, y, ws, ws_bytes: int | None = None, flags: int = 0,
          stream=None):
-    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    nbytes = _nbytes(ws) if ws_bytes is None else ws_bytes
     _check(_lib.bitq_gemv(ctypes.byref(desc), _ptr(w), _ptr(x), x_dtype, _ptr(y), _ptr(ws),
                           nbytes, flags, _stream(stream)))
 
 
 def gemm_smallM(desc: WDesc, w, act, M: int, y, ws, ws_bytes: int | None = None, flags: int = 0,
                 stream=None):
-    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    nbytes = _nbytes(ws) if ws_bytes is None else ws_bytes
     _check(_lib.bitq_gemm_smallM(ctypes.byref(desc), _ptr(w), _ptr(act), M, _ptr(y), _ptr(ws),
                                  nbytes, flags, _stream(stream)))
 

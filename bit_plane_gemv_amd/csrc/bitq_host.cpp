@@ -617,6 +617,17 @@ ActLayout act_layout(int M, int K) {
     return A;
 }
 
+BinActLayout binact_layout(int M, int K) {
+    BinActLayout A{};
+    A.M = M;
+    A.K = K;
+    A.Kp = round_up(K, kKBlock);
+    A.Kw = A.Kp / 32;
+    A.off_beta = align256(4 * static_cast<size_t>(M) * A.Kw);
+    A.total = align256(A.off_beta + 4 * static_cast<size_t>(M));
+    return A;
+}
+
 Plan make_plan(const bitq_wdesc& d, int M) {
     Plan p{};
     const bool lut = (d.fmt == BITQ_SIGN1 || d.fmt == BITQ_RABIT);
@@ -814,6 +825,34 @@ bitq_status bitq_quantize_act_bits(const void* x_dev, int32_t x_dtype, int32_t M
     return ok();
 }
 
+bitq_status bitq_binact_size(int32_t M, int32_t K, size_t* bytes) {
+    if (!bytes) return fail(BITQ_E_ARG, "bytes is NULL");
+    if (M < 1 || M > 64) return fail(BITQ_E_SHAPE, "M=%d out of range [1, 64]", M);
+    if (K < 32 || K > (1 << 20) || K % 32) return fail(BITQ_E_SHAPE, "K=%d must be a multiple of 32 in [32, 2^20]", K);
+    *bytes = binact_layout(M, K).total;
+    return ok();
+}
+
+bitq_status bitq_binarize_act(const void* x_dev, int32_t x_dtype, int32_t M, int32_t K, void* act_dev,
+                              size_t act_bytes, void* stream) {
+    size_t need = 0;
+    bitq_status s = bitq_binact_size(M, K, &need);
+    if (s) return s;
+    if (!x_dev || !act_dev) return fail(BITQ_E_ARG, "x_dev/act_dev is NULL");
+    if (x_dtype != BITQ_DT_F32 && x_dtype != BITQ_DT_BF16)
+        return fail(BITQ_E_ARG, "x_dtype must be BITQ_DT_F32 or BITQ_DT_BF16");
+    if (!aligned(x_dev, 4)) return fail(BITQ_E_ALIGN, "x_dev must be 4-byte aligned");
+    if (!aligned(act_dev, 256)) return fail(BITQ_E_ALIGN, "act_dev must be 256-byte aligned");
+    if (act_bytes < need) return fail(BITQ_E_CAPACITY, "binary activation buffer has %zu bytes, needs %zu", act_bytes, need);
+    int is950 = 0;
+    int e = current_device_is_gfx950(&is950);
+    if (e) return fail(BITQ_E_DEVICE, "HIP error %d while querying the device", e);
+    if (!is950) return fail(BITQ_E_UNSUPPORTED, "current device is not gfx950");
+    e = launch_binarize_act(x_dev, x_dtype, M, K, act_dev, stream);
+    if (e) return fail(BITQ_E_DEVICE, "HIP launch error %d", e);
+    return ok();
+}
+
 bitq_status bitq_workspace_size(const bitq_wdesc* desc, int32_t M, size_t* bytes) {
     bitq_status s = check_desc(desc);
     if (s) return s;
@@ -831,6 +870,21 @@ static bitq_status gemv_common(const bitq_wdesc* desc, const void* w_dev, const 
     const bitq_wdesc d = *desc;
     if (!w_dev || !x_dev || !y_dev) return fail(BITQ_E_ARG, "a device pointer is NULL");
     if (flags & ~BITQ_F_ACC_INT32) return fail(BITQ_E_ARG, "unknown flags 0x%x", flags);
+    const bool binary = x_dtype == BITQ_DT_BINARY;
+    if (binary) {  // fully binary XNOR path: SIGN1 weights x sign activations
+        if (d.fmt != BITQ_SIGN1)
+            return fail(BITQ_E_UNSUPPORTED, "binary activations (BITQ_DT_BINARY) need the SIGN1 format");
+        if (!aligned(x_dev, 256)) return fail(BITQ_E_ALIGN, "binary activation buffer must be 256-byte aligned");
+        if (!aligned(w_dev, 256)) return fail(BITQ_E_ALIGN, "w_dev must be 256-byte aligned");
+        if (!aligned(y_dev, 4)) return fail(BITQ_E_ALIGN, "y_dev must be 4-byte aligned");
+        int is950 = 0;
+        int e = current_device_is_gfx950(&is950);
+        if (e) return fail(BITQ_E_DEVICE, "HIP error %d while querying the device", e);
+        if (!is950) return fail(BITQ_E_UNSUPPORTED, "current device is not gfx950");
+        e = launch_gemv_xnor(d, w_dev, x_dev, M, y_dev, flags, stream);
+        if (e) return fail(BITQ_E_DEVICE, "HIP launch error %d", e);
+        return ok();
+    }
     const bool float_fmt = (d.fmt == BITQ_SIGN1 || d.fmt == BITQ_RABIT);
     if (float_fmt) {
         if (M != 1) return fail(BITQ_E_UNSUPPORTED, "SIGN1/RABIT support M = 1 only");
@@ -873,10 +927,12 @@ bitq_status bitq_gemm_smallM(const bitq_wdesc* desc, const void* w_dev, const vo
                              float* y_dev, void* ws_dev, size_t ws_bytes, uint32_t flags, void* stream) {
     bitq_status s = check_desc(desc);
     if (s) return s;
-    if (desc->fmt == BITQ_SIGN1 || desc->fmt == BITQ_RABIT)
-        return fail(BITQ_E_UNSUPPORTED, "bitq_gemm_smallM supports TERNARY, W2A8, BVSR4 and WNAM");
+    if (desc->fmt == BITQ_RABIT)
+        return fail(BITQ_E_UNSUPPORTED, "bitq_gemm_smallM supports SIGN1 (binary activations), TERNARY, W2A8, "
+                                        "BVSR4 and WNAM");
     if (M < 2 || M > 64) return fail(BITQ_E_SHAPE, "M=%d out of range [2, 64]", M);
-    return gemv_common(desc, w_dev, act_dev, BITQ_DT_ACT, M, y_dev, ws_dev, ws_bytes, flags, stream);
+    const int32_t dt = desc->fmt == BITQ_SIGN1 ? BITQ_DT_BINARY : BITQ_DT_ACT;
+    return gemv_common(desc, w_dev, act_dev, dt, M, y_dev, ws_dev, ws_bytes, flags, stream);
 }
 
 }  // extern "C"

@@ -36,6 +36,13 @@ struct ActLayout {
 };
 ActLayout act_layout(int M, int K);
 
+// Byte layout of a binary activation buffer (see bitq_binarize_act).
+struct BinActLayout {
+    int64_t M, K, Kp, Kw;
+    size_t off_beta, total;
+};
+BinActLayout binact_layout(int M, int K);
+
 // How a GEMV/GEMM call is split over workgroups, and its workspace.
 struct Plan {
     int waves_per_wg;      // 64-row waves per workgroup
@@ -57,6 +64,9 @@ int launch_gemv_float(const bitq_wdesc& d, const Plan& plan, const void* w, cons
                       int x_dtype, float* y, void* ws, void* stream);
 int launch_gemv_int(const bitq_wdesc& d, const Plan& plan, const void* w, const void* act,
                     int M, float* y, void* ws, uint32_t flags, void* stream);
+int launch_binarize_act(const void* x, int x_dtype, int M, int K, void* act, void* stream);
+int launch_gemv_xnor(const bitq_wdesc& d, const void* w, const void* act, int M, float* y, uint32_t flags,
+                     void* stream);
 
 // Device checks (bitq_kernels.hip): is the current device a gfx950?
 int current_device_is_gfx950(int* is_gfx950);

@@ -785,6 +785,112 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
     for (int m = 1; m < M; ++m) pass(m, false);
 }
 
+// ================================================== binary activations (XNOR)
+// [BitNet] §2.1 sign with the tie at 0 going to +1 (so -0.0 -> +1): one bit
+// per input, 1 <-> +1, LSB first, zero bits past K.  beta = mean_k |x_k| is
+// the per-token scale of the fully binary product (workgroup 0 of each token
+// sums the row in a fixed order).  Grid (words / 8, M), 256 lanes: each wave
+// turns 64 inputs into two words with one ballot.
+template <int DT>
+__global__ __launch_bounds__(256) void binarize_act_kernel(const void* __restrict__ x, int K, int Kw,
+                                                           uint32_t* __restrict__ bits, float* __restrict__ beta) {
+    __shared__ float s_sum[4];
+    const int m = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const size_t row = static_cast<size_t>(m) * K;
+    const int w0 = 8 * blockIdx.x + 2 * wave;
+    const int k = 32 * w0 + lane;
+    const bool pos = k < K && act_at<DT>(x, row + min(k, K - 1)) >= 0.0f;
+    const uint64_t b = __ballot(pos);
+    if (w0 < Kw) {
+        if (lane == 0) bits[static_cast<size_t>(m) * Kw + w0] = static_cast<uint32_t>(b);
+        if (lane == 32 && w0 + 1 < Kw) bits[static_cast<size_t>(m) * Kw + w0 + 1] = static_cast<uint32_t>(b >> 32);
+    }
+    if (blockIdx.x != 0) return;
+    float sum = 0.0f;
+    for (int i = tid; i < K; i += 256) sum += fabsf(act_at<DT>(x, row + i));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+    if (lane == 0) s_sum[wave] = sum;
+    __syncthreads();
+    if (tid == 0) beta[m] = ((s_sum[0] + s_sum[1]) + (s_sum[2] + s_sum[3])) / static_cast<float>(K);
+}
+
+// ====================================================== XNOR+popcount GEMV
+// [BitNet] §2.3: with both operands in {-1,+1} as sign bits (1 <-> +1),
+//   Y[m,n] = sum_k B[n,k] x_b[m,k] = K - 2 popcount(bits(B_n) XOR bits(x_m))
+// (the page prints popcount(xnor) times the scale; the affine map makes it
+// the dot product), one XOR and one popcount-accumulate per 32 weights, and
+// y = alpha_n beta_m Y.  Zero padding bits of both operands agree, so only
+// the real K counts.  Workgroups as in the AND+popcount kernel (RG rows x
+// 256/RG k-groups, row groups of a tile on one XCD), k in rounds of G BPL
+// blocks; the sign words of x come straight from global memory (one 16-byte
+// load per block, the same for the RG lanes of a k-group).  Per-token counts
+// are added in LDS with integer atomics: exact and order-independent.
+template <bool ACC, int BPL, int RG>
+__global__ __launch_bounds__(256) void gemv_xnor_kernel(const uint8_t* __restrict__ blob, size_t off_c0,
+                                                        const uint8_t* __restrict__ act, size_t act_off_beta, int M,
+                                                        int N, int K, int Tb, float* __restrict__ y) {
+    constexpr int G = 256 / RG;
+    constexpr int Q = 64 / RG;
+    constexpr int NBW = G * BPL;  // k blocks per round
+    __shared__ int s_cnt[64][RG];
+    const int tid = threadIdx.x, r = tid % RG, g = tid / RG;
+    const int wg = blockIdx.x;
+    const int t = 8 * (wg / (8 * Q)) + (wg & 7);  // 64-row tile (XCD-aware, see the AND+popcount kernel)
+    const int quarter = (wg >> 3) % Q;
+    if (t >= (N + 63) / 64) return;               // padding workgroups of the last XCD round
+    const int rowin = RG * quarter + r;
+    const int NB = Tb;
+    for (int i = tid; i < 64 * RG; i += 256) (&s_cnt[0][0])[i] = 0;
+    __syncthreads();
+    const uint8_t* __restrict__ tile = blob + kHeaderBytes + static_cast<size_t>(t) * Tb * 1024;  // one plane
+    const uint4* __restrict__ xw = reinterpret_cast<const uint4*>(act);  // [M][Kw] words = [M][NB] uint4
+    const int rounds = (NB + NBW - 1) / NBW;
+    for (int rd = 0; rd < rounds; ++rd) {
+        const int b_base = rd * NBW;
+        uint4 xv[BPL], wv[BPL];
+#pragma unroll
+        for (int j = 0; j < BPL; ++j) xv[j] = xw[min(b_base + g + G * j, NB - 1)];  // token 0
+#pragma unroll
+        for (int j = 0; j < BPL; ++j)
+            wv[j] = *reinterpret_cast<const uint4*>(tile + static_cast<uint32_t>(min(b_base + g + G * j, NB - 1) * 1024 +
+                                                                                 rowin * 16));
+        for (int m = 0; m < M; ++m) {
+            if (m > 0) {
+#pragma unroll
+                for (int j = 0; j < BPL; ++j) xv[j] = xw[static_cast<size_t>(m) * NB + min(b_base + g + G * j, NB - 1)];
+            }
+            int c = 0;
+#pragma unroll
+            for (int j = 0; j < BPL; ++j) {
+                const uint32_t keep = b_base + g + G * j < NB ? 0xFFFFFFFFu : 0u;  // clamped duplicates add 0
+                c = bcnt_acc((wv[j].x ^ xv[j].x) & keep, c);
+                c = bcnt_acc((wv[j].y ^ xv[j].y) & keep, c);
+                c = bcnt_acc((wv[j].z ^ xv[j].z) & keep, c);
+                c = bcnt_acc((wv[j].w ^ xv[j].w) & keep, c);
+            }
+#pragma unroll
+            for (int sh = RG; sh < 64; sh *= 2) c += __shfl_xor(c, sh, 64);
+            if ((tid & 63) < RG) atomicAdd(&s_cnt[m][r], c);
+        }
+    }
+    __syncthreads();
+    const float* beta = reinterpret_cast<const float*>(act + act_off_beta);
+    for (int i = tid; i < M * RG; i += 256) {
+        const int m = i / RG, rr = i % RG;
+        const int n = 64 * t + RG * quarter + rr;
+        if (n >= N) continue;
+        const int Y = K - 2 * s_cnt[m][rr];
+        if (ACC) {
+            reinterpret_cast<int32_t*>(y)[static_cast<size_t>(m) * N + n] = Y;
+        } else {
+            const float alpha = reinterpret_cast<const float*>(blob + off_c0)[n];
+            y[static_cast<size_t>(m) * N + n] = (alpha * beta[m]) * static_cast<float>(Y);
+        }
+    }
+}
+
 // =============================================================== launchers
 namespace {
 std::atomic<int> g_arch_cache[64];
@@ -935,6 +1041,50 @@ static void launch_wnam(const bitq_wdesc& d, const Plan& pl, const BlobLayout& L
         case 3: launch_nr<BITQ_WNAM, 3, ACC>(d, pl, L, w, act, M, y, st); break;
         default: launch_nr<BITQ_WNAM, 4, ACC>(d, pl, L, w, act, M, y, st); break;
     }
+}
+
+int launch_binarize_act(const void* x, int x_dtype, int M, int K, void* act, void* stream) {
+    BinActLayout A = binact_layout(M, K);
+    uint8_t* base = static_cast<uint8_t*>(act);
+    auto* bits = reinterpret_cast<uint32_t*>(base);
+    auto* beta = reinterpret_cast<float*>(base + A.off_beta);
+    const int Kw = static_cast<int>(A.Kw);
+    const dim3 grid((Kw + 7) / 8, M);
+    if (x_dtype == BITQ_DT_F32)
+        hipLaunchKernelGGL(binarize_act_kernel<BITQ_DT_F32>, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
+                           x, K, Kw, bits, beta);
+    else
+        hipLaunchKernelGGL(binarize_act_kernel<BITQ_DT_BF16>, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
+                           x, K, Kw, bits, beta);
+    return static_cast<int>(hipGetLastError());
+}
+
+template <bool ACC, int BPL>
+static void launch_xnor_bpl(const bitq_wdesc& d, const BlobLayout& L, const void* w, const void* act, int M,
+                            float* y, hipStream_t st) {
+    constexpr int RG = 8;
+    BinActLayout A = binact_layout(M, d.K);
+    const int tiles = static_cast<int>(L.Tn);
+    const int groups = 8 * (64 / RG) * ((tiles + 7) / 8);
+    hipLaunchKernelGGL((gemv_xnor_kernel<ACC, BPL, RG>), dim3(groups), dim3(256), 0, st,
+                       static_cast<const uint8_t*>(w), L.off_c0, static_cast<const uint8_t*>(act), A.off_beta, M,
+                       d.N, d.K, static_cast<int>(L.Tb), y);
+}
+
+int launch_gemv_xnor(const bitq_wdesc& d, const void* w, const void* act, int M, float* y, uint32_t flags,
+                     void* stream) {
+    BlobLayout L = blob_layout(d);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool acc = (flags & BITQ_F_ACC_INT32) != 0;
+    const int64_t need = (L.Tb + 31) / 32;  // blocks per lane with 32 k-groups (8 rows per workgroup)
+    const int bpl = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;  // more k: rounds
+    switch (bpl) {
+        case 1: acc ? launch_xnor_bpl<true, 1>(d, L, w, act, M, y, st) : launch_xnor_bpl<false, 1>(d, L, w, act, M, y, st); break;
+        case 2: acc ? launch_xnor_bpl<true, 2>(d, L, w, act, M, y, st) : launch_xnor_bpl<false, 2>(d, L, w, act, M, y, st); break;
+        case 4: acc ? launch_xnor_bpl<true, 4>(d, L, w, act, M, y, st) : launch_xnor_bpl<false, 4>(d, L, w, act, M, y, st); break;
+        default: acc ? launch_xnor_bpl<true, 8>(d, L, w, act, M, y, st) : launch_xnor_bpl<false, 8>(d, L, w, act, M, y, st); break;
+    }
+    return static_cast<int>(hipGetLastError());
 }
 
 int launch_gemv_int(const bitq_wdesc& d, const Plan& pl, const void* w, const void* act, int M, float* y,

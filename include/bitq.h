@@ -84,7 +84,9 @@ typedef enum {
 typedef enum {
     BITQ_DT_F32 = 0,   /* raw fp32 activations [M, K] */
     BITQ_DT_BF16 = 1,  /* raw bf16 activations [M, K] (uint16 bit patterns) */
-    BITQ_DT_ACT = 2    /* an activation buffer written by bitq_quantize_act */
+    BITQ_DT_ACT = 2,   /* an activation buffer written by bitq_quantize_act */
+    BITQ_DT_BINARY = 3 /* a binary activation buffer written by bitq_binarize_act
+                          (SIGN1 weights only: the fully binary XNOR path) */
 } bitq_dtype;
 
 /* Flags of bitq_gemv / bitq_gemm_smallM. */
@@ -237,6 +239,28 @@ bitq_status bitq_quantize_act_bits(const void* x_dev, int32_t x_dtype, int32_t M
                                    int32_t abits, void* act_dev, size_t act_bytes, void* stream);
 
 /*
+ * Binary activation buffer (written by bitq_binarize_act, read by the SIGN1
+ * XNOR path).  Kp = K rounded up to 128, Kw = Kp / 32.  Sections, each at a
+ * multiple of 256 bytes:
+ *   bits u32 [M][Kw]  bit i of word w = [x[m][32w + i] >= 0] (1 <-> +1; zero
+ *                     past K)
+ *   beta f32 [M]      mean_k |x[m][k]| (fp32 sum in a fixed order, / K)
+ */
+bitq_status bitq_binact_size(int32_t M, int32_t K, size_t* bytes);
+
+/*
+ * Binary activations of the fully binary path ([BitNet] §2.1: sign(x) = +1
+ * for x >= 0, else -1; §2.3 XNOR+popcount product): the sign bits of every
+ * input and the per-token scale beta = mean |x| (the page gives the weight
+ * scale only; beta is the reading taken, so that beta sign(x) approximates x).
+ *   x_dev   device [M][K] fp32 or bf16, 4-byte aligned
+ *   act_dev device buffer of bitq_binact_size bytes, 256-byte aligned
+ * 1 <= M <= 64.  The bits are exact; beta is an fp32 sum.
+ */
+bitq_status bitq_binarize_act(const void* x_dev, int32_t x_dtype, int32_t M, int32_t K,
+                              void* act_dev, size_t act_bytes, void* stream);
+
+/*
  * Workspace for one bitq_gemv / bitq_gemm_smallM call (device memory, 256-byte
  * aligned).  SIGN1/RABIT layers whose k range is split over several
  * workgroups need one 64-bit word per row (Np words), in which the splits
@@ -256,7 +280,10 @@ bitq_status bitq_workspace_size(const bitq_wdesc* desc, int32_t M, size_t* bytes
  *   x_dev  SIGN1/RABIT: raw activations, BITQ_DT_F32 or BITQ_DT_BF16, 16-byte
  *          aligned.  TERNARY/W2A8/BVSR4/WNAM: an activation buffer from
  *          bitq_quantize_act (WNAM: bitq_quantize_act_bits with desc->abits)
- *          with M = 1 (x_dtype = BITQ_DT_ACT).
+ *          with M = 1 (x_dtype = BITQ_DT_ACT).  SIGN1 with x_dtype =
+ *          BITQ_DT_BINARY: a binary activation buffer from bitq_binarize_act
+ *          with M = 1 (the XNOR path; no workspace needed, ws_dev may be
+ *          NULL).
  *   y_dev  fp32 [N], 4-byte aligned.
  * Float formats ([RaBiT] §3.2 sign-apply instead of multiplies): y_n =
  *   sum_p g_p[n] sum_k B_p[n,k] h_p[k] x_k (SIGN1: alpha_n sum_k B[n,k] x_k),
@@ -273,9 +300,12 @@ bitq_status bitq_workspace_size(const bitq_wdesc* desc, int32_t M, size_t* bytes
  *           P[n,g,j] = sum_{k in g} beta_j[n,k] q_k, (c, b) = cache[idx[n,g]]
  *   WNAM    as W2A8 with n-bit codes and m-bit q: the AND+popcount runs over
  *           n weight planes and m activation planes only
+ * Fully binary path (SIGN1, BITQ_DT_BINARY; [BitNet] §2.3 XNOR+popcount):
+ *   y_n = alpha_n beta Y_n, Y_n = sum_k B[n,k] sign(x_k)
+ *       = K - 2 popcount(bits(B_n) XOR bits(x)), exact
  * flags & BITQ_F_ACC_INT32 (integer formats): y_dev receives, as int32,
- *   TERNARY Y [N]; W2A8/WNAM A [N][K/128]; BVSR4 P [N][K/32][4]; the buffer
- *   must hold that many int32 values.
+ *   TERNARY Y [N]; W2A8/WNAM A [N][K/128]; BVSR4 P [N][K/32][4]; SIGN1 with
+ *   binary activations Y [N]; the buffer must hold that many int32 values.
  */
 bitq_status bitq_gemv(const bitq_wdesc* desc, const void* w_dev, const void* x_dev,
                       int32_t x_dtype, float* y_dev, void* ws_dev, size_t ws_bytes,
@@ -283,8 +313,10 @@ bitq_status bitq_gemv(const bitq_wdesc* desc, const void* w_dev, const void* x_d
 
 /*
  * Small-batch GEMM y[M][N] = x W^T for 2 <= M <= 64, integer formats
- * (TERNARY, W2A8, BVSR4, WNAM), reading every weight once for all M tokens.
- *   act_dev activation buffer from bitq_quantize_act(_bits) with this M.
+ * (TERNARY, W2A8, BVSR4, WNAM) and SIGN1 with binary activations, reading
+ * every weight once for all M tokens.
+ *   act_dev activation buffer from bitq_quantize_act(_bits) with this M
+ *           (SIGN1: from bitq_binarize_act).
  *   y_dev   fp32 [M][N].  BITQ_F_ACC_INT32 writes [M][...] int32 partials
  *           laid out as in bitq_gemv, one block per token.
  */

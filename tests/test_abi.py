@@ -168,3 +168,24 @@ def test_device_entry_points_validate_before_any_device_call():
 def test_act_size_matches_documented_layout():
     for M, K in [(1, 4096), (16, 512), (64, 11008), (3, 96)]:
         assert bq.act_size(M, K) == bq.act_layout(M, K)["total"]
+
+
+def test_binary_activation_buffer_and_validation():
+    for M, K in [(1, 4096), (5, 96), (64, 11008)]:
+        assert bq.binact_size(M, K) == bq.binact_layout(M, K)["total"]
+    good = 1 << 20
+    n = bq.binact_size(2, 256)
+    assert bq._lib.bitq_binarize_act(good, bq.DT_BF16, 0, 256, good, n, None) == bq.E_SHAPE
+    assert bq._lib.bitq_binarize_act(good, bq.DT_BF16, 2, 100, good, n, None) == bq.E_SHAPE
+    assert bq._lib.bitq_binarize_act(good, bq.DT_ACT, 2, 256, good, n, None) == bq.E_ARG
+    assert bq._lib.bitq_binarize_act(good, bq.DT_BF16, 2, 256, good + 64, n, None) == bq.E_ALIGN
+    assert bq._lib.bitq_binarize_act(good, bq.DT_BF16, 2, 256, good, n - 1, None) == bq.E_CAPACITY
+    # binary activations pair with SIGN1 weights only
+    dr = bq.wdesc(bq.RABIT, 128, 256)
+    assert bq._lib.bitq_gemv(ctypes.byref(dr), good, good, bq.DT_BINARY, good, good, 1 << 20, 0,
+                             None) == bq.E_UNSUPPORTED
+    ds = bq.wdesc(bq.SIGN1, 128, 256)
+    assert bq._lib.bitq_gemv(ctypes.byref(ds), good, good + 16, bq.DT_BINARY, good, None, 0, 0,
+                             None) == bq.E_ALIGN
+    assert bq._lib.bitq_gemm_smallM(ctypes.byref(ds), good, good, 1, good, None, 0, 0, None) == bq.E_SHAPE
+    assert bq._lib.bitq_gemm_smallM(ctypes.byref(dr), good, good, 4, good, None, 0, 0, None) == bq.E_UNSUPPORTED

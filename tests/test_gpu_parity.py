@@ -97,6 +97,79 @@ def test_sign_gemv(N, K, xk):
     _sign_case(N, K, xk)
 
 
+# ===================================================== fully binary (XNOR)
+def _binarize_dev(x_store, M, K):
+    t = torch()
+    x = to_dev(x_store)
+    dt = bq.DT_F32 if x_store.dtype == np.float32 else bq.DT_BF16
+    act = t.full((bq.binact_size(M, K),), 0x5A, dtype=t.uint8, device="cuda")  # poison
+    bq.binarize_act(x, dt, M, K, act)
+    t.cuda.synchronize()
+    L = bq.binact_layout(M, K)
+    h = act.cpu().numpy()
+    bits = h[:4 * M * L["Kw"]].view(np.uint32).reshape(M, L["Kw"])
+    beta = h[L["off_beta"]:L["off_beta"] + 4 * M].view(np.float32)
+    return act, bits, beta
+
+
+def _xnor_case(N, K, M, x_store, x_f32, seed=0, rows=None):
+    W = synth.gaussian_f32(np.random.default_rng(seed), (N, K), 1.0)
+    B, alpha = ow.quantize_sign(W)
+    xb, beta = oact.binarize(x_f32)
+    act, bits, beta_dev = _binarize_dev(x_store, M, K)
+    assert np.array_equal(bits, oact.binary_words(xb, bq.binact_layout(M, K)["Kp"])), "sign words"
+    assert np.all(np.abs(beta_dev - beta) <= 1e-6 * beta + 1e-30), "beta"
+    desc = bq.wdesc(bq.SIGN1, N, K)
+    bd = dev_blob(bq.pack_weights(desc, sign=B, alpha=alpha))
+    r = np.arange(N) if rows is None else rows
+    t = torch()
+    Yd = t.full((M * N,), -1, dtype=t.int32, device="cuda")
+    yd = t.full((M * N,), float("nan"), dtype=t.float32, device="cuda")
+    for buf, flags in ((Yd, bq.F_ACC_INT32), (yd, 0)):
+        if M == 1:
+            bq.gemv(desc, bd, act, bq.DT_BINARY, buf, None, flags=flags)
+        else:
+            bq.gemm_smallM(desc, bd, act, M, buf, None, flags=flags)
+    t.cuda.synchronize()
+    Y = Yd.cpu().numpy().reshape(M, N)
+    assert np.array_equal(Y[:, r], og.xnor_int(B[r], xb)), "xnor Y"
+    # the float output against the oracle, with the device's beta (an fp32 sum)
+    y_ref, tol = og.gemv_xnor(B[r], alpha[r], xb, beta_dev.astype(np.float64))
+    return assert_within(yd.cpu().numpy().reshape(M, N)[:, r], y_ref, tol, f"xnor {N}x{K} M={M}")
+
+
+@pytest.mark.parametrize("N,K,M", [(256, 256, 1), (70, 224, 1), (200, 4096, 1), (130, 1056, 5),
+                                   (64, 32, 1), (300, 40960, 1), (1000, 2048, 64)])
+def test_xnor_gemv(N, K, M):
+    say("xnor", N, K, M)
+    xs, xf = synth.random_bf16(np.random.default_rng(N + M), (M, K))
+    xs[:, 0] = 0x8000                                   # -0.0 -> +1
+    xf[:, 0] = -0.0
+    _xnor_case(N, K, M, xs, xf, seed=N)
+
+
+def test_xnor_gemv_workload_and_batch_invariance():
+    N, K = 11008, 4096
+    say("xnor workload", N, K)
+    xs, xf = synth.random_bf16(np.random.default_rng(77), (4, K))
+    rows = np.sort(np.random.default_rng(1).choice(N, 512, replace=False))
+    _xnor_case(N, K, 4, xs, xf, seed=9, rows=rows)
+    # token 2 alone equals token 2 of the batch, bit for bit
+    W = synth.gaussian_f32(np.random.default_rng(9), (N, K), 1.0)
+    B, alpha = ow.quantize_sign(W)
+    desc = bq.wdesc(bq.SIGN1, N, K)
+    bd = dev_blob(bq.pack_weights(desc, sign=B, alpha=alpha))
+    t = torch()
+    act4, _, _ = _binarize_dev(xs, 4, K)
+    act1, _, _ = _binarize_dev(xs[2:3], 1, K)
+    y4 = t.empty(4 * N, dtype=t.float32, device="cuda")
+    y1 = t.empty(N, dtype=t.float32, device="cuda")
+    bq.gemm_smallM(desc, bd, act4, 4, y4, None)
+    bq.gemv(desc, bd, act1, bq.DT_BINARY, y1, None)
+    t.cuda.synchronize()
+    assert np.array_equal(y4.cpu().numpy().reshape(4, N)[2].view(np.uint32), y1.cpu().numpy().view(np.uint32))
+
+
 def _rabit_case(N, K, P, W=None, xs=None, x=None, seed=0):
     if W is None:
         W = synth.gaussian_f32(np.random.default_rng(seed), (N, K), 0.02)
