@@ -85,6 +85,8 @@ WORKLOADS = {
     "w4a4": dict(fmt="wnam", planes=4, abits=4, data="w2a8", shape_idx=1, N=11008, K=4096),
     "w2a4": dict(fmt="wnam", planes=2, abits=4, data="w2a8", shape_idx=1, N=11008, K=4096),
     "w3a8": dict(fmt="wnam", planes=3, abits=8, data="w2a8", shape_idx=1, N=11008, K=4096),
+    # fully binary XNOR+popcount: SIGN1 weights x sign activations (binarizer + GEMV per step)
+    "xnor": dict(fmt="sign", binary=True, data="sign", shape_idx=0, N=11008, K=4096),
 }
 
 
@@ -119,6 +121,12 @@ def cpu_baseline(wl: dict, budget_s: float = 12.0) -> dict:
             q, d = oact.quantize(xf, wl["abits"])
             return og.gemv_w2a8(qw, delta, zero, q, d)
         what = f"oracle {wl['abits']}-bit act quantize + W{wl['planes']} gemv (fp64 dequant + dot)"
+    elif fmt == "sign" and wl.get("binary"):
+        B, alpha = ow.quantize_sign(W)
+        def run():
+            xb, beta = oact.binarize(xf)
+            return og.gemv_xnor(B, alpha, xb, beta)
+        what = "oracle binarize + gemv_xnor (fp64 dequant + dot)"
     elif fmt == "ternary":
         T, gamma = ow.quantize_ternary(W)
         def run():
@@ -201,20 +209,31 @@ def main():
 
     # ---- activations / outputs / workspace
     xs, xf = synth.activations(data, si, 1, K)
-    x = torch.from_numpy(np.ascontiguousarray(xs).view(np.int16)).to(dev)
+    if xs.dtype == np.float32:      # fp32 activations (the sign workloads' inputs)
+        x, x_dt = torch.from_numpy(np.ascontiguousarray(xs)).to(dev), bq.DT_F32
+    else:                           # bf16 bit patterns
+        x, x_dt = torch.from_numpy(np.ascontiguousarray(xs).view(np.int16)).to(dev), bq.DT_BF16
     y = torch.empty(N, dtype=torch.float32, device=dev)
     ws = torch.zeros(bq.workspace_size(desc, 1), dtype=torch.uint8, device=dev)
-    integer = fmt in ("ternary", "w2a8", "bvsr", "wnam")
-    act = torch.zeros(bq.act_size(1, K), dtype=torch.uint8, device=dev) if integer else None
+    binary = bool(wl.get("binary"))
+    integer = fmt in ("ternary", "w2a8", "bvsr", "wnam") or binary
+    if binary:
+        act = torch.zeros(bq.binact_size(1, K), dtype=torch.uint8, device=dev)
+    else:
+        act = torch.zeros(bq.act_size(1, K), dtype=torch.uint8, device=dev) if integer else None
+    act_dt = bq.DT_BINARY if binary else bq.DT_ACT
     stream = torch.cuda.current_stream()
 
     def step(i):
         w = blobs[i % copies]
-        if integer:
-            bq.quantize_act(x, bq.DT_BF16, 1, K, act, stream=stream, abits=abits)
+        if binary:
+            bq.binarize_act(x, x_dt, 1, K, act, stream=stream)
+            bq.gemv(desc, w, act, bq.DT_BINARY, y, None, stream=stream)
+        elif integer:
+            bq.quantize_act(x, x_dt, 1, K, act, stream=stream, abits=abits)
             bq.gemv(desc, w, act, bq.DT_ACT, y, ws, stream=stream)
         else:
-            bq.gemv(desc, w, x, bq.DT_BF16, y, ws, stream=stream)
+            bq.gemv(desc, w, x, x_dt, y, ws, stream=stream)
 
     for i in range(args.warmup):
         step(i)
@@ -264,7 +283,7 @@ def main():
             with torch.cuda.graph(g2, stream=s2):
                 st2 = torch.cuda.current_stream()
                 for i in range(K_steps):
-                    bq.gemv(desc, blobs[i % copies], act, bq.DT_ACT, y, ws, stream=st2)
+                    bq.gemv(desc, blobs[i % copies], act, act_dt, y, None if binary else ws, stream=st2)
         torch.cuda.current_stream().wait_stream(s2)
         g2.replay()
         torch.cuda.synchronize()
@@ -294,7 +313,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if fmt in ("rabit", "sign") else "int32",
+        "dtype": "f32" if fmt == "rabit" or (fmt == "sign" and not binary) else "int32",
         "data": "synthetic",
         "config": {"workload": f"{args.workload} {N}x{K} M=1 ({'RaBiT 2-path residual binary, bf16 x' if fmt == 'rabit' else fmt})",
                    "N": N, "K": K, "M": 1, "format": fmt, "packed_bytes": alg_bytes,
@@ -304,7 +323,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "traffic_bytes_per_launch": mt["bytes_per_launch"] if traffic is not None else None,
-                     "kernel": "gemv_sign_kernel" if fmt in ("rabit", "sign") else "gemv_bits_nr_kernel",
+                     "kernel": ("gemv_xnor_kernel" if binary else
+                                "gemv_sign_kernel" if fmt in ("rabit", "sign") else "gemv_bits_nr_kernel"),
                      "kernel_us": round(gemv_ms * 1e3, 3)},
         "cpu_baseline": None,
     }

@@ -841,7 +841,7 @@ bitq_status bitq_binarize_act(const void* x_dev, int32_t x_dtype, int32_t M, int
     if (!x_dev || !act_dev) return fail(BITQ_E_ARG, "x_dev/act_dev is NULL");
     if (x_dtype != BITQ_DT_F32 && x_dtype != BITQ_DT_BF16)
         return fail(BITQ_E_ARG, "x_dtype must be BITQ_DT_F32 or BITQ_DT_BF16");
-    if (!aligned(x_dev, 4)) return fail(BITQ_E_ALIGN, "x_dev must be 4-byte aligned");
+    if (!aligned(x_dev, 16)) return fail(BITQ_E_ALIGN, "x_dev must be 16-byte aligned");
     if (!aligned(act_dev, 256)) return fail(BITQ_E_ALIGN, "act_dev must be 256-byte aligned");
     if (act_bytes < need) return fail(BITQ_E_CAPACITY, "binary activation buffer has %zu bytes, needs %zu", act_bytes, need);
     int is950 = 0;

@@ -789,7 +789,7 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
 // [BitNet] §2.1 sign with the tie at 0 going to +1 (so -0.0 -> +1): one bit
 // per input, 1 <-> +1, LSB first, zero bits past K.  beta = mean_k |x_k| is
 // the per-token scale of the fully binary product (workgroup 0 of each token
-// sums the row in a fixed order).  Grid (words / 8, M), 256 lanes: each wave
+// sums the row in a fixed order).  The 16-byte loads need x 16-byte aligned.  Grid (words / 8, M), 256 lanes: each wave
 // turns 64 inputs into two words with one ballot.
 template <int DT>
 __global__ __launch_bounds__(256) void binarize_act_kernel(const void* __restrict__ x, int K, int Kw,
@@ -807,8 +807,26 @@ __global__ __launch_bounds__(256) void binarize_act_kernel(const void* __restric
         if (lane == 32 && w0 + 1 < Kw) bits[static_cast<size_t>(m) * Kw + w0 + 1] = static_cast<uint32_t>(b >> 32);
     }
     if (blockIdx.x != 0) return;
+    // sum |x| of the row: 16-byte loads, four in flight per lane, fixed order
+    constexpr int VEC = (DT == BITQ_DT_F32) ? 4 : 8;
+    const uint4* xv = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(x) + row * (DT == BITQ_DT_F32 ? 4 : 2));
+    const int nvec = K / VEC;  // K is a multiple of 32
     float sum = 0.0f;
-    for (int i = tid; i < K; i += 256) sum += fabsf(act_at<DT>(x, row + i));
+    for (int i0 = 0; i0 < nvec; i0 += 1024) {
+        uint4 v[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) v[h] = xv[min(i0 + tid + 256 * h, nvec - 1)];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const uint32_t keep = i0 + tid + 256 * h < nvec ? 0xFFFFFFFFu : 0u;  // clamped duplicates add 0
+            const uint32_t a[4] = {v[h].x & keep, v[h].y & keep, v[h].z & keep, v[h].w & keep};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (DT == BITQ_DT_F32) sum += fabsf(__uint_as_float(a[e]));
+                else sum += fabsf(__uint_as_float(a[e] << 16)) + fabsf(__uint_as_float(a[e] & 0xFFFF0000u));
+            }
+        }
+    }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
     if (lane == 0) s_sum[wave] = sum;

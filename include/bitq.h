@@ -253,7 +253,7 @@ bitq_status bitq_binact_size(int32_t M, int32_t K, size_t* bytes);
  * for x >= 0, else -1; §2.3 XNOR+popcount product): the sign bits of every
  * input and the per-token scale beta = mean |x| (the page gives the weight
  * scale only; beta is the reading taken, so that beta sign(x) approximates x).
- *   x_dev   device [M][K] fp32 or bf16, 4-byte aligned
+ *   x_dev   device [M][K] fp32 or bf16, 16-byte aligned
  *   act_dev device buffer of bitq_binact_size bytes, 256-byte aligned
  * 1 <= M <= 64.  The bits are exact; beta is an fp32 sum.
  */
