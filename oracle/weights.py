@@ -71,14 +71,15 @@ def rabit_scales(A: np.ndarray, iters: int = 30):
     return to_f16(r * u), to_f16(r * v)
 
 
-def quantize_rabit(W: np.ndarray, paths: int = 2, iters: int = 30):
+def quantize_rabit(W: np.ndarray, paths: int = 2, iters: int = 30, svid_sweeps: int = 0):
     """[RaBiT] §2.1 (two-path form W^ = g1.B1.h1 + g2.B2.h2) and §2.2 (the
     residual forward: B1 = sign(W), R1 = W - W^1, B2 = sign(R1)).
 
     Each path binarizes the current residual and fits its (g, h) to the
     residual's magnitude by a rank-1 fit; the next residual subtracts the path
     using the *stored* fp16 g and h, so that the recursion can be re-checked
-    from the stored values alone.  One greedy pass (no Gauss-Seidel refinement).
+    from the stored values alone.  That greedy pass is followed by
+    `svid_sweeps` Gauss-Seidel sweeps (refine_rabit_svid; 0 = greedy only).
     """
     R = np.asarray(W, dtype=np.float32).astype(np.float64)
     N, K = R.shape
@@ -89,6 +90,42 @@ def quantize_rabit(W: np.ndarray, paths: int = 2, iters: int = 30):
         B[p] = sign_pm1(R)
         g[p], h[p] = rabit_scales(np.abs(R), iters)
         R = R - (g[p].astype(np.float64)[:, None] * B[p]) * h[p].astype(np.float64)[None, :]
+    if svid_sweeps:
+        refine_rabit_svid(W, B, g, h, svid_sweeps, iters)
+    return B, g, h
+
+
+def rabit_path(B_p, g_p, h_p):
+    """g_p (.) B_p (.) h_p from the stored values, fp64 [N, K]."""
+    return (g_p.astype(np.float64)[:, None] * B_p) * h_p.astype(np.float64)[None, :]
+
+
+def refine_rabit_svid(W, B, g, h, sweeps: int = 20, iters: int = 30):
+    """[RaBiT] §2.2, function-aware initialization step 1: iterative residual
+    SVID, alternating over the paths Gauss-Seidel style (20 sweeps is the
+    page's default).  Path by path, the target is what the other paths leave,
+
+        T_p = W - sum_{q != p} g_q (.) B_q (.) h_q    (stored fp16 scales),
+        B_p = sign(T_p),   (g_p, h_p) = rank-1 fit of |T_p|,
+
+    which is the exact minimizer of ||T_p - g (.) B (.) h|| over that path:
+    for positive g h the best B is sign(T), and then ||T - g(.)B(.)h|| equals
+    || |T| - g h^T ||, minimized by the leading singular pair.  So the
+    reconstruction error does not grow except through the fp16 rounding of
+    g and h.  Updates B, g, h in place (B [P, N, K] int8, g [P, N], h [P, K]
+    fp16) and returns them."""
+    W64 = np.asarray(W, dtype=np.float32).astype(np.float64)
+    P = B.shape[0]
+    paths = [rabit_path(B[q], g[q], h[q]) for q in range(P)]
+    total = sum(paths)
+    for _ in range(sweeps):
+        for p in range(P):
+            T = W64 - (total - paths[p])
+            B[p] = sign_pm1(T)
+            g[p], h[p] = rabit_scales(np.abs(T), iters)
+            new = rabit_path(B[p], g[p], h[p])
+            total = total - paths[p] + new
+            paths[p] = new
     return B, g, h
 
 
