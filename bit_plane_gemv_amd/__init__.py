@@ -70,6 +70,10 @@ class WDesc(ctypes.Structure):
                 ("planes", ctypes.c_int32), ("group", ctypes.c_int32), ("abits", ctypes.c_int32)]
 
 
+class QuantOpts(ctypes.Structure):
+    _fields_ = [("rabit_svid_sweeps", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7)]
+
+
 class Logical(ctypes.Structure):
     _fields_ = [("sign", ctypes.c_void_p), ("tern", ctypes.c_void_p), ("code", ctypes.c_void_p),
                 ("alpha", ctypes.c_void_p), ("g", ctypes.c_void_p), ("h", ctypes.c_void_p),
@@ -87,6 +91,8 @@ _sigs = {
     "bitq_packed_size": ([ctypes.POINTER(WDesc), ctypes.POINTER(_SZ)], _I32),
     "bitq_pack_weights": ([ctypes.POINTER(WDesc), ctypes.POINTER(Logical), _P, _SZ], _I32),
     "bitq_quantize_weights": ([ctypes.POINTER(WDesc), _P, _P, _SZ, _I32], _I32),
+    "bitq_quantize_weights_opts": ([ctypes.POINTER(WDesc), _P, ctypes.POINTER(QuantOpts), _P, _SZ, _I32],
+                                   _I32),
     "bitq_act_size": ([_I32, _I32, ctypes.POINTER(_SZ)], _I32),
     "bitq_quantize_act": ([_P, _I32, _I32, _I32, _P, _SZ, _P], _I32),
     "bitq_quantize_act_bits": ([_P, _I32, _I32, _I32, _I32, _P, _SZ, _P], _I32),
@@ -177,14 +183,20 @@ def pack_weights(desc: WDesc, **fields) -> np.ndarray:
     return blob
 
 
-def quantize_weights(desc: WDesc, W: np.ndarray, nthreads: int = 0) -> np.ndarray:
-    """fp32 W [N, K] -> packed blob with the library's own offline quantizer."""
+def quantize_weights(desc: WDesc, W: np.ndarray, nthreads: int = 0, svid_sweeps: int = 0) -> np.ndarray:
+    """fp32 W [N, K] -> packed blob with the library's own offline quantizer
+    (RABIT: svid_sweeps Gauss-Seidel refinement sweeps after the greedy pass)."""
     W = np.ascontiguousarray(W, dtype=np.float32)
     if W.shape != (desc.N, desc.K):
         raise ValueError(f"W has shape {W.shape}, descriptor says {(desc.N, desc.K)}")
     blob = np.zeros(packed_size(desc), dtype=np.uint8)
-    _check(_lib.bitq_quantize_weights(ctypes.byref(desc), W.ctypes.data, blob.ctypes.data,
-                                      blob.nbytes, nthreads))
+    if svid_sweeps:
+        opts = QuantOpts(svid_sweeps)
+        _check(_lib.bitq_quantize_weights_opts(ctypes.byref(desc), W.ctypes.data, ctypes.byref(opts),
+                                               blob.ctypes.data, blob.nbytes, nthreads))
+    else:
+        _check(_lib.bitq_quantize_weights(ctypes.byref(desc), W.ctypes.data, blob.ctypes.data,
+                                          blob.nbytes, nthreads))
     return blob
 
 

@@ -413,6 +413,44 @@ bitq_status quantize_rabit(const bitq_wdesc& d, const float* W, std::vector<int8
     return BITQ_OK;
 }
 
+// [RaBiT] §2.2 iterative residual SVID: Gauss-Seidel sweeps over the paths.
+// Path p is refitted to what the other paths leave,
+//   T = W - sum_{q != p} (g_q B_q) h_q   (stored fp16 scales, paths in order),
+//   B_p = sign(T), (g_p, h_p) = rank-1 fit of |T|,
+// the exact minimizer for that path, so the error does not grow except by
+// the fp16 rounding of g and h.  T is rebuilt from the int8 signs and the fp16
+// scales each time (no fp64 copy of the paths is kept).
+void refine_rabit_svid(const bitq_wdesc& d, const float* W, std::vector<int8_t>& B, std::vector<uint16_t>& g,
+                       std::vector<uint16_t>& h, int sweeps, int nthreads) {
+    const int64_t N = d.N, K = d.K, P = d.planes;
+    std::vector<double> A(N * K), hq(P * K);
+    std::vector<double> u, v;
+    for (int s = 0; s < sweeps; ++s)
+        for (int64_t p = 0; p < P; ++p) {
+            for (int64_t i = 0; i < P * K; ++i) hq[i] = f16_to_f64(h[i]);
+            int8_t* Bp = &B[p * N * K];
+            parallel_for(N, nthreads, [&](int64_t n) {
+                for (int64_t k = 0; k < K; ++k) {
+                    double t = W[n * K + k];
+                    for (int64_t q = 0; q < P; ++q)
+                        if (q != p)
+                            t = t - (f16_to_f64(g[q * N + n]) * B[(q * N + n) * K + k]) * hq[q * K + k];
+                    Bp[n * K + k] = sign_pm1(t);
+                    A[n * K + k] = std::fabs(t);
+                }
+            });
+            double sigma = 0.0;
+            if (rank1_fit(A, N, K, 30, nthreads, u, v, sigma)) {
+                const double r = std::sqrt(std::max(sigma, 0.0));
+                for (int64_t n = 0; n < N; ++n) g[p * N + n] = f64_to_f16(r * u[n]);
+                for (int64_t k = 0; k < K; ++k) h[p * K + k] = f64_to_f16(r * v[k]);
+            } else {
+                for (int64_t n = 0; n < N; ++n) g[p * N + n] = 0;
+                for (int64_t k = 0; k < K; ++k) h[p * K + k] = 0;
+            }
+        }
+}
+
 // [ABQ] §3.2 Eq. (3) with gamma = 0 and clip factors 1: asymmetric min/max
 // round-to-nearest per group of 128 inputs on L = 2^planes - 1 steps (W2A8:
 // 2 planes, L = 3; WNAM: 1..4 planes).  delta = fl16((hi - lo)/L),
@@ -715,8 +753,21 @@ bitq_status bitq_pack_weights(const bitq_wdesc* desc, const bitq_logical* src, v
 
 bitq_status bitq_quantize_weights(const bitq_wdesc* desc, const float* W, void* dst, size_t dst_bytes,
                                   int32_t nthreads) {
+    bitq_quant_opts opts{};
+    return bitq_quantize_weights_opts(desc, W, &opts, dst, dst_bytes, nthreads);
+}
+
+bitq_status bitq_quantize_weights_opts(const bitq_wdesc* desc, const float* W, const bitq_quant_opts* opts,
+                                       void* dst, size_t dst_bytes, int32_t nthreads) {
     bitq_status s = check_desc(desc);
     if (s) return s;
+    if (!opts) return fail(BITQ_E_ARG, "opts is NULL");
+    for (int i = 0; i < 7; ++i)
+        if (opts->reserved[i]) return fail(BITQ_E_ARG, "opts->reserved[%d] must be 0", i);
+    if (opts->rabit_svid_sweeps < 0 || opts->rabit_svid_sweeps > 1000)
+        return fail(BITQ_E_ARG, "rabit_svid_sweeps=%d out of range [0, 1000]", opts->rabit_svid_sweeps);
+    if (opts->rabit_svid_sweeps && desc->fmt != BITQ_RABIT)
+        return fail(BITQ_E_ARG, "rabit_svid_sweeps applies to the RABIT format only");
     if (!W) return fail(BITQ_E_ARG, "W is NULL");
     if (!dst) return fail(BITQ_E_ARG, "dst is NULL");
     const bitq_wdesc d = *desc;
@@ -750,6 +801,7 @@ bitq_status bitq_quantize_weights(const bitq_wdesc* desc, const float* W, void* 
             }
             case BITQ_RABIT:
                 quantize_rabit(d, W, i8, g, h, nthreads);
+                refine_rabit_svid(d, W, i8, g, h, opts->rabit_svid_sweeps, nthreads);
                 lg.sign = i8.data();
                 lg.g = g.data();
                 lg.h = h.data();

@@ -200,6 +200,23 @@ bitq_status bitq_pack_weights(const bitq_wdesc* desc, const bitq_logical* src,
 bitq_status bitq_quantize_weights(const bitq_wdesc* desc, const float* W, void* dst,
                                   size_t dst_bytes, int32_t nthreads);
 
+/* Options of the offline quantizer (zero-initialize; reserved must stay 0). */
+typedef struct {
+    int32_t rabit_svid_sweeps;  /* RABIT: Gauss-Seidel sweeps of [RaBiT] §2.2's
+                                   iterative residual SVID after the greedy
+                                   pass (0 = greedy only; the page's default
+                                   is 20).  Path p is refitted to
+                                   T = W - sum_{q != p} g_q B_q h_q (stored fp16
+                                   scales): B_p = sign(T), (g_p, h_p) = rank-1
+                                   fit of |T|.  0..1000 */
+    int32_t reserved[7];
+} bitq_quant_opts;
+
+/* bitq_quantize_weights with options (NULL opts: BITQ_E_ARG). */
+bitq_status bitq_quantize_weights_opts(const bitq_wdesc* desc, const float* W,
+                                       const bitq_quant_opts* opts, void* dst,
+                                       size_t dst_bytes, int32_t nthreads);
+
 /*
  * Activation buffer (written by bitq_quantize_act, read by the integer
  * formats).  Kp = K rounded up to 128, Kw = Kp / 32.  Sections, each at a

@@ -116,16 +116,14 @@ def refine_rabit_svid(W, B, g, h, sweeps: int = 20, iters: int = 30):
     fp16) and returns them."""
     W64 = np.asarray(W, dtype=np.float32).astype(np.float64)
     P = B.shape[0]
-    paths = [rabit_path(B[q], g[q], h[q]) for q in range(P)]
-    total = sum(paths)
     for _ in range(sweeps):
         for p in range(P):
-            T = W64 - (total - paths[p])
+            T = W64.copy()
+            for q in range(P):          # the other paths, subtracted in path order
+                if q != p:
+                    T = T - rabit_path(B[q], g[q], h[q])
             B[p] = sign_pm1(T)
             g[p], h[p] = rabit_scales(np.abs(T), iters)
-            new = rabit_path(B[p], g[p], h[p])
-            total = total - paths[p] + new
-            paths[p] = new
     return B, g, h
 
 

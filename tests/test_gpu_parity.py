@@ -226,6 +226,23 @@ def test_rabit_split_k_deterministic_and_workspace_reuse():
     assert_within(outs[0][None, :], y_ref, tol, "rabit determinism")
 
 
+def test_rabit_gemv_svid_refined_blob():
+    """The refined RaBiT decomposition (library packer, 20 Gauss-Seidel sweeps)
+    runs through the same GEMV; parity from the logical form the oracle reads
+    back out of the blob."""
+    from oracle import layout
+    N, K = 4096, 4096
+    say("rabit svid blob", N, K)
+    W = synth.weights("rabit", 0, N, K)
+    xs, x = synth.activations("rabit", 0, 1, K)
+    desc = bq.wdesc(bq.RABIT, N, K, planes=2)
+    blob = bq.quantize_weights(desc, W, svid_sweeps=20)
+    L = layout.unpack(blob)
+    y = run_gemv(desc, dev_blob(blob), to_dev(xs[0]), bq.DT_BF16)
+    y_ref, tol = og.gemv_rabit(L["B"], L["g"], L["h"], x)
+    assert_within(y, y_ref, tol, "rabit svid")
+
+
 @pytest.mark.parametrize("shape_idx", [0, 1, 2])
 def test_rabit_gemv_workload(shape_idx):
     N, K = synth.CONFIGS["rabit"]["shapes"][shape_idx]

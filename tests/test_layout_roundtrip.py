@@ -119,3 +119,53 @@ def test_library_wnam_quantizer_matches_oracle(n):
     assert np.array_equal(out["q"], q)
     assert np.array_equal(out["delta"].view(np.uint16), delta.view(np.uint16))
     assert np.array_equal(out["zero"].view(np.uint16), zero.view(np.uint16))
+
+
+def _rabit_err(W, B, g, h):
+    What = sum(ow.rabit_path(B[p], g[p], h[p]) for p in range(B.shape[0]))
+    return float(np.sum((W.astype(np.float64) - What) ** 2))
+
+
+@pytest.mark.parametrize("sweeps", [0, 5])
+def test_library_rabit_quantizer_close_to_oracle(sweeps):
+    """Library (C++, threaded power iteration) against the oracle: the power
+    iterations add in different orders, so the fp16 scales may differ by an
+    ulp and a few near-zero residual signs may flip; the fit is the same."""
+    W = _w(64, 256, seed=11)
+    d = bq.wdesc(bq.RABIT, 64, 256, planes=2)
+    out = layout.unpack(bq.quantize_weights(d, W, svid_sweeps=sweeps))
+    B, g, h = ow.quantize_rabit(W, 2, svid_sweeps=sweeps)
+    assert np.mean(out["B"] == B) > 0.999
+    for a, b in ((out["g"], g), (out["h"], h)):
+        a64, b64 = a.astype(np.float64), b.astype(np.float64)
+        assert np.all(np.abs(a64 - b64) <= 2.0 ** -9 * np.abs(b64) + 1e-7)
+    e_lib, e_orc = _rabit_err(W, out["B"], out["g"], out["h"]), _rabit_err(W, B, g, h)
+    assert abs(e_lib - e_orc) <= 1e-3 * e_orc
+
+
+def test_library_rabit_svid_invariants():
+    W = _w(96, 384, seed=12)
+    d = bq.wdesc(bq.RABIT, 96, 384, planes=2)
+    g0 = layout.unpack(bq.quantize_weights(d, W))
+    s20 = layout.unpack(bq.quantize_weights(d, W, svid_sweeps=20))
+    # the last path is the sign of what the first leaves, from the stored values
+    T = W.astype(np.float64) - ow.rabit_path(s20["B"][0], s20["g"][0], s20["h"][0])
+    assert np.array_equal(s20["B"][1], np.where(T >= 0, 1, -1).astype(np.int8))
+    assert _rabit_err(W, s20["B"], s20["g"], s20["h"]) < 0.995 * _rabit_err(W, g0["B"], g0["g"], g0["h"])
+    assert np.all(s20["g"].astype(np.float64) >= 0) and np.all(s20["h"].astype(np.float64) >= 0)
+
+
+def test_quantize_options_validation():
+    import ctypes
+    W = _w(64, 128)
+    d = bq.wdesc(bq.RABIT, 64, 128)
+    blob = np.zeros(bq.packed_size(d), dtype=np.uint8)
+    call = lambda desc, opts: bq._lib.bitq_quantize_weights_opts(ctypes.byref(desc), W.ctypes.data, opts,
+                                                                 blob.ctypes.data, blob.nbytes, 1)
+    assert call(d, None) == bq.E_ARG
+    o = bq.QuantOpts(3)
+    o.reserved[2] = 1
+    assert call(d, ctypes.byref(o)) == bq.E_ARG
+    assert call(d, ctypes.byref(bq.QuantOpts(-1))) == bq.E_ARG
+    assert call(bq.wdesc(bq.SIGN1, 64, 128), ctypes.byref(bq.QuantOpts(2))) == bq.E_ARG
+    assert call(d, ctypes.byref(bq.QuantOpts(2))) == bq.OK
