@@ -121,6 +121,56 @@ def gemv_bvsr(code, idx, cache, q, d):
                            code.shape[0], act_hat(q, d))
 
 
+# ------------------------------------------- HGF gated low-rank correction
+SILU_SLOPE_MAX = 1.1    # >= max_z |d silu / dz| (about 1.0998)
+
+
+def silu(z):
+    """SiLU, z * sigmoid(z) = z / (1 + exp(-z)), in fp64: the activation of
+    [HGF] §2.1's correction path.  Large negative z gives exp(-z) = inf and
+    the quotient -0."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def lora_down(x, A):
+    """h = silu(x A) ([HGF] §2.1): x [M, K] is the layer input before
+    activation quantization, A [K, r] the down matrix; fp64 [M, r]."""
+    return silu(np.asarray(x, dtype=np.float64) @ np.asarray(A, dtype=np.float64))
+
+
+def lora_gate(alpha):
+    """The gate tanh(alpha), which [HGF] §2.1 uses to keep it in (-1, 1)."""
+    return np.tanh(np.float64(alpha))
+
+
+def lora_correction(x, A, B, alpha):
+    """[HGF] §2.1: tanh(alpha) * (silu(x A) B) with B [r, N]; returns the
+    fp64 [M, N] correction and its tolerance.
+
+    The bound covers what an fp32 evaluation can lose: |gate| sum_j |B_jn|
+    (|h_j| + SILU_SLOPE_MAX sum_k |x_k A_kj|), times the float tolerance."""
+    x = np.asarray(x, dtype=np.float64)
+    A = np.asarray(A, dtype=np.float64)
+    B = np.asarray(B, dtype=np.float64)
+    h = lora_down(x, A)
+    g = lora_gate(alpha)
+    out = g * (h @ B)
+    zabs = np.abs(x) @ np.abs(A)
+    bound = abs(g) * ((np.abs(h) + SILU_SLOPE_MAX * zabs) @ np.abs(B))
+    return out, TOL_REL * bound
+
+
+def gemv_hgf(T, gamma, q, d, x, A, B, alpha):
+    """[HGF] §2.1 and §4.1: the ternary product of the quantized activations
+    plus the gated low-rank correction of the unquantized input x; returns
+    (y, tol) with the two paths' tolerances added."""
+    yt, tt = gemv_ternary(T, gamma, q, d)
+    yl, tl = lora_correction(x, A, B, alpha)
+    return yt + yl, tt + tl
+
+
 # ------------------------------------------------- exact integer partial sums
 def ternary_int(T, q):
     """[HGF] §1.2 Y_int = int8_matmul(X_quant, W_quant^T): [M, N] int64."""

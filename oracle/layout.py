@@ -9,7 +9,9 @@ Specification (all little-endian):
   header, 256 bytes: u32 magic 0x51544942, u32 version 1, u32 format,
       u32 N, u32 K, u32 P (planes), u32 group, u32 Np, u32 Kp, u32 reserved,
       u64 off_planes, u64 off_c0, u64 off_c1, u64 total_bytes; then at byte
-      72 f32 hbound[3] (SIGN1: 1; RABIT: max over k of |h_p[k]|).
+      72 f32 hbound[3] (SIGN1: 1; RABIT: max over k of |h_p[k]|); HGF only,
+      at byte 88: u64 off_c2, u32 rank, f32 alpha, f32 gate (tanh(alpha)
+      rounded to fp32), f32 amax_a (max |A|).
   Np = N rounded up to 64 (row tile), Kp = K rounded up to 128 (k block).
   planes section: 1024-byte tiles ordered [row tile t][k block b][plane p];
       inside a tile, row r (= n - 64 t) owns 16 bytes = 4 uint32 words,
@@ -24,6 +26,8 @@ Specification (all little-endian):
       5 bvsr    c0 = idx    u8  [Np/64][Kp/128][64][4] (byte j = group 4b+j),
                 c1 = cache  f32 [256][5]      (plane k = bitvector beta_k)
       6 wnam    as w2a8 with P = n planes      (plane i = bit i of q)
+      7 hgf     as ternary, plus c1 = A^T f16 [r][Kp] (row j = column j of
+                A) and c2 = B^T f16 [Np][r] (row n = column n of B)
   Every section starts at a multiple of 256 bytes.
 """
 from __future__ import annotations
@@ -36,7 +40,7 @@ MAGIC = 0x51544942
 HEADER_BYTES = 256
 ROW_TILE = 64
 K_BLOCK = 128
-FORMATS = {1: "sign", 2: "rabit", 3: "ternary", 4: "w2a8", 5: "bvsr", 6: "wnam"}
+FORMATS = {1: "sign", 2: "rabit", 3: "ternary", 4: "w2a8", 5: "bvsr", 6: "wnam", 7: "hgf"}
 
 
 def parse_header(blob: np.ndarray) -> dict:
@@ -50,6 +54,11 @@ def parse_header(blob: np.ndarray) -> dict:
              hbound=b[72:84].view(np.float32).astype(np.float64))
     if h["magic"] != MAGIC:
         raise ValueError("bad magic")
+    if h["fmt"] == 7:
+        h["off_c2"] = int(b[88:96].view(np.uint64)[0])
+        h["rank"] = int(b[96:100].view(np.uint32)[0])
+        f = b[100:112].view(np.float32)
+        h["alpha"], h["gate"], h["amax_a"] = np.float32(f[0]), np.float32(f[1]), np.float32(f[2])
     return h
 
 
@@ -89,11 +98,19 @@ def unpack(blob: np.ndarray) -> dict:
         hh = _section(b, h["off_c1"], 2 * P * Kp, np.float16).reshape(P, Kp)
         out["g"], out["h"] = g[:, :N].copy(), hh[:, :K].copy()
         pad_ok &= bool(np.all(g[:, N:] == 0) and np.all(hh[:, K:] == 0))
-    elif fmt == 3:
+    elif fmt in (3, 7):
         plus, minus = bits[0].astype(np.int8), bits[1].astype(np.int8)
         out["both_set"] = bool(np.any(plus & minus))
         out["T"] = plus - minus
         out["gamma"] = np.float32(_section(b, h["off_c0"], 4, np.float32)[0])
+        if fmt == 7:
+            r = h["rank"]
+            At = _section(b, h["off_c1"], 2 * r * Kp, np.float16).reshape(r, Kp)
+            Bt = _section(b, h["off_c2"], 2 * Np * r, np.float16).reshape(Np, r)
+            out["A"] = At[:, :K].T.copy()          # [K, r]
+            out["B"] = Bt[:N].T.copy()             # [r, N]
+            out["alpha"], out["gate"], out["amax_a"] = h["alpha"], h["gate"], h["amax_a"]
+            pad_ok &= bool(np.all(At[:, K:] == 0) and np.all(Bt[N:] == 0))
     elif fmt in (4, 6):   # w2a8 (2 planes), wnam (P planes): code = sum_p 2^p plane_p
         out["q"] = sum((bits[p].astype(np.int64) << p) for p in range(P)).astype(np.uint8)
         dz = _section(b, h["off_c0"], 4 * Np * (Kp // K_BLOCK), np.uint32)

@@ -15,6 +15,8 @@ Workloads (layer shapes are out x in, i.e. W is [N, K], x is [M, K]):
   w2a8    : W ~ N(0, 0.02^2) fp32,  x ~ N(0, 1) with 1% of the input
             channels scaled x20 (same channels for every token) -> bf16
   bvsr    : W ~ N(0, 0.015^2) fp32, x ~ N(0, 1) -> bf16, 70B-class shapes
+  hgf     : the ternary workload plus a rank-r correction: A [K, r] and
+            B [r, N] ~ N(0, 0.02^2) rounded to fp16, gate parameter 0.1
 
 The pages measure on trained Llama/LLaMA/Gemma layers and text datasets; these
 Gaussian layers of the same shapes stand in for them.
@@ -41,7 +43,7 @@ CONFIGS = {
                  shapes=[(8192, 8192), (28672, 8192)], M=[1], x_dtype="bf16"),
 }
 
-ROLE_W, ROLE_X, ROLE_OUTLIER = 0, 1, 2
+ROLE_W, ROLE_X, ROLE_OUTLIER, ROLE_LORA = 0, 1, 2, 3
 
 
 def seed_for(cfg: int, shape_idx: int, role: int) -> int:
@@ -109,3 +111,23 @@ def random_bf16(gen: np.random.Generator, shape, scale: float = 1.0):
     x = gaussian_f32(gen, shape, scale)
     bits = f32_to_bf16_bits(x)
     return bits, bf16_bits_to_f32(bits)
+
+
+def f32_to_f16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 to IEEE half (round-half-to-even); returns uint16 bits."""
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float32).astype(np.float16)).view(np.uint16)
+
+
+def lora_params(shape_idx: int, N: int, K: int, r: int, sigma: float = 0.02,
+                seed_offset: int = 0):
+    """Low-rank correction parameters of an hgf layer (ternary config seeds).
+
+    Returns (A_bits [K, r], B_bits [r, N]) as fp16 bit patterns and the gate
+    parameter alpha (float32 0.1).  A and B are drawn N(0, sigma^2) in
+    float64, stored float32, then rounded to fp16.
+    """
+    gen = np.random.default_rng(seed_for(CONFIGS["ternary"]["cfg"], shape_idx, ROLE_LORA)
+                                + 100000 * seed_offset)
+    A = gaussian_f32(gen, (K, r), sigma)
+    B = gaussian_f32(gen, (r, N), sigma)
+    return f32_to_f16_bits(A), f32_to_f16_bits(B), np.float32(0.1)

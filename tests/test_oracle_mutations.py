@@ -119,3 +119,36 @@ def test_mutation_w2a8_dropped_zero_point_term(monkeypatch):
     monkeypatch.setattr(og, "w2a8_from_int", no_zero)
     with pytest.raises(AssertionError):
         tg.test_w2a8_int_zero_point_identity()
+
+
+def test_mutation_hgf_relu_instead_of_silu(monkeypatch):
+    import test_oracle_hgf as th
+    monkeypatch.setattr(og, "silu", lambda z: np.maximum(np.asarray(z, np.float64), 0.0))
+    with pytest.raises(AssertionError):
+        th.test_lora_correction_hand_case()
+
+
+def test_mutation_hgf_sigmoid_sign(monkeypatch):
+    import test_oracle_hgf as th
+    monkeypatch.setattr(og, "silu", lambda z: np.asarray(z, np.float64) / (1.0 + np.exp(np.asarray(z, np.float64))))
+    with pytest.raises(AssertionError):
+        th.test_silu_special_values()
+
+
+def test_mutation_hgf_ungated(monkeypatch):
+    import test_oracle_hgf as th
+    monkeypatch.setattr(og, "lora_gate", lambda alpha: np.float64(alpha))
+    with pytest.raises(AssertionError):
+        th.test_lora_correction_hand_case()
+
+
+def test_mutation_hgf_quantized_input(monkeypatch):
+    # feeding the correction the quantized activation q instead of x
+    import test_oracle_hgf as th
+    orig = og.gemv_hgf
+
+    def wrong(T, gamma, q, d, x, A, B, alpha):
+        return orig(T, gamma, q, d, q.astype(np.float64), A, B, alpha)
+    monkeypatch.setattr(og, "gemv_hgf", wrong)
+    with pytest.raises(AssertionError):
+        th.test_gemv_hgf_hand_case()
