@@ -47,16 +47,17 @@ if len(_hip_runtimes()) > 1:
 
 # ------------------------------------------------------------------ enums
 OK, E_ARG, E_SHAPE, E_ALIGN, E_UNSUPPORTED, E_CAPACITY, E_DEVICE = 0, -1, -2, -3, -4, -5, -6
-SIGN1, RABIT, TERNARY, W2A8, BVSR4, WNAM = 1, 2, 3, 4, 5, 6
+SIGN1, RABIT, TERNARY, W2A8, BVSR4, WNAM, HGF = 1, 2, 3, 4, 5, 6, 7
 DT_F32, DT_BF16, DT_ACT, DT_BINARY = 0, 1, 2, 3
 F_ACC_INT32 = 1
 
 FORMAT_NAMES = {SIGN1: "sign", RABIT: "rabit", TERNARY: "ternary", W2A8: "w2a8", BVSR4: "bvsr",
-                WNAM: "wnam"}
+                WNAM: "wnam", HGF: "hgf"}
 FORMATS = {v: k for k, v in FORMAT_NAMES.items()}
-DEFAULT_PLANES = {SIGN1: 1, RABIT: 2, TERNARY: 2, W2A8: 2, BVSR4: 4, WNAM: 4}
-DEFAULT_GROUP = {SIGN1: 0, RABIT: 0, TERNARY: 0, W2A8: 128, BVSR4: 32, WNAM: 128}
-DEFAULT_ABITS = {SIGN1: 0, RABIT: 0, TERNARY: 8, W2A8: 8, BVSR4: 8, WNAM: 4}
+DEFAULT_PLANES = {SIGN1: 1, RABIT: 2, TERNARY: 2, W2A8: 2, BVSR4: 4, WNAM: 4, HGF: 2}
+DEFAULT_GROUP = {SIGN1: 0, RABIT: 0, TERNARY: 0, W2A8: 128, BVSR4: 32, WNAM: 128, HGF: 0}
+DEFAULT_ABITS = {SIGN1: 0, RABIT: 0, TERNARY: 8, W2A8: 8, BVSR4: 8, WNAM: 4, HGF: 8}
+DEFAULT_RANK = {HGF: 32}
 
 
 class BitqError(RuntimeError):
@@ -67,7 +68,8 @@ class BitqError(RuntimeError):
 
 class WDesc(ctypes.Structure):
     _fields_ = [("fmt", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
-                ("planes", ctypes.c_int32), ("group", ctypes.c_int32), ("abits", ctypes.c_int32)]
+                ("planes", ctypes.c_int32), ("group", ctypes.c_int32), ("abits", ctypes.c_int32),
+                ("rank", ctypes.c_int32)]
 
 
 class QuantOpts(ctypes.Structure):
@@ -78,7 +80,8 @@ class Logical(ctypes.Structure):
     _fields_ = [("sign", ctypes.c_void_p), ("tern", ctypes.c_void_p), ("code", ctypes.c_void_p),
                 ("alpha", ctypes.c_void_p), ("g", ctypes.c_void_p), ("h", ctypes.c_void_p),
                 ("gamma", ctypes.c_float), ("delta", ctypes.c_void_p), ("zero", ctypes.c_void_p),
-                ("idx", ctypes.c_void_p), ("cache", ctypes.c_void_p)]
+                ("idx", ctypes.c_void_p), ("cache", ctypes.c_void_p), ("lora_a", ctypes.c_void_p),
+                ("lora_b", ctypes.c_void_p), ("lora_alpha", ctypes.c_float)]
 
 
 _P = ctypes.c_void_p
@@ -96,6 +99,8 @@ _sigs = {
     "bitq_act_size": ([_I32, _I32, ctypes.POINTER(_SZ)], _I32),
     "bitq_quantize_act": ([_P, _I32, _I32, _I32, _P, _SZ, _P], _I32),
     "bitq_quantize_act_bits": ([_P, _I32, _I32, _I32, _I32, _P, _SZ, _P], _I32),
+    "bitq_hgf_act_size": ([ctypes.POINTER(WDesc), _I32, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)], _I32),
+    "bitq_quantize_act_hgf": ([ctypes.POINTER(WDesc), _P, _P, _I32, _I32, _P, _SZ, _P, _SZ, _P], _I32),
     "bitq_binact_size": ([_I32, _I32, ctypes.POINTER(_SZ)], _I32),
     "bitq_binarize_act": ([_P, _I32, _I32, _I32, _P, _SZ, _P], _I32),
     "bitq_workspace_size": ([ctypes.POINTER(WDesc), _I32, ctypes.POINTER(_SZ)], _I32),
@@ -138,12 +143,13 @@ def _stream(stream) -> int | None:
 
 
 def wdesc(fmt, N: int, K: int, planes: int | None = None, group: int | None = None,
-          abits: int | None = None) -> WDesc:
+          abits: int | None = None, rank: int | None = None) -> WDesc:
     if isinstance(fmt, str):
         fmt = FORMATS[fmt]
     return WDesc(fmt, N, K, DEFAULT_PLANES[fmt] if planes is None else planes,
                  DEFAULT_GROUP[fmt] if group is None else group,
-                 DEFAULT_ABITS[fmt] if abits is None else abits)
+                 DEFAULT_ABITS[fmt] if abits is None else abits,
+                 DEFAULT_RANK.get(fmt, 0) if rank is None else rank)
 
 
 # -------------------------------------------------------------- host calls
@@ -167,10 +173,10 @@ def pack_weights(desc: WDesc, **fields) -> np.ndarray:
     lg = Logical()
     conv = {"sign": np.int8, "tern": np.int8, "code": np.uint8, "alpha": np.float32,
             "g": np.uint16, "h": np.uint16, "delta": np.uint16, "zero": np.uint16,
-            "idx": np.uint8, "cache": np.float32}
+            "idx": np.uint8, "cache": np.float32, "lora_a": np.uint16, "lora_b": np.uint16}
     for name, val in fields.items():
-        if name == "gamma":
-            lg.gamma = float(val)
+        if name in ("gamma", "lora_alpha"):
+            setattr(lg, name, float(val))
             continue
         arr = np.asarray(val)
         if arr.dtype == np.float16:
@@ -204,6 +210,13 @@ def act_size(M: int, K: int) -> int:
     n = _SZ(0)
     _check(_lib.bitq_act_size(M, K, ctypes.byref(n)))
     return n.value
+
+
+def hgf_act_size(desc: WDesc, M: int) -> tuple:
+    """(activation buffer bytes, workspace bytes) of an HGF layer's activation step."""
+    a, w = _SZ(0), _SZ(0)
+    _check(_lib.bitq_hgf_act_size(ctypes.byref(desc), M, ctypes.byref(a), ctypes.byref(w)))
+    return a.value, w.value
 
 
 def binact_size(M: int, K: int) -> int:
@@ -243,6 +256,14 @@ def quantize_act(x, x_dtype: int, M: int, K: int, act, act_bytes: int | None = N
                                            _stream(stream)))
 
 
+def quantize_act_hgf(desc: WDesc, w, x, x_dtype: int, M: int, act, ws, act_bytes: int | None = None,
+                     ws_bytes: int | None = None, stream=None):
+    abytes = act.numel() * act.element_size() if act_bytes is None else act_bytes
+    wbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check(_lib.bitq_quantize_act_hgf(ctypes.byref(desc), _ptr(w), _ptr(x), x_dtype, M, _ptr(act), abytes,
+                                      _ptr(ws), wbytes, _stream(stream)))
+
+
 def _nbytes(buf) -> int:
     """Size of a device buffer (0 for None: calls that need no workspace)."""
     return 0 if buf is None else buf.numel() * buf.element_size()
@@ -262,8 +283,9 @@ def gemm_smallM(desc: WDesc, w, act, M: int, y, ws, ws_bytes: int | None = None,
                                  nbytes, flags, _stream(stream)))
 
 
-def act_layout(M: int, K: int) -> dict:
-    """Section offsets of an activation buffer (mirrors bitq_act_size)."""
+def act_layout(M: int, K: int, rank: int = 0) -> dict:
+    """Section offsets of an activation buffer (mirrors bitq_act_size; rank > 0:
+    the HGF buffer of bitq_hgf_act_size with its h section)."""
     Kp = (K + 127) // 128 * 128
     Kw = Kp // 32
 
@@ -272,5 +294,6 @@ def act_layout(M: int, K: int) -> dict:
     off_S = a256(M * Kw * 32)
     off_q = a256(off_S + M * Kw * 4)
     off_d = a256(off_q + M * Kp)
-    return dict(Kp=Kp, Kw=Kw, off_planes=0, off_S=off_S, off_q=off_q, off_d=off_d,
-                total=a256(off_d + 4 * M))
+    off_h = a256(off_d + 4 * M)
+    return dict(Kp=Kp, Kw=Kw, off_planes=0, off_S=off_S, off_q=off_q, off_d=off_d, off_h=off_h,
+                total=a256(off_h + 4 * M * rank))

@@ -99,7 +99,7 @@ void parallel_for(int64_t n, int nthreads, F&& body) {
 // ------------------------------------------------------------- validation
 bitq_status check_desc(const bitq_wdesc* d) {
     if (!d) return fail(BITQ_E_ARG, "desc is NULL");
-    if (d->fmt < BITQ_SIGN1 || d->fmt > BITQ_WNAM) return fail(BITQ_E_ARG, "unknown format %d", d->fmt);
+    if (d->fmt < BITQ_SIGN1 || d->fmt > BITQ_HGF) return fail(BITQ_E_ARG, "unknown format %d", d->fmt);
     if (d->N < 1 || d->N > (1 << 24)) return fail(BITQ_E_SHAPE, "N=%d out of range [1, 2^24]", d->N);
     if (d->K < 32 || d->K > (1 << 20)) return fail(BITQ_E_SHAPE, "K=%d out of range [32, 2^20]", d->K);
     if (d->K % 32) return fail(BITQ_E_SHAPE, "K=%d is not a multiple of 32", d->K);
@@ -133,10 +133,18 @@ bitq_status check_desc(const bitq_wdesc* d) {
             if (d->K % 128) return fail(BITQ_E_SHAPE, "WNAM needs K %% 128 == 0 (K=%d)", d->K);
             if (d->abits < 2 || d->abits > 8) return fail(BITQ_E_SHAPE, "WNAM needs abits in 2..8 (abits=%d)", d->abits);
             break;
+        case BITQ_HGF:
+            if (d->planes != 2 || d->group != 0) return fail(BITQ_E_SHAPE, "HGF needs planes=2, group=0");
+            if (d->rank != 8 && d->rank != 16 && d->rank != 32 && d->rank != 64)
+                return fail(BITQ_E_SHAPE, "HGF needs rank 8, 16, 32 or 64 (rank=%d)", d->rank);
+            if (d->K > kMaxHgfK) return fail(BITQ_E_SHAPE, "K=%d: HGF supports K <= %d", d->K, kMaxHgfK);
+            break;
     }
-    const bool intfmt = d->fmt == BITQ_TERNARY || d->fmt == BITQ_W2A8 || d->fmt == BITQ_BVSR4;
+    if (d->fmt != BITQ_HGF && d->rank != 0)
+        return fail(BITQ_E_SHAPE, "rank=%d: only HGF has a correction rank (use 0)", d->rank);
+    const bool intfmt = d->fmt == BITQ_TERNARY || d->fmt == BITQ_W2A8 || d->fmt == BITQ_BVSR4 || d->fmt == BITQ_HGF;
     if (intfmt && d->abits != 0 && d->abits != 8)
-        return fail(BITQ_E_SHAPE, "abits=%d: TERNARY/W2A8/BVSR4 use 8-bit activations (abits 0 or 8)", d->abits);
+        return fail(BITQ_E_SHAPE, "abits=%d: TERNARY/W2A8/BVSR4/HGF use 8-bit activations (abits 0 or 8)", d->abits);
     if ((d->fmt == BITQ_SIGN1 || d->fmt == BITQ_RABIT) && d->abits != 0)
         return fail(BITQ_E_SHAPE, "abits=%d: SIGN1/RABIT take raw activations (abits 0)", d->abits);
     return BITQ_OK;
@@ -158,6 +166,12 @@ void write_header(const bitq_wdesc& d, const BlobLayout& L, uint8_t* dst) {
     uint64_t v[4] = {L.off_planes, L.off_c0, L.off_c1, L.total};
     std::memcpy(dst, u, sizeof(u));
     std::memcpy(dst + 40, v, sizeof(v));
+    if (d.fmt == BITQ_HGF) {
+        const uint64_t off_c2 = L.off_c2;
+        const uint32_t rank = static_cast<uint32_t>(d.rank);
+        std::memcpy(dst + kHdrOffC2, &off_c2, 8);
+        std::memcpy(dst + kHdrRank, &rank, 4);
+    }
 }
 
 // Offset in bytes of the word (plane p, row n, word kw) inside the blob.
@@ -203,10 +217,22 @@ bitq_status check_logical(const bitq_wdesc& d, const bitq_logical* s) {
             break;
         }
         case BITQ_TERNARY:
+        case BITQ_HGF:
             if ((st = need(s->tern, "tern"))) return st;
             for (int64_t i = 0; i < N * K; ++i)
                 if (s->tern[i] < -1 || s->tern[i] > 1)
                     return fail(BITQ_E_ARG, "tern[%lld]=%d not in {-1,0,1}", (long long)i, s->tern[i]);
+            if (d.fmt == BITQ_HGF) {
+                if ((st = need(s->lora_a, "lora_a")) || (st = need(s->lora_b, "lora_b"))) return st;
+                const int64_t r = d.rank;
+                for (int64_t i = 0; i < K * r; ++i)
+                    if ((s->lora_a[i] & 0x7C00u) == 0x7C00u)
+                        return fail(BITQ_E_ARG, "lora_a[%lld] is not finite", (long long)i);
+                for (int64_t i = 0; i < r * N; ++i)
+                    if ((s->lora_b[i] & 0x7C00u) == 0x7C00u)
+                        return fail(BITQ_E_ARG, "lora_b[%lld] is not finite", (long long)i);
+                if (!std::isfinite(s->lora_alpha)) return fail(BITQ_E_ARG, "lora_alpha is not finite");
+            }
             break;
         case BITQ_W2A8:
         case BITQ_WNAM: {
@@ -250,6 +276,18 @@ void pack_coefficients(const bitq_wdesc& d, const BlobLayout& L, const bitq_logi
             std::memcpy(dst + L.off_c0, &gmm, 4);
             break;
         }
+        case BITQ_HGF: {
+            float gmm = s->gamma;
+            std::memcpy(dst + L.off_c0, &gmm, 4);
+            const int64_t r = d.rank;
+            uint16_t* at = reinterpret_cast<uint16_t*>(dst + L.off_c1);  // [r][Kp]
+            uint16_t* bt = reinterpret_cast<uint16_t*>(dst + L.off_c2);  // [Np][r]
+            for (int64_t k = 0; k < K; ++k)
+                for (int64_t j = 0; j < r; ++j) at[j * Kp + k] = s->lora_a[k * r + j];
+            for (int64_t j = 0; j < r; ++j)
+                for (int64_t n = 0; n < N; ++n) bt[n * r + j] = s->lora_b[j * N + n];
+            break;
+        }
         case BITQ_W2A8:
         case BITQ_WNAM: {
             const int64_t G = K / 128;
@@ -290,6 +328,7 @@ bitq_status pack_impl(const bitq_wdesc& d, const bitq_logical* s, void* dstv, si
                         [&](int64_t p, int64_t n, int64_t k) { return s->sign[(p * N + n) * K + k] > 0; });
             break;
         case BITQ_TERNARY:
+        case BITQ_HGF:
             pack_planes(d, L, dst, nthreads, [&](int64_t p, int64_t n, int64_t k) {
                 int8_t t = s->tern[n * K + k];
                 return p == 0 ? t == 1 : t == -1;
@@ -317,6 +356,19 @@ bitq_status pack_impl(const bitq_wdesc& d, const bitq_logical* s, void* dstv, si
             hb[p] = static_cast<float>(m);
         }
         std::memcpy(dst + kHdrHBound, hb, sizeof(hb));
+    }
+    if (d.fmt == BITQ_HGF) {
+        // the gate tanh(alpha) is a property of the weights: computed here
+        // once (fp64, rounded to fp32); amax_a bounds the activation step's
+        // fixed-point sums
+        const float alpha = s->lora_alpha;
+        const float gate = static_cast<float>(std::tanh(static_cast<double>(alpha)));
+        double am = 0.0;
+        for (int64_t i = 0; i < K * d.rank; ++i) am = std::max(am, std::fabs(f16_to_f64(s->lora_a[i])));
+        const float amax_a = static_cast<float>(am);
+        std::memcpy(dst + kHdrAlpha, &alpha, 4);
+        std::memcpy(dst + kHdrGate, &gate, 4);
+        std::memcpy(dst + kHdrAmaxA, &amax_a, 4);
     }
     return ok();
 }
@@ -634,14 +686,17 @@ BlobLayout blob_layout(const bitq_wdesc& d) {
         case BITQ_W2A8:
         case BITQ_WNAM: L.c0_bytes = 4 * L.Np * L.Tb; L.c1_bytes = 0; break;
         case BITQ_BVSR4: L.c0_bytes = L.Np * (L.Kp / 32); L.c1_bytes = 256 * 5 * 4; break;
+        case BITQ_HGF: L.c0_bytes = 4; L.c1_bytes = 2 * static_cast<size_t>(d.rank) * L.Kp; break;
         default: L.c0_bytes = L.c1_bytes = 0;
     }
     L.off_c1 = align256(L.off_c0 + L.c0_bytes);
-    L.total = align256(L.off_c1 + L.c1_bytes);
+    L.off_c2 = align256(L.off_c1 + L.c1_bytes);
+    L.c2_bytes = d.fmt == BITQ_HGF ? 2 * static_cast<size_t>(L.Np) * d.rank : 0;
+    L.total = align256(L.off_c2 + L.c2_bytes);
     return L;
 }
 
-ActLayout act_layout(int M, int K) {
+ActLayout act_layout(int M, int K, int rank) {
     ActLayout A{};
     A.M = M;
     A.K = K;
@@ -651,7 +706,8 @@ ActLayout act_layout(int M, int K) {
     A.off_S = align256(static_cast<size_t>(M * A.Kw) * 32);
     A.off_q = align256(A.off_S + static_cast<size_t>(M * A.Kw) * 4);
     A.off_d = align256(A.off_q + static_cast<size_t>(M * A.Kp));
-    A.total = align256(A.off_d + 4 * static_cast<size_t>(M));
+    A.off_h = align256(A.off_d + 4 * static_cast<size_t>(M));
+    A.total = align256(A.off_h + 4 * static_cast<size_t>(M) * rank);
     return A;
 }
 
@@ -828,6 +884,9 @@ bitq_status bitq_quantize_weights_opts(const bitq_wdesc* desc, const float* W, c
                 lg.delta = delta.data();
                 lg.zero = zero.data();
                 break;
+            case BITQ_HGF:
+                return fail(BITQ_E_UNSUPPORTED, "HGF layers are packed with bitq_pack_weights (the correction "
+                                                "path's A, B and alpha are trained parameters, not derived from W)");
             case BITQ_BVSR4:
                 cache.resize(256 * 5);
                 bvsr_cache(d, W, cache.data());
@@ -873,6 +932,42 @@ bitq_status bitq_quantize_act_bits(const void* x_dev, int32_t x_dtype, int32_t M
     if (e) return fail(BITQ_E_DEVICE, "HIP error %d while querying the device", e);
     if (!is950) return fail(BITQ_E_UNSUPPORTED, "current device is not gfx950");
     e = launch_quantize_act(x_dev, x_dtype, M, K, abits, act_dev, stream);
+    if (e) return fail(BITQ_E_DEVICE, "HIP launch error %d", e);
+    return ok();
+}
+
+bitq_status bitq_hgf_act_size(const bitq_wdesc* desc, int32_t M, size_t* act_bytes, size_t* ws_bytes) {
+    bitq_status s = check_desc(desc);
+    if (s) return s;
+    if (desc->fmt != BITQ_HGF) return fail(BITQ_E_ARG, "bitq_hgf_act_size needs an HGF descriptor");
+    if (!act_bytes || !ws_bytes) return fail(BITQ_E_ARG, "act_bytes/ws_bytes is NULL");
+    if (M < 1 || M > 64) return fail(BITQ_E_SHAPE, "M=%d out of range [1, 64]", M);
+    *act_bytes = act_layout(M, desc->K, desc->rank).total;
+    *ws_bytes = align256(8 * static_cast<size_t>(M) * desc->rank);
+    return ok();
+}
+
+bitq_status bitq_quantize_act_hgf(const bitq_wdesc* desc, const void* w_dev, const void* x_dev, int32_t x_dtype,
+                                  int32_t M, void* act_dev, size_t act_bytes, void* ws_dev, size_t ws_bytes,
+                                  void* stream) {
+    size_t need_act = 0, need_ws = 0;
+    bitq_status s = bitq_hgf_act_size(desc, M, &need_act, &need_ws);
+    if (s) return s;
+    if (!w_dev || !x_dev || !act_dev || !ws_dev) return fail(BITQ_E_ARG, "a device pointer is NULL");
+    if (x_dtype != BITQ_DT_F32 && x_dtype != BITQ_DT_BF16)
+        return fail(BITQ_E_ARG, "x_dtype must be BITQ_DT_F32 or BITQ_DT_BF16");
+    if (!aligned(x_dev, 16)) return fail(BITQ_E_ALIGN, "x_dev must be 16-byte aligned");
+    if (!aligned(w_dev, 256) || !aligned(act_dev, 256) || !aligned(ws_dev, 256))
+        return fail(BITQ_E_ALIGN, "w_dev, act_dev and ws_dev must be 256-byte aligned");
+    if (act_bytes < need_act)
+        return fail(BITQ_E_CAPACITY, "act buffer has %zu bytes, needs %zu", act_bytes, need_act);
+    if (ws_bytes < need_ws) return fail(BITQ_E_CAPACITY, "workspace has %zu bytes, needs %zu", ws_bytes, need_ws);
+    int is950 = 0;
+    int e = current_device_is_gfx950(&is950);
+    if (e) return fail(BITQ_E_DEVICE, "HIP error %d while querying the device", e);
+    if (!is950) return fail(BITQ_E_UNSUPPORTED, "current device is not gfx950");
+    e = launch_quantize_act_hgf(x_dev, x_dtype, M, desc->K, desc->rank, w_dev, blob_layout(*desc), act_dev, ws_dev,
+                                stream);
     if (e) return fail(BITQ_E_DEVICE, "HIP launch error %d", e);
     return ok();
 }
@@ -946,7 +1041,7 @@ static bitq_status gemv_common(const bitq_wdesc* desc, const void* w_dev, const 
         if (!aligned(x_dev, 16)) return fail(BITQ_E_ALIGN, "x_dev must be 16-byte aligned");
     } else {
         if (x_dtype != BITQ_DT_ACT)
-            return fail(BITQ_E_ARG, "TERNARY/W2A8/BVSR4/WNAM take an activation buffer (BITQ_DT_ACT)");
+            return fail(BITQ_E_ARG, "TERNARY/W2A8/BVSR4/WNAM/HGF take an activation buffer (BITQ_DT_ACT)");
         if (!aligned(x_dev, 256)) return fail(BITQ_E_ALIGN, "activation buffer must be 256-byte aligned");
     }
     if (!aligned(w_dev, 256)) return fail(BITQ_E_ALIGN, "w_dev must be 256-byte aligned");
@@ -981,7 +1076,7 @@ bitq_status bitq_gemm_smallM(const bitq_wdesc* desc, const void* w_dev, const vo
     if (s) return s;
     if (desc->fmt == BITQ_RABIT)
         return fail(BITQ_E_UNSUPPORTED, "bitq_gemm_smallM supports SIGN1 (binary activations), TERNARY, W2A8, "
-                                        "BVSR4 and WNAM");
+                                        "BVSR4, WNAM and HGF");
     if (M < 2 || M > 64) return fail(BITQ_E_SHAPE, "M=%d out of range [2, 64]", M);
     const int32_t dt = desc->fmt == BITQ_SIGN1 ? BITQ_DT_BINARY : BITQ_DT_ACT;
     return gemv_common(desc, w_dev, act_dev, dt, M, y_dev, ws_dev, ws_bytes, flags, stream);

@@ -15,6 +15,9 @@ constexpr int kHeaderBytes = 256;
 constexpr uint32_t kMagic = 0x51544942u;
 constexpr int kHdrHBound = 72;    // header: f32 [3] max_k |h_p[k]| (SIGN1: 1)
 constexpr int kMaxFloatK = 63 * 8 * kKBlock;  // float formats: <= 63 splits of <= 8 k blocks
+// HGF header fields: u64 off_c2, u32 rank, f32 alpha, f32 gate, f32 amax_a
+constexpr int kHdrOffC2 = 88, kHdrRank = 96, kHdrAlpha = 100, kHdrGate = 104, kHdrAmaxA = 108;
+constexpr int kMaxHgfK = 63 * 256;  // HGF: <= 63 runs of 256 inputs meet in one fixed-point word
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -25,16 +28,18 @@ struct BlobLayout {
     size_t off_planes, planes_bytes;
     size_t off_c0, c0_bytes;
     size_t off_c1, c1_bytes;
+    size_t off_c2, c2_bytes;  // HGF: B transposed (otherwise off_c2 = total, 0 bytes)
     size_t total;
 };
 BlobLayout blob_layout(const bitq_wdesc& d);
 
-// Byte layout of an activation buffer (see bitq_quantize_act).
+// Byte layout of an activation buffer (see bitq_quantize_act); rank > 0
+// adds the HGF section h f32 [M][rank].
 struct ActLayout {
     int64_t M, K, Kp, Kw;
-    size_t off_planes, off_S, off_q, off_d, total;
+    size_t off_planes, off_S, off_q, off_d, off_h, total;
 };
-ActLayout act_layout(int M, int K);
+ActLayout act_layout(int M, int K, int rank = 0);
 
 // Byte layout of a binary activation buffer (see bitq_binarize_act).
 struct BinActLayout {
@@ -64,6 +69,8 @@ int launch_gemv_float(const bitq_wdesc& d, const Plan& plan, const void* w, cons
                       int x_dtype, float* y, void* ws, void* stream);
 int launch_gemv_int(const bitq_wdesc& d, const Plan& plan, const void* w, const void* act,
                     int M, float* y, void* ws, uint32_t flags, void* stream);
+int launch_quantize_act_hgf(const void* x, int x_dtype, int M, int K, int rank, const void* w, const BlobLayout& L,
+                            void* act, void* ws, void* stream);
 int launch_binarize_act(const void* x, int x_dtype, int M, int K, void* act, void* stream);
 int launch_gemv_xnor(const bitq_wdesc& d, const void* w, const void* act, int M, float* y, uint32_t flags,
                      void* stream);

@@ -58,16 +58,51 @@ __device__ __forceinline__ float wave_max(float v) {
 // inputs in LDS), then each lane quantizes one input and each of the
 // 8 planes of the wave's 64 inputs comes out of one ballot: bit i of the
 // ballot of (q >> j) & 1 is plane j of input i.
+//
+// RANK > 0 (HGF layers) adds the correction path's down projection
+// ([HGF] §2.1) h = silu(x A) over the same unquantized inputs: thread
+// (c, j) = (tid / RANK, tid % RANK) sums x_k A[k][j] in fp32 over the run
+// k = lo + RANK c + i, i < RANK (row j of A^T, RANK/8 16-byte loads issued
+// together), the 256/RANK runs of a column are added in order through LDS,
+// and the workgroups of a token meet in one 64-bit fixed-point word per
+// column (lora_arrive below); the workgroup that completes a column applies
+// silu and writes h.
 template <int DT>
 __device__ __forceinline__ float act_at(const void* x, size_t i) {
     if (DT == BITQ_DT_F32) return static_cast<const float*>(x)[i];
     return bf16_to_f32(static_cast<const uint16_t*>(x)[i]);
 }
 
-template <int DT>
+// Exact cross-workgroup sum of the down projection: each of the `arrivals`
+// workgroups of a token adds (1 << 58) + rint(part 2^S) to the column's word
+// (the count in the top 6 bits, the fixed-point sum below, as in the float
+// GEMV's split-k hand-off).  S = 52 - e with the bound K amax_x amax_a < 2^e,
+// which bounds every partial sum of the column's terms, so the sum never
+// reaches the count field.  The last arrival turns the total back into z,
+// writes silu(z) = z / (1 + exp(-z)) and resets the word.
+__device__ __forceinline__ void lora_arrive(unsigned long long* word, float part, double bound, int arrivals,
+                                            float* h) {
+    int e = 0;
+    if (bound > 0.0) (void)frexp(bound, &e);  // bound < 2^e
+    const int S = 52 - e;
+    const long long v = static_cast<long long>(rint(ldexp(static_cast<double>(part), S)));
+    const unsigned long long add = (1ull << 58) + static_cast<unsigned long long>(v);
+    const unsigned long long prev = __hip_atomic_fetch_add(word, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long arrived = (prev + (1ull << 57)) >> 58;
+    if (arrived != static_cast<unsigned long long>(arrivals - 1)) return;
+    const long long total = static_cast<long long>(prev + add - (static_cast<unsigned long long>(arrivals) << 58));
+    const float z = static_cast<float>(ldexp(static_cast<double>(total), -S));
+    *h = z / (1.0f + expf(-z));
+    __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int DT, int RANK>
 __global__ __launch_bounds__(256) void quant_act_kernel(const void* __restrict__ x, int K, int Kw, float qmax,
                                                         uint32_t* __restrict__ planes, int32_t* __restrict__ S,
-                                                        int8_t* __restrict__ q, float* __restrict__ dq) {
+                                                        int8_t* __restrict__ q, float* __restrict__ dq,
+                                                        const uint8_t* __restrict__ blob, size_t off_at, int Kp,
+                                                        unsigned long long* __restrict__ ws,
+                                                        float* __restrict__ hout) {
     constexpr int VEC = (DT == BITQ_DT_F32) ? 4 : 8;  // inputs per 16-byte load
     constexpr int HOLD = 4;                            // 16-byte loads kept per thread
     __shared__ float s_red[4];
@@ -120,6 +155,38 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const void* __restrict__
     if (lane == 0) s_red[wave] = amax;
     __syncthreads();
     amax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    if constexpr (RANK > 0) {
+        __shared__ float s_part[256];
+        const int c = tid / RANK, j = tid % RANK;
+        const int k0 = lo + RANK * c;  // this thread's run; inputs past K count as 0
+        const int kc = min(k0, Kp - RANK);  // in-bounds row position (runs past Kp have x = 0)
+        const uint16_t* at = reinterpret_cast<const uint16_t*>(blob + off_at);  // A^T [RANK][Kp]
+        const float amax_a = *reinterpret_cast<const float*>(blob + kHdrAmaxA);
+        const uint4* arow = reinterpret_cast<const uint4*>(at + static_cast<size_t>(j) * Kp + kc);
+        uint4 av[RANK / 8];
+#pragma unroll
+        for (int i = 0; i < RANK / 8; ++i) av[i] = arow[i];
+        float part = 0.0f;
+#pragma unroll
+        for (int i = 0; i < RANK / 8; ++i) {
+            const uint32_t a[4] = {av[i].x, av[i].y, av[i].z, av[i].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int k = k0 + 8 * i + e;
+                const float xk = (k < K) ? s_slice[k - lo] : 0.0f;
+                part = fmaf(xk, f16_bits_to_f32(a[e >> 1] >> (16 * (e & 1))), part);
+            }
+        }
+        s_part[tid] = part;
+        __syncthreads();
+        if (tid < RANK) {
+            float col = 0.0f;
+            for (int cc = 0; cc < 256 / RANK; ++cc) col += s_part[RANK * cc + tid];
+            const double bound = static_cast<double>(K) * static_cast<double>(amax) * static_cast<double>(amax_a);
+            lora_arrive(&ws[static_cast<size_t>(m) * RANK + tid], col, bound, static_cast<int>(gridDim.x),
+                        &hout[static_cast<size_t>(m) * RANK + tid]);
+        }
+    }
     float s = 0.0f;
     if (amax > 0.0f) s = __fdiv_rn(qmax, amax);
     if (blockIdx.x == 0 && tid == 0) dq[m] = (amax > 0.0f) ? __fdiv_rn(amax, qmax) : 0.0f;
@@ -467,6 +534,10 @@ __device__ __forceinline__ void barrier_after_loads() {
     asm volatile("" ::: "memory");
 }
 
+// A wave-uniform value moved to a scalar register (the compiler cannot tell
+// that threadIdx.x / 64 is uniform).
+__device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 // Horner combination of per-plane popcounts: sum_j c_j a_j.
 __device__ __forceinline__ int combine_planes(const int (&a)[8]) {
     int r = -a[7];
@@ -484,11 +555,20 @@ __device__ __forceinline__ int combine_planes(const int (&a)[8]) {
 // planes and group sums of the round are staged once in LDS; the G k-groups'
 // results for a row are added in a fixed order (lane exchanges, then four
 // waves through LDS).
+//
+// HGF layers run the ternary loop and add, in the epilogue of each row, the
+// correction's up projection gate sum_j h_j B[j][n] ([HGF] §4.1 asks for the
+// ternary product and the correction in one kernel): the workgroup's RG rows
+// of B^T (RG rank fp16) and the token's h (rank floats, written by the
+// activation step) are copied into LDS ahead of the weight stream.
 template <int FMT, int P, bool ACC, int BPL, int RG, bool ONE>
 __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __restrict__ blob, size_t off_c0,
                                                            size_t off_c1, const uint8_t* __restrict__ act,
                                                            size_t act_off_S, size_t act_off_d, int M, int N, int K,
-                                                           int Tb, int abits, float* __restrict__ y) {
+                                                           int Tb, int abits, size_t off_c2, size_t act_off_h,
+                                                           int rank, float* __restrict__ y) {
+    constexpr bool TERN = FMT == BITQ_TERNARY || FMT == BITQ_HGF;  // ternary planes
+    constexpr bool LORA = FMT == BITQ_HGF && !ACC;                 // the correction epilogue
     constexpr int G = 256 / RG;    // k-groups: lanes that share a row
     constexpr int Q = 64 / RG;     // row groups per 64-row tile
     constexpr int NBW = G * BPL;   // k blocks per round
@@ -503,10 +583,21 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
     __shared__ __attribute__((aligned(16))) uint32_t s_act[SLOT_PASSES * 256 * 4];
     __shared__ __attribute__((aligned(16))) int32_t s_S[S_PASSES * 256 * 4];
     __shared__ float4 s_cache[FMT == BITQ_BVSR4 ? 512 : 1];
+    // HGF: B^T rows of the group (RG x rank fp16, rank <= 64: RG 8 slots of
+    // 16 bytes) and h of the current token (rank floats; the copy fills one
+    // 16-byte slot per lane of a wave: 64 slots).  Declared as one word
+    // array: with vector-typed arrays of template-dependent size here, this
+    // compiler drops the kernel's host-side stub.
+    __shared__ __attribute__((aligned(16))) uint32_t s_lora[FMT == BITQ_HGF ? (RG * 8 + 64) * 4 : 4];
+    uint4* const s_bt = reinterpret_cast<uint4*>(s_lora);
+    float4* const s_h = reinterpret_cast<float4*>(s_lora + RG * 8 * 4);
     __shared__ float s_red[4][16];
     __shared__ int32_t s_redi[4][16];
 
     const int tid = threadIdx.x, r = tid % RG, g = tid / RG, wave = tid >> 6;
+    // the wave index as a uniform value, for branches around the LDS copies
+    // (their LDS destination must be uniform)
+    const int wave_u = wave_uniform(wave);
     // Workgroup wg runs on XCD wg mod 8 (round-robin dispatch); the Q row
     // groups of a 64-row tile go to workgroups wg, wg+8, ..., wg+8(Q-1) of one
     // XCD, so the tile's coefficient lines (64 rows x 4 bytes) are fetched
@@ -563,6 +654,12 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
         for (int v = 0; v < S_PASSES; ++v)
             __builtin_amdgcn_global_load_lds(srcS + min(tid + 256 * v, last),
                                              reinterpret_cast<int4*>(s_S) + 256 * v + 64 * wave, 16, 0, 0);
+        if (LORA && b_base == 0 && wave_u == 0) {  // h[m]: rank / 4 16-byte slots
+            const float4* hsrc = reinterpret_cast<const float4*>(act + act_off_h) + static_cast<size_t>(m) * (rank / 4);
+            // (wave_u is 0 here; a destination computed from it, rather than
+            // the constant s_h, avoids a crash of this compiler's SGPR-copy pass)
+            __builtin_amdgcn_global_load_lds(hsrc + min(tid, rank / 4 - 1), s_h + 64 * wave_u, 16, 0, 0);
+        }
     };
 
     // Issue order: coefficient cache (BVSR), activation copies, then the
@@ -580,6 +677,13 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
                                              reinterpret_cast<float*>(s_cache) + 256 * v + 64 * wave, 4, 0, 0);
         }
     }
+    if (LORA && wave_u < RG / 8) {
+        // B^T rows 64t + RG quarter .. + RG - 1 are contiguous: RG rank / 8
+        // 16-byte slots (<= 128, waves 0 and 1; the rows exist up to Np)
+        const uint4* bsrc = reinterpret_cast<const uint4*>(blob + off_c2) +
+                            static_cast<size_t>(64 * t + RG * quarter) * (rank / 8);
+        __builtin_amdgcn_global_load_lds(bsrc + min(tid, RG * (rank / 8) - 1), s_bt + 64 * wave_u, 16, 0, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
     if (ONE) stage(0, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -591,8 +695,9 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
     auto pass = [&](int m, bool first) __attribute__((always_inline)) {
         // per-token (and per-tensor) scales: uniform loads issued now, long
         // before the epilogue needs them
-        const float scale = (FMT == BITQ_TERNARY && !ACC ? *reinterpret_cast<const float*>(blob + off_c0) : 1.0f) *
+        const float scale = (TERN && !ACC ? *reinterpret_cast<const float*>(blob + off_c0) : 1.0f) *
                             (ACC ? 1.0f : ad[m]);
+        const float gate = LORA ? *reinterpret_cast<const float*>(blob + kHdrGate) : 0.0f;
         float yacc = 0.0f;
         int tacc[2][8];
 #pragma unroll
@@ -626,7 +731,7 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
                 // it, above the barrier, ahead of the whole weight stream.
                 uint32_t cw = coef[j];
                 asm volatile("" : "+v"(cw));
-                if (FMT == BITQ_TERNARY) {
+                if (TERN) {
 #pragma unroll
                     for (int w = 0; w < 4; ++w) {
                         const uint4 x0 = *reinterpret_cast<const uint4*>(xa + 8 * w);
@@ -745,10 +850,10 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
                 }
             }
         }
-        if (ACC && FMT != BITQ_TERNARY) return;  // partials already written per group
+        if (ACC && !TERN) return;  // partials already written per group
 
         // ---- add the G k-groups of each row in a fixed order
-        if (FMT == BITQ_TERNARY && ACC) {
+        if (TERN && ACC) {
             int Y[8];
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) Y[jj] = tacc[0][jj] - tacc[1][jj];
@@ -762,7 +867,7 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
                     (s_redi[0][r] + s_redi[1][r]) + (s_redi[2][r] + s_redi[3][r]);
         } else {
             float v;
-            if (FMT == BITQ_TERNARY) {
+            if (TERN) {
                 int Y[8];
 #pragma unroll
                 for (int jj = 0; jj < 8; ++jj) Y[jj] = tacc[0][jj] - tacc[1][jj];
@@ -777,6 +882,23 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
             if (tid < RG && n < N) {
                 float tot = (s_red[0][r] + s_red[1][r]) + (s_red[2][r] + s_red[3][r]);
                 tot = scale * tot;
+                if (LORA) {  // gate sum_j h_j B[j][n], fp32 in j order
+                    float l = 0.0f;
+                    const uint4* bt = &s_bt[r * (rank / 8)];
+                    for (int c = 0; c < rank / 8; ++c) {
+                        const uint4 b = bt[c];
+                        const float4 h0 = s_h[2 * c], h1 = s_h[2 * c + 1];
+                        l = fmaf(h0.x, f16_bits_to_f32(b.x), l);
+                        l = fmaf(h0.y, f16_bits_to_f32(b.x >> 16), l);
+                        l = fmaf(h0.z, f16_bits_to_f32(b.y), l);
+                        l = fmaf(h0.w, f16_bits_to_f32(b.y >> 16), l);
+                        l = fmaf(h1.x, f16_bits_to_f32(b.z), l);
+                        l = fmaf(h1.y, f16_bits_to_f32(b.z >> 16), l);
+                        l = fmaf(h1.z, f16_bits_to_f32(b.w), l);
+                        l = fmaf(h1.w, f16_bits_to_f32(b.w >> 16), l);
+                    }
+                    tot = fmaf(gate, l, tot);
+                }
                 y[static_cast<size_t>(m) * N + n] = tot;
             }
         }
@@ -945,11 +1067,53 @@ int launch_quantize_act(const void* x, int x_dtype, int M, int K, int abits, voi
     const dim3 grid((Kw + 7) / 8, M);
     const float qmax = static_cast<float>((1 << (abits - 1)) - 1);  // 127 for int8
     if (x_dtype == BITQ_DT_F32)
-        hipLaunchKernelGGL(quant_act_kernel<BITQ_DT_F32>, grid, dim3(256), 0, static_cast<hipStream_t>(stream), x,
-                           K, Kw, qmax, planes, S, q, d);
+        hipLaunchKernelGGL((quant_act_kernel<BITQ_DT_F32, 0>), grid, dim3(256), 0, static_cast<hipStream_t>(stream),
+                           x, K, Kw, qmax, planes, S, q, d, nullptr, 0, 0, nullptr, nullptr);
     else
-        hipLaunchKernelGGL(quant_act_kernel<BITQ_DT_BF16>, grid, dim3(256), 0, static_cast<hipStream_t>(stream), x,
-                           K, Kw, qmax, planes, S, q, d);
+        hipLaunchKernelGGL((quant_act_kernel<BITQ_DT_BF16, 0>), grid, dim3(256), 0, static_cast<hipStream_t>(stream),
+                           x, K, Kw, qmax, planes, S, q, d, nullptr, 0, 0, nullptr, nullptr);
+    return static_cast<int>(hipGetLastError());
+}
+
+template <int DT, int RANK>
+static void launch_quant_hgf(dim3 grid, hipStream_t st, const void* x, int K, int Kw, uint32_t* planes, int32_t* S,
+                             int8_t* q, float* d, const uint8_t* blob, size_t off_at, int Kp,
+                             unsigned long long* ws, float* h) {
+    hipLaunchKernelGGL((quant_act_kernel<DT, RANK>), grid, dim3(256), 0, st, x, K, Kw, 127.0f, planes, S, q, d, blob,
+                       off_at, Kp, ws, h);
+}
+
+template <int DT>
+static void launch_quant_hgf_rank(int rank, dim3 grid, hipStream_t st, const void* x, int K, int Kw,
+                                  uint32_t* planes, int32_t* S, int8_t* q, float* d, const uint8_t* blob,
+                                  size_t off_at, int Kp, unsigned long long* ws, float* h) {
+    switch (rank) {
+        case 8: launch_quant_hgf<DT, 8>(grid, st, x, K, Kw, planes, S, q, d, blob, off_at, Kp, ws, h); break;
+        case 16: launch_quant_hgf<DT, 16>(grid, st, x, K, Kw, planes, S, q, d, blob, off_at, Kp, ws, h); break;
+        case 32: launch_quant_hgf<DT, 32>(grid, st, x, K, Kw, planes, S, q, d, blob, off_at, Kp, ws, h); break;
+        default: launch_quant_hgf<DT, 64>(grid, st, x, K, Kw, planes, S, q, d, blob, off_at, Kp, ws, h); break;
+    }
+}
+
+int launch_quantize_act_hgf(const void* x, int x_dtype, int M, int K, int rank, const void* w, const BlobLayout& L,
+                            void* act, void* ws, void* stream) {
+    ActLayout A = act_layout(M, K, rank);
+    uint8_t* base = static_cast<uint8_t*>(act);
+    auto* planes = reinterpret_cast<uint32_t*>(base + A.off_planes);
+    auto* S = reinterpret_cast<int32_t*>(base + A.off_S);
+    auto* q = reinterpret_cast<int8_t*>(base + A.off_q);
+    auto* d = reinterpret_cast<float*>(base + A.off_d);
+    auto* h = reinterpret_cast<float*>(base + A.off_h);
+    const int Kw = static_cast<int>(A.Kw);
+    const dim3 grid((Kw + 7) / 8, M);
+    const uint8_t* blob = static_cast<const uint8_t*>(w);  // A^T and amax_a are read by the kernel
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    auto* wsw = static_cast<unsigned long long*>(ws);
+    const int Kp = static_cast<int>(L.Kp);
+    if (x_dtype == BITQ_DT_F32)
+        launch_quant_hgf_rank<BITQ_DT_F32>(rank, grid, st, x, K, Kw, planes, S, q, d, blob, L.off_c1, Kp, wsw, h);
+    else
+        launch_quant_hgf_rank<BITQ_DT_BF16>(rank, grid, st, x, K, Kw, planes, S, q, d, blob, L.off_c1, Kp, wsw, h);
     return static_cast<int>(hipGetLastError());
 }
 
@@ -1002,7 +1166,7 @@ int launch_gemv_float(const bitq_wdesc& d, const Plan& pl, const void* w, const 
 template <int FMT, int P, bool ACC, int BPL, int RG>
 static void launch_nr_bpl(const bitq_wdesc& d, const BlobLayout& L, const void* w, const void* act, int M,
                           float* y, hipStream_t st) {
-    ActLayout A = act_layout(M, d.K);
+    ActLayout A = act_layout(M, d.K, d.rank);
     // 64/RG row groups per 64-row tile, tiles dealt round-robin to the 8 XCDs:
     // the grid is padded to whole rounds of 8 tiles (extra workgroups exit)
     const int tiles = static_cast<int>(L.Tn);
@@ -1012,7 +1176,7 @@ static void launch_nr_bpl(const bitq_wdesc& d, const BlobLayout& L, const void* 
     const int abits = d.fmt == BITQ_WNAM ? d.abits : 8;
     hipLaunchKernelGGL(kern, dim3(groups), dim3(256), 0, st, static_cast<const uint8_t*>(w), L.off_c0, L.off_c1,
                        static_cast<const uint8_t*>(act), A.off_S, A.off_d, M, d.N, d.K, static_cast<int>(L.Tb),
-                       abits, y);
+                       abits, L.off_c2, A.off_h, d.rank, y);
 }
 
 template <int FMT, int P, bool ACC, int RG>
@@ -1115,6 +1279,10 @@ int launch_gemv_int(const bitq_wdesc& d, const Plan& pl, const void* w, const vo
         case BITQ_TERNARY:
             acc ? launch_nr<BITQ_TERNARY, 2, true>(d, pl, L, w, act, M, y, st)
                 : launch_nr<BITQ_TERNARY, 2, false>(d, pl, L, w, act, M, y, st);
+            break;
+        case BITQ_HGF:  // the exact partials Y are the ternary kernel's
+            acc ? launch_nr<BITQ_TERNARY, 2, true>(d, pl, L, w, act, M, y, st)
+                : launch_nr<BITQ_HGF, 2, false>(d, pl, L, w, act, M, y, st);
             break;
         case BITQ_W2A8:
             acc ? launch_nr<BITQ_W2A8, 2, true>(d, pl, L, w, act, M, y, st)

@@ -7,7 +7,8 @@
  *   [RaBiT]  "RaBiT框架：突破2比特量化性能瓶颈的LLM部署方案"
  *            (2-path residual binarization W^ = g1.B1.h1 + g2.B2.h2)
  *   [HGF]    "1.58位LLM混合门控流优化技术解析"
- *            (ternary weights with absmean gamma, int8 activations)
+ *            (ternary weights with absmean gamma, int8 activations, a gated
+ *             low-rank fp16 correction path)
  *   [ABQ]    "ABQ-LLM：用于大語言模型的任意比特量化推理加速"
  *            (arbitrary-bit weight/activation planes, binary-TensorCore-
  *             equivalent integer GEMV)
@@ -73,11 +74,17 @@ typedef enum {
                           beta_0..3 and a coefficient set (c_0..c_3, b) picked by
                           a u8 index from a shared 256-entry cache of fp32 sets.
                           planes = 4, group = 32. */
-    BITQ_WNAM = 6      /* [ABQ] §1 arbitrary-bit WnAm: n-bit asymmetric codes
+    BITQ_WNAM = 6,     /* [ABQ] §1 arbitrary-bit WnAm: n-bit asymmetric codes
                           q in 0..2^n-1, W^ = delta * (q - z) per group of 128
                           inputs (delta, z fp16; the W2A8 arithmetic with
                           2^n - 1 steps), times m-bit symmetric activations.
                           planes = n (1..4), group = 128, abits = m (2..8). */
+    BITQ_HGF = 7       /* [HGF] §2.1 and §4.1: the TERNARY layer plus a gated
+                          low-rank correction of its unquantized input x:
+                          y = gamma d (T q) + tanh(alpha) (silu(x A) B), with
+                          A [K][r] and B [r][N] in fp16 and the gate parameter
+                          alpha in fp32.  planes = 2, group = 0, rank = r
+                          (8, 16, 32 or 64), K <= 16128. */
 } bitq_format;
 
 /* Activation dtypes accepted by bitq_quantize_act / bitq_gemv. */
@@ -106,6 +113,8 @@ typedef struct {
                          other integer formats 0 or 8 (int8); float formats 0.
                          Activation buffers passed to the GEMV must have been
                          written with the same bit count. */
+    int32_t rank;     /* HGF: rank r of the correction path (8, 16, 32, 64);
+                         0 for every other format */
 } bitq_wdesc;
 
 /*
@@ -122,6 +131,8 @@ typedef struct {
  *                cache [256][5] as (c0, c1, c2, c3, b)
  *   BITQ_WNAM    code [N][K] (0..2^n-1), delta [N][K/128], zero [N][K/128]
  *                (zero must hold an integer 0..2^n-1)
+ *   BITQ_HGF     tern [N][K] (-1/0/+1), gamma, lora_a [K][r], lora_b [r][N]
+ *                (finite fp16), lora_alpha (finite)
  *
  * This mirrors the weight-parameter struct of [BitNet] §3.2 (binary weights,
  * scales, optional zero points) generalized to the six formats.
@@ -138,6 +149,9 @@ typedef struct {
     const uint16_t* zero;
     const uint8_t*  idx;
     const float*    cache;
+    const uint16_t* lora_a;
+    const uint16_t* lora_b;
+    float           lora_alpha;
 } bitq_logical;
 
 /*
@@ -149,7 +163,9 @@ typedef struct {
  *     u32 reserved (0), u64 off_planes, u64 off_c0, u64 off_c1,
  *     u64 total_bytes, then at byte 72 f32 hbound[3]: SIGN1 1, RABIT
  *     max_k |h_p[k]| for p < P (the float GEMV bounds its split-k sums with
- *     it); the rest is zero.
+ *     it); HGF only, from byte 88: u64 off_c2, u32 rank, f32 alpha,
+ *     f32 gate = tanh(alpha) (fp64, rounded to fp32), f32 amax_a =
+ *     max |A|; the rest is zero.
  *   planes section: tiles of 64 rows x 128 inputs x 1 plane = 1024 bytes,
  *     ordered [row tile t][k block b][plane p].  Inside a tile, row
  *     r = n - 64t owns 16 contiguous bytes = 4 uint32 words; word w holds
@@ -159,7 +175,7 @@ typedef struct {
  *     output rows stored next to each other).  Rows >= N and inputs >= K are
  *     zero bits.
  *   plane meaning: SIGN1/RABIT bit 1 <-> +1, 0 <-> -1 (one plane per path);
- *     TERNARY plane 0 = [T == +1], plane 1 = [T == -1]; W2A8 plane i = bit i
+ *     TERNARY and HGF plane 0 = [T == +1], plane 1 = [T == -1]; W2A8 plane i = bit i
  *     of q; BVSR4 plane k = beta_k.
  *   coefficient sections (zero-padded):
  *     SIGN1   c0 = alpha f32 [Np]
@@ -168,6 +184,9 @@ typedef struct {
  *     W2A8    c0 = u32 [Np/64][Kp/128][64]: low 16 bits delta, high 16 bits z
  *     BVSR4   c0 = idx u8 [Np/64][Kp/128][64][4] (byte j: group 4b + j);
  *             c1 = cache f32 [256][5]
+ *     HGF     c0 = gamma f32 [1];  c1 = A transposed, f16 [r][Kp] (row j
+ *             holds A[k][j] for every k);  c2 = B transposed, f16 [Np][r]
+ *             (row n holds B[j][n] for every j)
  *   Every section starts at a multiple of 256 bytes; off_c1 = total_bytes
  *   when a format has no c1 section.
  */
@@ -256,6 +275,37 @@ bitq_status bitq_quantize_act_bits(const void* x_dev, int32_t x_dtype, int32_t M
                                    int32_t abits, void* act_dev, size_t act_bytes, void* stream);
 
 /*
+ * HGF activation buffer: the sections of bitq_act_size(M, K), then, at the
+ * next multiple of 256 bytes,
+ *   h  f32 [M][r]   h[m] = silu(x[m] A), the correction path's hidden vector.
+ * ws_bytes is the workspace of bitq_quantize_act_hgf: M*r 64-bit words.  The
+ * caller zero-fills it once before its first use; every completed call
+ * leaves it zero again, so it is reused without clearing.  Calls that share
+ * a workspace must be ordered (same stream).
+ */
+bitq_status bitq_hgf_act_size(const bitq_wdesc* desc, int32_t M, size_t* act_bytes, size_t* ws_bytes);
+
+/*
+ * Activation step of an HGF layer: the int8 quantization of
+ * bitq_quantize_act ([HGF] §1.2; bit-exact, the same sections), and from the
+ * same unquantized input the correction's down projection ([HGF] §2.1)
+ *   h[m][j] = silu(z), z = sum_k x[m][k] A[k][j], silu(z) = z / (1 + exp(-z)).
+ * z is summed in fp32 over each run of 256 inputs.  The runs are then added
+ * exactly as 64-bit fixed-point integers, scaled to the bound
+ * K max_k|x[m][k]| amax_a, so h does not depend on workgroup order; the
+ * arrival count shares the word, and the run that completes a sum applies
+ * silu in fp32.
+ *   desc    an HGF descriptor; w_dev its packed blob (device, 256-byte aligned)
+ *   x_dev   device [M][K] fp32 or bf16, 16-byte aligned, finite values
+ *   act_dev device, >= act_bytes of bitq_hgf_act_size, 256-byte aligned
+ *   ws_dev  device, >= ws_bytes of bitq_hgf_act_size, 256-byte aligned
+ * 1 <= M <= 64.
+ */
+bitq_status bitq_quantize_act_hgf(const bitq_wdesc* desc, const void* w_dev, const void* x_dev,
+                                  int32_t x_dtype, int32_t M, void* act_dev, size_t act_bytes,
+                                  void* ws_dev, size_t ws_bytes, void* stream);
+
+/*
  * Binary activation buffer (written by bitq_binarize_act, read by the SIGN1
  * XNOR path).  Kp = K rounded up to 128, Kw = Kp / 32.  Sections, each at a
  * multiple of 256 bytes:
@@ -297,7 +347,8 @@ bitq_status bitq_workspace_size(const bitq_wdesc* desc, int32_t M, size_t* bytes
  *   x_dev  SIGN1/RABIT: raw activations, BITQ_DT_F32 or BITQ_DT_BF16, 16-byte
  *          aligned.  TERNARY/W2A8/BVSR4/WNAM: an activation buffer from
  *          bitq_quantize_act (WNAM: bitq_quantize_act_bits with desc->abits)
- *          with M = 1 (x_dtype = BITQ_DT_ACT).  SIGN1 with x_dtype =
+ *          with M = 1 (x_dtype = BITQ_DT_ACT); HGF: the buffer of
+ *          bitq_quantize_act_hgf with M = 1.  SIGN1 with x_dtype =
  *          BITQ_DT_BINARY: a binary activation buffer from bitq_binarize_act
  *          with M = 1 (the XNOR path; no workspace needed, ws_dev may be
  *          NULL).
@@ -317,11 +368,14 @@ bitq_status bitq_workspace_size(const bitq_wdesc* desc, int32_t M, size_t* bytes
  *           P[n,g,j] = sum_{k in g} beta_j[n,k] q_k, (c, b) = cache[idx[n,g]]
  *   WNAM    as W2A8 with n-bit codes and m-bit q: the AND+popcount runs over
  *           n weight planes and m activation planes only
+ *   HGF     y_n = gamma d Y_n + gate sum_j h_j B[j][n] ([HGF] §4.1: the
+ *           ternary product and the correction in one kernel), Y_n as
+ *           TERNARY, the correction's up projection in fp32
  * Fully binary path (SIGN1, BITQ_DT_BINARY; [BitNet] §2.3 XNOR+popcount):
  *   y_n = alpha_n beta Y_n, Y_n = sum_k B[n,k] sign(x_k)
  *       = K - 2 popcount(bits(B_n) XOR bits(x)), exact
  * flags & BITQ_F_ACC_INT32 (integer formats): y_dev receives, as int32,
- *   TERNARY Y [N]; W2A8/WNAM A [N][K/128]; BVSR4 P [N][K/32][4]; SIGN1 with
+ *   TERNARY/HGF Y [N]; W2A8/WNAM A [N][K/128]; BVSR4 P [N][K/32][4]; SIGN1 with
  *   binary activations Y [N]; the buffer must hold that many int32 values.
  */
 bitq_status bitq_gemv(const bitq_wdesc* desc, const void* w_dev, const void* x_dev,
@@ -330,10 +384,10 @@ bitq_status bitq_gemv(const bitq_wdesc* desc, const void* w_dev, const void* x_d
 
 /*
  * Small-batch GEMM y[M][N] = x W^T for 2 <= M <= 64, integer formats
- * (TERNARY, W2A8, BVSR4, WNAM) and SIGN1 with binary activations, reading
- * every weight once for all M tokens.
+ * (TERNARY, W2A8, BVSR4, WNAM, HGF) and SIGN1 with binary activations,
+ * reading every weight once for all M tokens.
  *   act_dev activation buffer from bitq_quantize_act(_bits) with this M
- *           (SIGN1: from bitq_binarize_act).
+ *           (SIGN1: from bitq_binarize_act; HGF: from bitq_quantize_act_hgf).
  *   y_dev   fp32 [M][N].  BITQ_F_ACC_INT32 writes [M][...] int32 partials
  *           laid out as in bitq_gemv, one block per token.
  */

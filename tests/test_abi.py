@@ -45,7 +45,14 @@ def test_version_and_error_string():
     (bq.WDesc(bq.W2A8, 64, 96, 2, 128), bq.E_SHAPE),
     (bq.WDesc(bq.W2A8, 64, 128, 2, 64), bq.E_SHAPE),
     (bq.WDesc(bq.BVSR4, 64, 128, 3, 32), bq.E_SHAPE),
-    (bq.WDesc(7, 64, 128, 1, 0), bq.E_ARG),
+    (bq.WDesc(8, 64, 128, 1, 0), bq.E_ARG),
+    (bq.WDesc(bq.HGF, 64, 128, 2, 0, 8, 0), bq.E_SHAPE),        # rank 0
+    (bq.WDesc(bq.HGF, 64, 128, 2, 0, 8, 12), bq.E_SHAPE),       # rank not 8/16/32/64
+    (bq.WDesc(bq.HGF, 64, 128, 2, 0, 8, 128), bq.E_SHAPE),
+    (bq.WDesc(bq.HGF, 64, 16256, 2, 0, 8, 32), bq.E_SHAPE),     # K > 16128
+    (bq.WDesc(bq.HGF, 64, 128, 1, 0, 8, 32), bq.E_SHAPE),
+    (bq.WDesc(bq.HGF, 64, 128, 2, 0, 4, 32), bq.E_SHAPE),       # int8 activations only
+    (bq.WDesc(bq.TERNARY, 64, 128, 2, 0, 8, 32), bq.E_SHAPE),   # rank belongs to HGF
     (bq.WDesc(bq.WNAM, 64, 128, 0, 128, 4), bq.E_SHAPE),
     (bq.WDesc(bq.WNAM, 64, 128, 5, 128, 4), bq.E_SHAPE),
     (bq.WDesc(bq.WNAM, 64, 128, 3, 32, 4), bq.E_SHAPE),
@@ -78,6 +85,14 @@ def test_packed_size_formula():
         off_c0 = a(256 + planes)
         off_c1 = a(off_c0 + c0)
         assert bq.packed_size(d) == a(off_c1 + c1)
+    # HGF: gamma, A^T [r][Kp] and B^T [Np][r] in fp16
+    for N, K, r in [(4096, 4096, 32), (100, 96, 8), (2048, 512, 64)]:
+        d = bq.wdesc(bq.HGF, N, K, rank=r)
+        Np, Kp = (N + 63) // 64 * 64, (K + 127) // 128 * 128
+        off_c0 = a(256 + Np * Kp * 2 // 8)
+        off_c1 = a(off_c0 + 4)
+        off_c2 = a(off_c1 + 2 * r * Kp)
+        assert bq.packed_size(d) == a(off_c2 + 2 * Np * r)
 
 
 def test_pack_rejects_bad_codes_and_capacity():
@@ -189,3 +204,59 @@ def test_binary_activation_buffer_and_validation():
                              None) == bq.E_ALIGN
     assert bq._lib.bitq_gemm_smallM(ctypes.byref(ds), good, good, 1, good, None, 0, 0, None) == bq.E_SHAPE
     assert bq._lib.bitq_gemm_smallM(ctypes.byref(dr), good, good, 4, good, None, 0, 0, None) == bq.E_UNSUPPORTED
+
+
+def _hgf_logical(N, K, r, seed=0):
+    rng = np.random.default_rng(seed)
+    T = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    A = rng.normal(0, 0.02, size=(K, r)).astype(np.float16)
+    B = rng.normal(0, 0.02, size=(r, N)).astype(np.float16)
+    return T, A, B
+
+
+def test_hgf_pack_and_quantize_validation():
+    N, K, r = 8, 64, 8
+    d = bq.wdesc(bq.HGF, N, K, rank=r)
+    T, A, B = _hgf_logical(N, K, r)
+    bq.pack_weights(d, tern=T, gamma=0.5, lora_a=A, lora_b=B, lora_alpha=0.1)
+    bad = A.copy()
+    bad[3, 1] = np.float16(np.inf)
+    for kw in (dict(lora_a=bad, lora_b=B, lora_alpha=0.1),
+               dict(lora_a=A, lora_b=B, lora_alpha=float("nan")),
+               dict(lora_a=A, lora_alpha=0.1)):               # lora_b missing
+        with pytest.raises(bq.BitqError) as e:
+            bq.pack_weights(d, tern=T, gamma=0.5, **kw)
+        assert e.value.status == bq.E_ARG
+    with pytest.raises(bq.BitqError) as e:                    # A, B and alpha are trained inputs
+        bq.quantize_weights(d, np.zeros((N, K), np.float32))
+    assert e.value.status == bq.E_UNSUPPORTED
+
+
+def test_hgf_act_size_and_validation():
+    d = bq.wdesc(bq.HGF, 128, 256, rank=32)
+    for M in (1, 16, 64):
+        act, ws = bq.hgf_act_size(d, M)
+        lay = bq.act_layout(M, 256, 32)
+        assert act == lay["total"] and lay["off_h"] == bq.act_layout(M, 256)["total"]
+        assert ws == (8 * M * 32 + 255) // 256 * 256
+    with pytest.raises(bq.BitqError):
+        bq.hgf_act_size(bq.wdesc(bq.TERNARY, 128, 256), 1)
+    with pytest.raises(bq.BitqError):
+        bq.hgf_act_size(d, 65)
+    good = 1 << 20
+    act, ws = bq.hgf_act_size(d, 2)
+    f = bq._lib.bitq_quantize_act_hgf
+    dt = bq.wdesc(bq.TERNARY, 128, 256)
+    assert f(ctypes.byref(dt), good, good, bq.DT_BF16, 2, good, act, good, ws, None) == bq.E_ARG
+    assert f(ctypes.byref(d), None, good, bq.DT_BF16, 2, good, act, good, ws, None) == bq.E_ARG
+    assert f(ctypes.byref(d), good, good, bq.DT_BF16, 2, good, act, None, ws, None) == bq.E_ARG
+    assert f(ctypes.byref(d), good, good, bq.DT_ACT, 2, good, act, good, ws, None) == bq.E_ARG
+    assert f(ctypes.byref(d), good, good + 2, bq.DT_BF16, 2, good, act, good, ws, None) == bq.E_ALIGN
+    assert f(ctypes.byref(d), good + 16, good, bq.DT_BF16, 2, good, act, good, ws, None) == bq.E_ALIGN
+    assert f(ctypes.byref(d), good, good, bq.DT_BF16, 2, good, act, good + 8, ws, None) == bq.E_ALIGN
+    assert f(ctypes.byref(d), good, good, bq.DT_BF16, 2, good, act - 1, good, ws, None) == bq.E_CAPACITY
+    assert f(ctypes.byref(d), good, good, bq.DT_BF16, 2, good, act, good, ws - 1, None) == bq.E_CAPACITY
+    assert f(ctypes.byref(d), good, good, bq.DT_BF16, 0, good, act, good, ws, None) == bq.E_SHAPE
+    # the GEMV takes the HGF activation buffer; no workspace
+    assert bq.workspace_size(d, 1) == 0
+    assert bq._lib.bitq_gemv(ctypes.byref(d), good, good, bq.DT_BF16, good, None, 0, 0, None) == bq.E_ARG

@@ -29,6 +29,12 @@ def _need_gpu():
 # ======================================================= activation quantizer
 def _check_act(x_store, x_f32, M, K, abits=8):
     act, got = quantize_act_dev(x_store, M, K, abits)
+    _act_matches(got, x_f32, K, abits)
+    return act
+
+
+def _act_matches(got, x_f32, K, abits=8):
+    """The parsed activation sections equal the oracle's quantization."""
     q, d = oact.quantize(x_f32, abits)
     assert np.array_equal(got["q"][:, :K], q), "q"
     assert np.all(got["q"][:, K:] == 0), "q padding"
@@ -39,7 +45,6 @@ def _check_act(x_store, x_f32, M, K, abits=8):
     assert np.all(got["planes"][:, Kw_real:, :] == 0), "planes padding"
     assert np.array_equal(got["S"][:, :Kw_real], oact.group_sums(q, 32)), "S"
     assert np.all(got["S"][:, Kw_real:] == 0)
-    return act
 
 
 @pytest.mark.parametrize("M,K", [(1, 4096), (1, 224), (16, 512), (64, 11008), (3, 32)])
@@ -492,3 +497,136 @@ def test_single_element_tables_on_gpu(fmt, c):
         else:
             Y = run_gemv(desc, bd, act, bq.DT_ACT, M, bq.F_ACC_INT32, M * ncodes).reshape(M, ncodes)
             assert np.array_equal(Y, np.outer(v, np.arange(ncodes) - 1))
+
+
+# ====================================================================== HGF
+def _hgf_run(desc, blob, xs, M, K, ws=None):
+    """bitq_quantize_act_hgf then bitq_gemv/gemm_smallM: returns (act buffer
+    on the device, parsed act sections, h [M, r], workspace)."""
+    t = torch()
+    act_bytes, ws_bytes = bq.hgf_act_size(desc, M)
+    act = t.full((act_bytes,), 0x5A, dtype=t.uint8, device="cuda")     # poison
+    if ws is None:
+        ws = t.zeros(ws_bytes, dtype=t.uint8, device="cuda")
+    x = to_dev(xs)
+    dt = bq.DT_F32 if xs.dtype == np.float32 else bq.DT_BF16
+    bq.quantize_act_hgf(desc, blob, x, dt, M, act, ws)
+    t.cuda.synchronize()
+    buf = act.cpu().numpy()
+    L = bq.act_layout(M, K, desc.rank)
+    h = buf[L["off_h"]:L["off_h"] + 4 * M * desc.rank].view(np.float32).reshape(M, desc.rank)
+    return act, parse_act(buf, M, K), h.copy(), ws
+
+
+def _h_tol(xf, A):
+    """fp32 bound of the down projection: the run sums (rank terms), the
+    256/rank runs and the final rounding give at most 65 2^-24 sum|x A|, times
+    max |silu'| < 1.1; exp and the division add a few ulp of |h|."""
+    ref = og.lora_down(xf, A)
+    zabs = np.abs(np.asarray(xf, np.float64)) @ np.abs(np.asarray(A, np.float64))
+    return ref, 1e-5 * zabs + 1e-6 * np.abs(ref) + 1e-30
+
+
+def _hgf_case(N, K, M, r, W, xs, xf, A, B, alpha, rows=None, T=None):
+    q, d = oact.quantize(xf)
+    if T is None:
+        T, gamma = ow.quantize_ternary(W)
+    else:
+        gamma = np.float32(0.0125)
+    desc = bq.wdesc(bq.HGF, N, K, rank=r)
+    blob = bq.pack_weights(desc, tern=T, gamma=gamma, lora_a=A, lora_b=B, lora_alpha=alpha)
+    bd = dev_blob(blob)
+    act, pa, h, ws = _hgf_run(desc, bd, xs, M, K)
+    _act_matches(pa, xf, K)          # the int8 sections are bitq_quantize_act's, bit for bit
+    A64, B64 = A.astype(np.float64), B.astype(np.float64)
+    h_ref, h_tol = _h_tol(xf, A64)
+    assert_within(h, h_ref, h_tol, f"hgf h {N}x{K} r={r} M={M}")
+    assert not ws.cpu().numpy().any(), "workspace left non-zero"
+    r_ = np.arange(N) if rows is None else rows
+    Yi = run_gemv(desc, bd, act, bq.DT_ACT, M, bq.F_ACC_INT32, M * N).reshape(M, N)
+    assert np.array_equal(Yi[:, r_], og.ternary_int(T[r_], q)), "hgf Y_int"
+    y = run_gemv(desc, bd, act, bq.DT_ACT, M)
+    y_ref, tol = og.gemv_hgf(T[r_], gamma, q, d, xf, A64, B64[:, r_], np.float32(alpha))
+    assert_within(y[:, r_], y_ref, tol, f"hgf y {N}x{K} r={r} M={M}")
+    return desc, bd, act, y, h
+
+
+def _hgf_inputs(N, K, M, r, shape_idx=0, sigma_ab=0.02, seed=0, f32=False):
+    W = synth.gaussian_f32(np.random.default_rng(7 * N + K + seed), (N, K), 0.02)
+    if f32:
+        xf = synth.gaussian_f32(np.random.default_rng(M + seed), (M, K), 1.0)
+        xs = xf
+    else:
+        xs, xf = synth.random_bf16(np.random.default_rng(M + seed), (M, K))
+    Ab, Bb, alpha = synth.lora_params(shape_idx, N, K, r, sigma=sigma_ab, seed_offset=seed)
+    return W, xs, xf, Ab.view(np.float16), Bb.view(np.float16), alpha
+
+
+@pytest.mark.parametrize("N,K,M,r", [(70, 224, 1, 32), (130, 32, 1, 8), (200, 1056, 4, 16), (64, 4096, 1, 64),
+                                     (300, 416, 16, 32), (100, 16128, 1, 8), (520, 2048, 64, 64)])
+def test_hgf_gemv(N, K, M, r):
+    say("hgf", N, K, M, r)
+    W, xs, xf, A, B, alpha = _hgf_inputs(N, K, M, r)
+    _hgf_case(N, K, M, r, W, xs, xf, A, B, alpha)
+
+
+def test_hgf_f32_input_and_saturated_silu():
+    # A ~ N(0, 1): |z| reaches tens, so silu saturates on both sides
+    N, K, M, r = 130, 512, 2, 16
+    say("hgf f32 saturated", N, K, M, r)
+    W, xs, xf, A, B, alpha = _hgf_inputs(N, K, M, r, sigma_ab=1.0, f32=True)
+    _, _, _, _, h = _hgf_case(N, K, M, r, W, xs, xf, A, B, np.float32(-0.8))
+    assert (h < -1e-3).any() and (h > 20).any()
+
+
+def test_hgf_correction_alone_and_zero_b():
+    N, K, M, r = 200, 768, 3, 32
+    say("hgf isolated paths", N, K, M, r)
+    W, xs, xf, A, B, alpha = _hgf_inputs(N, K, M, r, sigma_ab=0.5)
+    # T = 0: y is the correction alone, checked with its own (tight) bound
+    T0 = np.zeros((N, K), np.int8)
+    _, _, _, y, _ = _hgf_case(N, K, M, r, W, xs, xf, A, B, np.float32(1.5), T=T0)
+    ref, tol = og.lora_correction(xf, A.astype(np.float64), B.astype(np.float64), np.float32(1.5))
+    assert_within(y, ref, tol, "correction alone")
+    assert np.abs(ref).max() > 1.0
+    # B = 0: the HGF output equals the TERNARY kernel's, bit for bit
+    Bz = np.zeros_like(B)
+    desc, bd, act, y0, _ = _hgf_case(N, K, M, r, W, xs, xf, A, Bz, alpha)
+    T, gamma = ow.quantize_ternary(W)
+    dt = bq.wdesc(bq.TERNARY, N, K)
+    bt = dev_blob(bq.pack_weights(dt, tern=T, gamma=gamma))
+    yt = run_gemv(dt, bt, act, bq.DT_ACT, M)       # the HGF buffer starts with the int8 sections
+    assert np.array_equal(y0.view(np.uint32), yt.view(np.uint32))
+
+
+def test_hgf_zero_token_deterministic_and_workspace_reuse():
+    N, K, M, r = 256, 1152, 4, 32
+    say("hgf determinism", N, K, M, r)
+    W, xs, xf, A, B, alpha = _hgf_inputs(N, K, M, r)
+    xs = xs.copy()
+    xf = xf.copy()
+    xs[2] = 0
+    xf[2] = 0.0                                      # an all-zero token: d = 0, h = 0, y = 0
+    desc, bd, act, y, h = _hgf_case(N, K, M, r, W, xs, xf, A, B, alpha)
+    assert np.all(h[2] == 0) and np.all(y[2] == 0)
+    _, _, h2, ws = _hgf_run(desc, bd, xs, M, K)
+    for _ in range(3):                               # the same workspace, reused without clearing
+        _, _, h3, ws = _hgf_run(desc, bd, xs, M, K, ws=ws)
+        assert np.array_equal(h3.view(np.uint32), h.view(np.uint32))
+    assert np.array_equal(h2.view(np.uint32), h.view(np.uint32))
+    # batch invariance: token m of the batch equals the M = 1 result
+    act1, _, h1, _ = _hgf_run(desc, bd, xs[1:2], 1, K)
+    assert np.array_equal(h1[0].view(np.uint32), h[1].view(np.uint32))
+    y1 = run_gemv(desc, bd, act1, bq.DT_ACT, 1)
+    assert np.array_equal(y1[0].view(np.uint32), y[1].view(np.uint32))
+
+
+@pytest.mark.parametrize("N,K,M,r", [(512, 512, 1, 32), (2048, 512, 1, 32), (512, 2048, 16, 32),
+                                     (4096, 4096, 1, 32), (4096, 4096, 16, 64), (11008, 4096, 1, 32)])
+def test_hgf_workload(N, K, M, r):
+    say("hgf workload", N, K, M, r)
+    si = {(512, 512): 0, (2048, 512): 1, (512, 2048): 2, (4096, 4096): 3}.get((N, K), 0)
+    W = synth.weights("ternary", si, N, K)
+    xs, xf = synth.activations("ternary", si, M, K)
+    Ab, Bb, alpha = synth.lora_params(si, N, K, r)
+    _hgf_case(N, K, M, r, W, xs, xf, Ab.view(np.float16), Bb.view(np.float16), alpha)

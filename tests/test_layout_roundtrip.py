@@ -169,3 +169,29 @@ def test_quantize_options_validation():
     assert call(d, ctypes.byref(bq.QuantOpts(-1))) == bq.E_ARG
     assert call(bq.wdesc(bq.SIGN1, 64, 128), ctypes.byref(bq.QuantOpts(2))) == bq.E_ARG
     assert call(d, ctypes.byref(bq.QuantOpts(2))) == bq.OK
+
+
+@pytest.mark.parametrize("N,K,r", [(64, 128, 32), (100, 96, 8), (130, 416, 64), (70, 256, 16)])
+def test_roundtrip_hgf(N, K, r):
+    W = _w(N, K)
+    T, gamma = ow.quantize_ternary(W)
+    rng = np.random.default_rng(N + K + r)
+    A = rng.normal(0, 0.02, size=(K, r)).astype(np.float16)
+    B = rng.normal(0, 0.02, size=(r, N)).astype(np.float16)
+    alpha = np.float32(-0.37)
+    d = bq.wdesc(bq.HGF, N, K, rank=r)
+    blob = bq.pack_weights(d, tern=T, gamma=gamma, lora_a=A, lora_b=B, lora_alpha=alpha)
+    u = layout.unpack(blob)
+    assert u["format"] == "hgf" and u["pad_ok"] and not u["both_set"]
+    np.testing.assert_array_equal(u["T"], T)
+    assert u["gamma"] == np.float32(gamma)
+    np.testing.assert_array_equal(u["A"].view(np.uint16), A.view(np.uint16))
+    np.testing.assert_array_equal(u["B"].view(np.uint16), B.view(np.uint16))
+    assert u["alpha"] == alpha and u["header"]["rank"] == r
+    # the packer's gate is tanh(alpha) in fp64 rounded to fp32; amax_a = max |A|
+    assert u["gate"] == np.float32(np.tanh(np.float64(alpha)))
+    assert u["amax_a"] == np.float32(np.abs(A.astype(np.float64)).max())
+    # the ternary sections are the TERNARY blob's
+    bt = bq.pack_weights(bq.wdesc(bq.TERNARY, N, K), tern=T, gamma=gamma)
+    h = u["header"]
+    np.testing.assert_array_equal(blob[256:h["off_c1"]], bt[256:h["off_c1"]])
