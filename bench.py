@@ -58,7 +58,11 @@ def kernels_sha() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 # Algorithmic packed bytes of one layer (planes + coefficients), by format.
-def packed_bytes(fmt: str, N: int, K: int, planes: int = 2) -> int:
+# HGF: the ternary planes and gamma, A (read by the activation step) and B
+# (read by the GEMV), r fp16 per input and per output.
+def packed_bytes(fmt: str, N: int, K: int, planes: int = 2, rank: int = 0) -> int:
+    if fmt == "hgf":
+        return 2 * N * K // 8 + 4 + 2 * rank * K + 2 * rank * N
     if fmt == "wnam":
         return planes * N * K // 8 + 4 * N * (K // 128)
     if fmt == "rabit":
@@ -87,7 +91,21 @@ WORKLOADS = {
     "w3a8": dict(fmt="wnam", planes=3, abits=8, data="w2a8", shape_idx=1, N=11008, K=4096),
     # fully binary XNOR+popcount: SIGN1 weights x sign activations (binarizer + GEMV per step)
     "xnor": dict(fmt="sign", binary=True, data="sign", shape_idx=0, N=11008, K=4096),
+    # HGF: ternary layer + rank-32 gated correction (activation step with the
+    # down projection, then the fused GEMV); the C3 4096 x 4096 layer, and the
+    # headline shape
+    "hgf": dict(fmt="hgf", data="ternary", shape_idx=3, N=4096, K=4096, rank=32),
+    "hgf_11008": dict(fmt="hgf", data="ternary", shape_idx=4, N=11008, K=4096, rank=32),
 }
+
+
+def kernel_bytes(wl: dict) -> int:
+    """Algorithmic bytes the GEMV kernel itself reads per launch (the HGF
+    down-projection matrix A is read by the activation step instead)."""
+    fmt, N, K = wl["fmt"], wl["N"], wl["K"]
+    if fmt == "hgf":
+        return 2 * N * K // 8 + 4 + 2 * wl["rank"] * N
+    return packed_bytes(fmt, N, K, wl.get("planes", 2))
 
 
 def log(*a):
@@ -133,6 +151,15 @@ def cpu_baseline(wl: dict, budget_s: float = 12.0) -> dict:
             q, d = oact.quantize(xf)
             return og.gemv_ternary(T, gamma, q, d)
         what = "oracle act quantize + gemv_ternary (fp64 dequant + dot)"
+    elif fmt == "hgf":
+        T, gamma = ow.quantize_ternary(W)
+        Ab, Bb, alpha = synth.lora_params(si, N, K, wl["rank"])
+        A = Ab.view(np.float16).astype(np.float64)
+        B = Bb.view(np.float16).astype(np.float64)
+        def run():
+            q, d = oact.quantize(xf)
+            return og.gemv_hgf(T, gamma, q, d, xf, A, B, alpha)
+        what = "oracle act quantize + gemv_hgf (fp64 ternary dequant + dot, fp64 correction)"
     elif fmt == "bvsr":
         # logical form from the library's quantizer (the oracle's exhaustive
         # search is far too slow at this size), read back by the oracle
@@ -158,7 +185,7 @@ def cpu_baseline(wl: dict, budget_s: float = 12.0) -> dict:
         if time.perf_counter() - t_all > budget_s or len(times) >= 50:
             break
     med = float(np.median(times))
-    return {"value": packed_bytes(fmt, N, K, wl.get("planes", 2)) / med / 1e9, "unit": "GB/s",
+    return {"value": packed_bytes(fmt, N, K, wl.get("planes", 2), wl.get("rank", 0)) / med / 1e9, "unit": "GB/s",
             "cores": int(threads),
             "kind": "oracle",
             "sample": f"{what}, {fmt} {N}x{K} M=1, {len(times)} runs, median {med * 1e3:.1f} ms "
@@ -192,11 +219,17 @@ def main():
     t0 = time.perf_counter()
     data = wl.get("data", fmt)
     W = synth.weights(data, si, N, K)
-    desc = bq.wdesc(fmt, N, K, planes=wl.get("planes"), abits=wl.get("abits"))
+    desc = bq.wdesc(fmt, N, K, planes=wl.get("planes"), abits=wl.get("abits"), rank=wl.get("rank"))
     abits = wl.get("abits", 8)
-    blob = bq.quantize_weights(desc, W)
+    hgf = fmt == "hgf"
+    if hgf:
+        Ab, Bb, alpha = synth.lora_params(si, N, K, wl["rank"])
+        blob = bq.quantize_weights_hgf(desc, W, Ab, Bb, alpha)
+    else:
+        blob = bq.quantize_weights(desc, W)
     log(f"quantized+packed {fmt} {N}x{K} in {time.perf_counter() - t0:.1f}s, blob {blob.nbytes} B")
-    alg_bytes = packed_bytes(fmt, N, K, wl.get("planes", 2))
+    alg_bytes = packed_bytes(fmt, N, K, wl.get("planes", 2), wl.get("rank", 0))
+    gemv_bytes = kernel_bytes(wl)
     copies = max(2, math.ceil(ROTATE_BYTES / blob.nbytes))
     base = torch.empty(blob.nbytes, dtype=torch.uint8, device=dev)
     base.copy_(torch.from_numpy(blob))
@@ -216,9 +249,13 @@ def main():
     y = torch.empty(N, dtype=torch.float32, device=dev)
     ws = torch.zeros(bq.workspace_size(desc, 1), dtype=torch.uint8, device=dev)
     binary = bool(wl.get("binary"))
-    integer = fmt in ("ternary", "w2a8", "bvsr", "wnam") or binary
+    integer = fmt in ("ternary", "w2a8", "bvsr", "wnam", "hgf") or binary
     if binary:
         act = torch.zeros(bq.binact_size(1, K), dtype=torch.uint8, device=dev)
+    elif hgf:
+        act_bytes, act_ws_bytes = bq.hgf_act_size(desc, 1)
+        act = torch.zeros(act_bytes, dtype=torch.uint8, device=dev)
+        act_ws = torch.zeros(act_ws_bytes, dtype=torch.uint8, device=dev)
     else:
         act = torch.zeros(bq.act_size(1, K), dtype=torch.uint8, device=dev) if integer else None
     act_dt = bq.DT_BINARY if binary else bq.DT_ACT
@@ -229,6 +266,9 @@ def main():
         if binary:
             bq.binarize_act(x, x_dt, 1, K, act, stream=stream)
             bq.gemv(desc, w, act, bq.DT_BINARY, y, None, stream=stream)
+        elif hgf:
+            bq.quantize_act_hgf(desc, w, x, x_dt, 1, act, act_ws, stream=stream)
+            bq.gemv(desc, w, act, bq.DT_ACT, y, None, stream=stream)
         elif integer:
             bq.quantize_act(x, x_dt, 1, K, act, stream=stream, abits=abits)
             bq.gemv(desc, w, act, bq.DT_ACT, y, ws, stream=stream)
@@ -294,7 +334,7 @@ def main():
         e1.record(torch.cuda.current_stream())
         torch.cuda.synchronize()
         gemv_ms = e0.elapsed_time(e1) / K_steps
-    achieved = alg_bytes / (gemv_ms * 1e-3) / 1e9
+    achieved = gemv_bytes / (gemv_ms * 1e-3) / 1e9
     traffic = None
     mt = MEASURED_TRAFFIC.get(args.workload)
     if mt is not None and mt["kernels_sha256_16"] == kernels_sha():
@@ -319,7 +359,8 @@ def main():
                    "N": N, "K": K, "M": 1, "format": fmt, "packed_bytes": alg_bytes,
                    "rotating_copies": copies, "rotating_bytes": copies * stride,
                    "graph_replay": graph is not None, "host_wall_s": round(wall, 4),
-                   **({"weight_bits": wl["planes"], "act_bits": abits} if fmt == "wnam" else {})},
+                   **({"weight_bits": wl["planes"], "act_bits": abits} if fmt == "wnam" else {}),
+                   **({"rank": wl["rank"], "gemv_kernel_bytes": gemv_bytes} if hgf else {})},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "traffic_bytes_per_launch": mt["bytes_per_launch"] if traffic is not None else None,

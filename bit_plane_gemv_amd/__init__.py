@@ -96,6 +96,7 @@ _sigs = {
     "bitq_quantize_weights": ([ctypes.POINTER(WDesc), _P, _P, _SZ, _I32], _I32),
     "bitq_quantize_weights_opts": ([ctypes.POINTER(WDesc), _P, ctypes.POINTER(QuantOpts), _P, _SZ, _I32],
                                    _I32),
+    "bitq_quantize_weights_hgf": ([ctypes.POINTER(WDesc), _P, _P, _P, ctypes.c_float, _P, _SZ, _I32], _I32),
     "bitq_act_size": ([_I32, _I32, ctypes.POINTER(_SZ)], _I32),
     "bitq_quantize_act": ([_P, _I32, _I32, _I32, _P, _SZ, _P], _I32),
     "bitq_quantize_act_bits": ([_P, _I32, _I32, _I32, _I32, _P, _SZ, _P], _I32),
@@ -203,6 +204,25 @@ def quantize_weights(desc: WDesc, W: np.ndarray, nthreads: int = 0, svid_sweeps:
     else:
         _check(_lib.bitq_quantize_weights(ctypes.byref(desc), W.ctypes.data, blob.ctypes.data,
                                           blob.nbytes, nthreads))
+    return blob
+
+
+def quantize_weights_hgf(desc: WDesc, W: np.ndarray, lora_a, lora_b, lora_alpha: float,
+                         nthreads: int = 0) -> np.ndarray:
+    """fp32 W [N, K] -> HGF blob: the library's ternary quantizer for W plus
+    the correction parameters A [K, r], B [r, N] (fp16 arrays or their bits)."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    if W.shape != (desc.N, desc.K):
+        raise ValueError(f"W has shape {W.shape}, descriptor says {(desc.N, desc.K)}")
+    a = np.ascontiguousarray(np.asarray(lora_a).view(np.uint16) if np.asarray(lora_a).dtype == np.float16
+                             else lora_a, dtype=np.uint16)
+    b = np.ascontiguousarray(np.asarray(lora_b).view(np.uint16) if np.asarray(lora_b).dtype == np.float16
+                             else lora_b, dtype=np.uint16)
+    if desc.fmt == HGF and (a.shape != (desc.K, desc.rank) or b.shape != (desc.rank, desc.N)):
+        raise ValueError("lora_a must be [K, rank] and lora_b [rank, N]")
+    blob = np.zeros(packed_size(desc), dtype=np.uint8)
+    _check(_lib.bitq_quantize_weights_hgf(ctypes.byref(desc), W.ctypes.data, a.ctypes.data, b.ctypes.data,
+                                          float(lora_alpha), blob.ctypes.data, blob.nbytes, nthreads))
     return blob
 
 

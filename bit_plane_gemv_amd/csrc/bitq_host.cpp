@@ -374,6 +374,22 @@ bitq_status pack_impl(const bitq_wdesc& d, const bitq_logical* s, void* dstv, si
 }
 
 // -------------------------------------------------------------- quantizers
+// [HGF] §1.2 ternary quantizer: gamma = mean |W| (fp64 sum, stored fp32),
+// T = clamp(rint(W / gamma), -1, 1) with the division in fp32.
+float quantize_ternary(const float* W, int64_t count, std::vector<int8_t>& T) {
+    double sabs = 0.0;
+    for (int64_t i = 0; i < count; ++i) sabs += std::fabs(static_cast<double>(W[i]));
+    const float gamma = static_cast<float>(sabs / static_cast<double>(count));
+    T.assign(count, 0);
+    if (gamma > 0.0f) {
+        for (int64_t i = 0; i < count; ++i) {
+            float r = std::nearbyint(W[i] / gamma);  // fp32 division, then RNE
+            T[i] = static_cast<int8_t>(std::min(1.0f, std::max(-1.0f, r)));
+        }
+    }
+    return gamma;
+}
+
 // [BitNet] §2.1: sign(x) = +1 if x >= 0 else -1.
 inline int8_t sign_pm1(double v) { return v >= 0 ? 1 : -1; }
 
@@ -862,21 +878,10 @@ bitq_status bitq_quantize_weights_opts(const bitq_wdesc* desc, const float* W, c
                 lg.g = g.data();
                 lg.h = h.data();
                 break;
-            case BITQ_TERNARY: {
-                double sabs = 0.0;
-                for (int64_t i = 0; i < N * K; ++i) sabs += std::fabs(static_cast<double>(W[i]));
-                float gamma = static_cast<float>(sabs / static_cast<double>(N * K));
-                i8.assign(N * K, 0);
-                if (gamma > 0.0f) {
-                    for (int64_t i = 0; i < N * K; ++i) {
-                        float r = std::nearbyint(W[i] / gamma);  // fp32 division, then RNE
-                        i8[i] = static_cast<int8_t>(std::min(1.0f, std::max(-1.0f, r)));
-                    }
-                }
+            case BITQ_TERNARY:
+                lg.gamma = quantize_ternary(W, N * K, i8);
                 lg.tern = i8.data();
-                lg.gamma = gamma;
                 break;
-            }
             case BITQ_W2A8:
             case BITQ_WNAM:
                 quantize_w2a8(d, W, u8, delta, zero, nthreads);
@@ -896,6 +901,35 @@ bitq_status bitq_quantize_weights_opts(const bitq_wdesc* desc, const float* W, c
                 lg.cache = cache.data();
                 break;
         }
+        return pack_impl(d, &lg, dst, dst_bytes, nthreads);
+    } catch (...) {
+        return fail(BITQ_E_ARG, "host allocation failed while quantizing");
+    }
+}
+
+bitq_status bitq_quantize_weights_hgf(const bitq_wdesc* desc, const float* W, const uint16_t* lora_a,
+                                      const uint16_t* lora_b, float lora_alpha, void* dst, size_t dst_bytes,
+                                      int32_t nthreads) {
+    bitq_status s = check_desc(desc);
+    if (s) return s;
+    if (desc->fmt != BITQ_HGF) return fail(BITQ_E_ARG, "bitq_quantize_weights_hgf needs an HGF descriptor");
+    if (!W) return fail(BITQ_E_ARG, "W is NULL");
+    if (!dst) return fail(BITQ_E_ARG, "dst is NULL");
+    const bitq_wdesc d = *desc;
+    size_t need = blob_layout(d).total;
+    if (dst_bytes < need) return fail(BITQ_E_CAPACITY, "dst has %zu bytes, blob needs %zu", dst_bytes, need);
+    const int64_t N = d.N, K = d.K;
+    for (int64_t i = 0; i < N * K; ++i)
+        if (!std::isfinite(W[i])) return fail(BITQ_E_ARG, "W[%lld] is not finite", (long long)i);
+    try {
+        std::vector<int8_t> T;
+        bitq_logical lg{};
+        lg.gamma = quantize_ternary(W, N * K, T);
+        lg.tern = T.data();
+        lg.lora_a = lora_a;
+        lg.lora_b = lora_b;
+        lg.lora_alpha = lora_alpha;
+        if ((s = check_logical(d, &lg))) return s;
         return pack_impl(d, &lg, dst, dst_bytes, nthreads);
     } catch (...) {
         return fail(BITQ_E_ARG, "host allocation failed while quantizing");

@@ -38,6 +38,15 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<unsigned short>(h & 0xFFFFu)));
 }
 
+// 16-byte load of element i of a global array given by its address as an
+// integer (so the load carries no restrict/invariant provenance and stays in
+// program order around memory clobbers), as a global (not flat) access.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 global_load16(uintptr_t base, int i) {
+    const u32x4_t v = ((const __attribute__((address_space(1))) u32x4_t*)base)[i];
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -158,14 +167,13 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const void* __restrict__
     if constexpr (RANK > 0) {
         __shared__ float s_part[256];
         const int c = tid / RANK, j = tid % RANK;
-        const int k0 = lo + RANK * c;  // this thread's run; inputs past K count as 0
+        const int k0 = lo + RANK * c;       // this thread's run; inputs past K count as 0
         const int kc = min(k0, Kp - RANK);  // in-bounds row position (runs past Kp have x = 0)
-        const uint16_t* at = reinterpret_cast<const uint16_t*>(blob + off_at);  // A^T [RANK][Kp]
-        const float amax_a = *reinterpret_cast<const float*>(blob + kHdrAmaxA);
-        const uint4* arow = reinterpret_cast<const uint4*>(at + static_cast<size_t>(j) * Kp + kc);
+        const uint4* arow = reinterpret_cast<const uint4*>(blob + off_at) + (static_cast<size_t>(j) * Kp + kc) / 8;
         uint4 av[RANK / 8];
 #pragma unroll
         for (int i = 0; i < RANK / 8; ++i) av[i] = arow[i];
+        const float amax_a = *reinterpret_cast<const float*>(blob + kHdrAmaxA);
         float part = 0.0f;
 #pragma unroll
         for (int i = 0; i < RANK / 8; ++i) {
@@ -285,15 +293,6 @@ __device__ __forceinline__ void split_k_add(unsigned long long* word, float part
     const long long total = static_cast<long long>(prev + add - (static_cast<unsigned long long>(splits) << 58));
     *y_n = finite ? static_cast<float>(ldexp(static_cast<double>(total), -S)) : __builtin_nanf("");
     __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// 16-byte load of element i of a global array given by its address as an
-// integer (so the load carries no restrict/invariant provenance and stays in
-// program order around memory clobbers), as a global (not flat) access.
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 global_load16(uintptr_t base, int i) {
-    const u32x4_t v = ((const __attribute__((address_space(1))) u32x4_t*)base)[i];
-    return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 template <int DT>

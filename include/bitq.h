@@ -219,6 +219,17 @@ bitq_status bitq_pack_weights(const bitq_wdesc* desc, const bitq_logical* src,
 bitq_status bitq_quantize_weights(const bitq_wdesc* desc, const float* W, void* dst,
                                   size_t dst_bytes, int32_t nthreads);
 
+/*
+ * HGF host quantizer + packer: the TERNARY quantizer of bitq_quantize_weights
+ * for the backbone W (fp32 [N][K], host), together with the trained
+ * correction parameters ([HGF] §2.1) lora_a [K][r] and lora_b [r][N] (fp16
+ * bit patterns, finite, host) and the gate parameter lora_alpha (finite).
+ * desc must be an HGF descriptor.
+ */
+bitq_status bitq_quantize_weights_hgf(const bitq_wdesc* desc, const float* W, const uint16_t* lora_a,
+                                      const uint16_t* lora_b, float lora_alpha, void* dst,
+                                      size_t dst_bytes, int32_t nthreads);
+
 /* Options of the offline quantizer (zero-initialize; reserved must stay 0). */
 typedef struct {
     int32_t rabit_svid_sweeps;  /* RABIT: Gauss-Seidel sweeps of [RaBiT] §2.2's

@@ -195,3 +195,21 @@ def test_roundtrip_hgf(N, K, r):
     bt = bq.pack_weights(bq.wdesc(bq.TERNARY, N, K), tern=T, gamma=gamma)
     h = u["header"]
     np.testing.assert_array_equal(blob[256:h["off_c1"]], bt[256:h["off_c1"]])
+
+
+def test_library_hgf_quantizer_matches_oracle():
+    N, K, r = 130, 384, 16
+    W = _w(N, K)
+    Ab, Bb, alpha = synth.lora_params(0, N, K, r)
+    d = bq.wdesc(bq.HGF, N, K, rank=r)
+    blob = bq.quantize_weights_hgf(d, W, Ab, Bb, alpha)
+    T, gamma = ow.quantize_ternary(W)
+    ref = bq.pack_weights(d, tern=T, gamma=gamma, lora_a=Ab, lora_b=Bb, lora_alpha=alpha)
+    assert np.array_equal(blob, ref)
+    with pytest.raises(bq.BitqError):
+        bq.quantize_weights_hgf(bq.wdesc(bq.TERNARY, N, K), W, Ab, Bb, alpha)
+    bad = Ab.copy()
+    bad[0, 0] = 0x7E00                      # NaN
+    with pytest.raises(bq.BitqError) as e:
+        bq.quantize_weights_hgf(d, W, bad, Bb, alpha)
+    assert e.value.status == bq.E_ARG
