@@ -769,6 +769,10 @@ Plan make_plan(const bitq_wdesc& d, int M) {
         p.splits = 1;
         p.off_partials = p.off_counters = 0;
         p.ws_bytes = 0;
+        // the contraction is compute-bound on the VALU from 2 tokens on; from
+        // kMfmaMinM tokens the int8 matrix-core kernel is faster and takes
+        // over (HGF and BVSR4 stay on the VALU)
+        p.mfma = M >= kMfmaMinM && (d.fmt == BITQ_TERNARY || d.fmt == BITQ_W2A8 || d.fmt == BITQ_WNAM);
         return p;
     }
     p.waves_per_wg = lut ? 4 : 1;

@@ -59,8 +59,10 @@ struct Plan {
     size_t off_partials;   // float formats: u64 [Np] split-k words (count + fixed-point sum)
     size_t off_counters;   // unused (0)
     size_t ws_bytes;
+    bool mfma;             // integer formats, M >= kMfmaMinM: the int8 matrix-core kernel
 };
 Plan make_plan(const bitq_wdesc& d, int M);
+constexpr int kMfmaMinM = 4;  // tokens from which TERNARY/W2A8/WNAM use the matrix cores
 
 // Kernel launchers (bitq_kernels.hip).  Arguments are already validated.
 // Each returns hipSuccess or the HIP error code of the launch.

@@ -339,11 +339,24 @@ def test_w2a8_batch_invariance_and_determinism():
     y16a = run_gemv(desc, bd, act16, bq.DT_ACT, 16, ws=ws)
     y16b = run_gemv(desc, bd, act16, bq.DT_ACT, 16, ws=ws)
     assert np.array_equal(y16a.view(np.uint32), y16b.view(np.uint32)), "run-to-run"
-    ws1 = workspace(desc, 1)
+    # M >= 2 runs on the matrix cores: a token gets the same bits whatever the
+    # batch and its place in it (M = 1 runs the VALU kernel: its integer
+    # partials are the same, y agrees within the tolerance)
     for m in (0, 9, 15):
+        sub = np.ascontiguousarray(xs[[(m + 5) % 16, m]])
+        act2, _ = quantize_act_dev(sub, 2, K)
+        y2 = run_gemv(desc, bd, act2, bq.DT_ACT, 2, ws=ws)
+        assert np.array_equal(y2[1].view(np.uint32), y16a[m].view(np.uint32)), f"token {m}"
+    act40, _ = quantize_act_dev(np.ascontiguousarray(np.concatenate([xs, xs, xs[:8]])), 40, K)
+    y40 = run_gemv(desc, bd, act40, bq.DT_ACT, 40, ws=ws)
+    assert np.array_equal(y40[16:32].view(np.uint32), y16a.view(np.uint32))
+    G = K // 128
+    A16 = run_gemv(desc, bd, act16, bq.DT_ACT, 16, bq.F_ACC_INT32, 16 * N * G).reshape(16, N, G)
+    ws1 = workspace(desc, 1)
+    for m in (0, 15):
         act1, _ = quantize_act_dev(xs[m:m + 1], 1, K)
-        y1 = run_gemv(desc, bd, act1, bq.DT_ACT, 1, ws=ws1)
-        assert np.array_equal(y1[0].view(np.uint32), y16a[m].view(np.uint32)), f"token {m}"
+        A1 = run_gemv(desc, bd, act1, bq.DT_ACT, 1, bq.F_ACC_INT32, N * G).reshape(N, G)
+        assert np.array_equal(A1, A16[m]), f"token {m} partials"
 
 
 # ===================================================================== WnAm
@@ -630,3 +643,59 @@ def test_hgf_workload(N, K, M, r):
     xs, xf = synth.activations("ternary", si, M, K)
     Ab, Bb, alpha = synth.lora_params(si, N, K, r)
     _hgf_case(N, K, M, r, W, xs, xf, Ab.view(np.float16), Bb.view(np.float16), alpha)
+
+
+# ====================================== int8 matrix-core small-M kernel (M >= 2)
+@pytest.mark.parametrize("M", [2, 17, 33, 50])
+@pytest.mark.parametrize("fmt,N,K", [(bq.TERNARY, 70, 224), (bq.TERNARY, 200, 1056), (bq.W2A8, 130, 1152),
+                                     (bq.W2A8, 64, 128)])
+def test_mfma_ragged(fmt, N, K, M):
+    say("mfma ragged", fmt, N, K, M)
+    W = synth.gaussian_f32(np.random.default_rng(N * K + M), (N, K), 0.02)
+    xs, xf = synth.random_bf16(np.random.default_rng(M + 3), (M, K))
+    _int_case(fmt, N, K, M, W, xs, xf)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4])
+@pytest.mark.parametrize("m,M", [(4, 5), (8, 64), (3, 2)])
+def test_mfma_wnam(n, m, M):
+    N, K = 190, 640
+    say("mfma wnam", n, m, M)
+    W = synth.gaussian_f32(np.random.default_rng(n * 10 + m), (N, K), 0.02)
+    xs, xf = synth.random_bf16(np.random.default_rng(M + n), (M, K))
+    _wnam_case(N, K, M, n, m, W, xs, xf)
+
+
+def test_mfma_extreme_codes_and_activations():
+    # all weight codes at the extremes of their range against +-127 (and the
+    # most negative sums): the int32 group sums must still be exact
+    N, K, M = 64, 512, 20
+    say("mfma extremes", N, K, M)
+    rng = np.random.default_rng(99)
+    for fmt in (bq.W2A8, bq.TERNARY):
+        x = np.where(rng.random((M, K)) < 0.5, 127.0, -127.0).astype(np.float32)
+        x[:, 0] = 127.0
+        x[3] = -127.0
+        x[3, 0] = 127.0
+        if fmt == bq.W2A8:
+            code = np.full((N, K), 3, np.uint8)
+            code[::2] = 0
+            desc = bq.wdesc(fmt, N, K)
+            blob = bq.pack_weights(desc, code=code, delta=np.ones((N, K // 128), np.float16),
+                                   zero=np.zeros((N, K // 128), np.float16))
+        else:
+            code = np.where(rng.random((N, K)) < 0.5, 1, -1).astype(np.int8)
+            code[5] = -1
+            desc = bq.wdesc(fmt, N, K)
+            blob = bq.pack_weights(desc, tern=code, gamma=1.0)
+        bd = dev_blob(blob)
+        act, got = quantize_act_dev(x, M, K)
+        q = got["q"][:, :K].astype(np.int64)
+        if fmt == bq.W2A8:
+            G = K // 128
+            A = run_gemv(desc, bd, act, bq.DT_ACT, M, bq.F_ACC_INT32, M * N * G).reshape(M, N, G)
+            ref = np.einsum("nk,mk->mnk", code.astype(np.int64), q).reshape(M, N, G, 128).sum(-1)
+        else:
+            A = run_gemv(desc, bd, act, bq.DT_ACT, M, bq.F_ACC_INT32, M * N).reshape(M, N)
+            ref = q @ code.astype(np.int64).T
+        assert np.array_equal(A, ref), fmt
