@@ -6,7 +6,11 @@
 A step is one batch-1 GEMV y = W^ x over one Llama-2-7B gate/up layer
 (11008 x 4096): the RaBiT 2-path residual-binary layer by default (the
 workload the headline metric is quoted on), or the W2A8 bit-plane layer
-(activation quantizer + AND+popcount GEMV) with --workload w2a8.
+(activation quantizer + AND+popcount GEMV) with --workload w2a8; the other
+workloads are listed in WORKLOADS.  --tokens M (integer formats, 2..64) runs
+the small-M path instead: M tokens per step, each weight read once, and the
+roofline is then the contraction's (int8 matrix cores from 4 tokens on,
+else VALU lane-operations).
 
 Measurement:
   * The packed layer is replicated into >= 1 GiB of distinct device copies and
@@ -38,6 +42,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+INT8_MFMA_PEAK_TOPS = 5000.0      # MI355X dense int8 matrix-core peak
+# VALU lane-operations per second: 256 CUs x 4 SIMDs x 16 lanes per clock x
+# 2.4 GHz (one 64-lane instruction every 4 clocks per SIMD)
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+MFMA_MIN_TOKENS = 4               # the library's switch to the matrix-core kernel
 ROTATE_BYTES = 1 << 30
 KERNEL_SRC = os.path.join(ROOT, "bit_plane_gemv_amd", "csrc", "bitq_kernels.hip")
 
@@ -200,6 +209,8 @@ def main():
     ap.add_argument("--workload", default="rabit", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch every step from the host")
+    ap.add_argument("--tokens", type=int, default=1,
+                    help="tokens per step (integer formats: 2..64 run the small-M path)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -212,6 +223,10 @@ def main():
 
     wl = WORKLOADS[args.workload]
     fmt, N, K, si = wl["fmt"], wl["N"], wl["K"], wl["shape_idx"]
+    M = args.tokens
+    if M != 1 and (fmt in ("rabit",) or (fmt == "sign" and not wl.get("binary")) or not 1 <= M <= 64):
+        print("--tokens > 1 needs an integer-activation workload and at most 64 tokens", file=sys.stderr)
+        sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -241,37 +256,44 @@ def main():
     blobs = [pool[c * stride:c * stride + blob.nbytes] for c in range(copies)]
 
     # ---- activations / outputs / workspace
-    xs, xf = synth.activations(data, si, 1, K)
+    xs, xf = synth.activations(data, si, M, K)
     if xs.dtype == np.float32:      # fp32 activations (the sign workloads' inputs)
         x, x_dt = torch.from_numpy(np.ascontiguousarray(xs)).to(dev), bq.DT_F32
     else:                           # bf16 bit patterns
         x, x_dt = torch.from_numpy(np.ascontiguousarray(xs).view(np.int16)).to(dev), bq.DT_BF16
-    y = torch.empty(N, dtype=torch.float32, device=dev)
-    ws = torch.zeros(bq.workspace_size(desc, 1), dtype=torch.uint8, device=dev)
+    y = torch.empty(M * N, dtype=torch.float32, device=dev)
+    ws = torch.zeros(bq.workspace_size(desc, M), dtype=torch.uint8, device=dev)
     binary = bool(wl.get("binary"))
     integer = fmt in ("ternary", "w2a8", "bvsr", "wnam", "hgf") or binary
     if binary:
-        act = torch.zeros(bq.binact_size(1, K), dtype=torch.uint8, device=dev)
+        act = torch.zeros(bq.binact_size(M, K), dtype=torch.uint8, device=dev)
     elif hgf:
-        act_bytes, act_ws_bytes = bq.hgf_act_size(desc, 1)
+        act_bytes, act_ws_bytes = bq.hgf_act_size(desc, M)
         act = torch.zeros(act_bytes, dtype=torch.uint8, device=dev)
         act_ws = torch.zeros(act_ws_bytes, dtype=torch.uint8, device=dev)
     else:
-        act = torch.zeros(bq.act_size(1, K), dtype=torch.uint8, device=dev) if integer else None
+        act = torch.zeros(bq.act_size(M, K), dtype=torch.uint8, device=dev) if integer else None
     act_dt = bq.DT_BINARY if binary else bq.DT_ACT
     stream = torch.cuda.current_stream()
+
+    def product(w, a, a_dt, ws_, st):
+        """The GEMV (one token) or the small-M GEMM (M tokens)."""
+        if M == 1:
+            bq.gemv(desc, w, a, a_dt, y, ws_, stream=st)
+        else:
+            bq.gemm_smallM(desc, w, a, M, y, ws_, stream=st)
 
     def step(i):
         w = blobs[i % copies]
         if binary:
-            bq.binarize_act(x, x_dt, 1, K, act, stream=stream)
-            bq.gemv(desc, w, act, bq.DT_BINARY, y, None, stream=stream)
+            bq.binarize_act(x, x_dt, M, K, act, stream=stream)
+            product(w, act, bq.DT_BINARY, None, stream)
         elif hgf:
-            bq.quantize_act_hgf(desc, w, x, x_dt, 1, act, act_ws, stream=stream)
-            bq.gemv(desc, w, act, bq.DT_ACT, y, None, stream=stream)
+            bq.quantize_act_hgf(desc, w, x, x_dt, M, act, act_ws, stream=stream)
+            product(w, act, bq.DT_ACT, None, stream)
         elif integer:
-            bq.quantize_act(x, x_dt, 1, K, act, stream=stream, abits=abits)
-            bq.gemv(desc, w, act, bq.DT_ACT, y, ws, stream=stream)
+            bq.quantize_act(x, x_dt, M, K, act, stream=stream, abits=abits)
+            product(w, act, bq.DT_ACT, ws, stream)
         else:
             bq.gemv(desc, w, x, x_dt, y, ws, stream=stream)
 
@@ -323,7 +345,7 @@ def main():
             with torch.cuda.graph(g2, stream=s2):
                 st2 = torch.cuda.current_stream()
                 for i in range(K_steps):
-                    bq.gemv(desc, blobs[i % copies], act, act_dt, y, None if binary else ws, stream=st2)
+                    product(blobs[i % copies], act, act_dt, None if binary else ws, st2)
         torch.cuda.current_stream().wait_stream(s2)
         g2.replay()
         torch.cuda.synchronize()
@@ -335,8 +357,28 @@ def main():
         torch.cuda.synchronize()
         gemv_ms = e0.elapsed_time(e1) / K_steps
     achieved = gemv_bytes / (gemv_ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    mfma = M >= MFMA_MIN_TOKENS and fmt in ("ternary", "w2a8", "wnam")
+    if M > 1:
+        # the small-M contraction: int8 ops (2 M N K) on the matrix cores, or,
+        # on the VALU, the AND and popcount lane-operations of the bit planes
+        # (2 per weight plane x activation plane x 32 weights x token)
+        if mfma:
+            tops = 2.0 * M * N * K / (gemv_ms * 1e-3) / 1e12
+            roof = {"bound": "mfma", "achieved": round(tops, 2), "peak": INT8_MFMA_PEAK_TOPS, "unit": "TOP/s",
+                    "frac": round(tops / INT8_MFMA_PEAK_TOPS, 4)}
+        else:
+            wplanes = {"ternary": 2, "w2a8": 2, "bvsr": 4, "hgf": 2}.get(fmt, wl.get("planes", 1))
+            aplanes = 1 if binary else abits
+            ops = M * N * K * wplanes * aplanes * 2 / 32
+            tops = ops / (gemv_ms * 1e-3) / 1e12
+            roof = {"bound": "alu", "achieved": round(tops, 2), "peak": round(VALU_PEAK_TOPS, 2),
+                    "unit": "Tlane-op/s", "frac": round(tops / VALU_PEAK_TOPS, 4)}
+        roof["hbm_gbs"] = round(achieved, 2)
+        roof["hbm_frac"] = round(achieved / HBM_PEAK_GBS, 4)
     traffic = None
-    mt = MEASURED_TRAFFIC.get(args.workload)
+    mt = MEASURED_TRAFFIC.get(args.workload) if M == 1 else None
     if mt is not None and mt["kernels_sha256_16"] == kernels_sha():
         traffic = round(mt["bytes_per_launch"] / (gemv_ms * 1e-3) / 1e9, 2)
 
@@ -355,21 +397,21 @@ def main():
         "vs_baseline": None,
         "dtype": "f32" if fmt == "rabit" or (fmt == "sign" and not binary) else "int32",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload} {N}x{K} M=1 ({'RaBiT 2-path residual binary, bf16 x' if fmt == 'rabit' else fmt})",
-                   "N": N, "K": K, "M": 1, "format": fmt, "packed_bytes": alg_bytes,
+        "config": {"workload": f"{args.workload} {N}x{K} M={M} ({'RaBiT 2-path residual binary, bf16 x' if fmt == 'rabit' else fmt})",
+                   "N": N, "K": K, "M": M, "format": fmt, "packed_bytes": alg_bytes,
                    "rotating_copies": copies, "rotating_bytes": copies * stride,
                    "graph_replay": graph is not None, "host_wall_s": round(wall, 4),
                    **({"weight_bits": wl["planes"], "act_bits": abits} if fmt == "wnam" else {}),
                    **({"rank": wl["rank"], "gemv_kernel_bytes": gemv_bytes} if hgf else {})},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+        "roofline": {**roof, "traffic": traffic,
                      "traffic_bytes_per_launch": mt["bytes_per_launch"] if traffic is not None else None,
                      "kernel": ("gemv_xnor_kernel" if binary else
-                                "gemv_sign_kernel" if fmt in ("rabit", "sign") else "gemv_bits_nr_kernel"),
+                                "gemv_sign_kernel" if fmt in ("rabit", "sign") else
+                                "gemm_mfma_kernel" if mfma else "gemv_bits_nr_kernel"),
                      "kernel_us": round(gemv_ms * 1e3, 3)},
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and M == 1:
         try:
             out["cpu_baseline"] = cpu_baseline(wl)
         except Exception as e:  # reported, never fatal for the GPU figure
