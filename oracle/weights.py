@@ -219,6 +219,39 @@ BVSR_NR = 16          # ratios r_i = 1.6 + 0.8 i / 15
 BVSR_NL = 16          # spans L_j = ((j + 1/2)/16)-quantile of group ranges
 
 
+
+def quantize_bit_balance(W: np.ndarray, group: int = 128):
+    """[ABQ] §3.3 bit balance: the 2-bit integer grid, whose four values
+    ({-2,-1,0,1} or {-1,0,1,2}) break the symmetry of the weight
+    distribution, is widened to the symmetric five values {-2,-1,0,1,2}.
+    Per group of `group` inputs, with a symmetric round-to-nearest step:
+
+        delta = fl16(max |W| / 2)
+        t     = clamp(rint(W / delta), -2, 2)
+        code  = t + 2                 (0..4, stored on three bit planes)
+        z     = 2                     (so W^ = delta * (code - z) = delta * t)
+
+    A group whose step is zero gets delta = 1 and code 2 (W^ = 0).
+    Arithmetic in fp64 from the fp32 weights and the fp16 step.  Returns
+    (code uint8 [N, K], delta fp16 [N, G], zero fp16 [N, G]) in the WnAm
+    logical form with n = 3.
+    """
+    W = np.asarray(W, dtype=np.float32)
+    N, K = W.shape
+    assert K % group == 0
+    G = K // group
+    Wg = W.reshape(N, G, group).astype(np.float64)
+    amax = np.abs(Wg).max(axis=-1)
+    step16 = to_f16(amax / 2.0)
+    step = step16.astype(np.float64)
+    flat = step == 0.0
+    div = np.where(flat, 1.0, step)
+    t = np.clip(np.rint(Wg / div[..., None]), -2, 2)
+    t = np.where(flat[..., None], 0.0, t)
+    step16 = np.where(flat, np.float16(1.0), step16).astype(np.float16)
+    zero = np.full((N, G), 2.0, dtype=np.float16)
+    return (t + 2).reshape(N, K).astype(np.uint8), step16, zero
+
 def quantile_linear(sorted_vals: np.ndarray, qf: float) -> float:
     """Linear-interpolation quantile of sorted data, written out so that the
     arithmetic order is fixed: pos = q (n-1); i = floor(pos);

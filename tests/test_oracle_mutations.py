@@ -152,3 +152,32 @@ def test_mutation_hgf_quantized_input(monkeypatch):
     monkeypatch.setattr(og, "gemv_hgf", wrong)
     with pytest.raises(AssertionError):
         th.test_gemv_hgf_hand_case()
+
+
+def test_mutation_bit_balance_asymmetric_grid(monkeypatch):
+    # the four-level INT2 grid {-2,-1,0,1} in place of the balanced five levels
+    import test_oracle_bitbalance as tbb
+    orig = ow.quantize_bit_balance
+
+    def four_level(W, group=128):
+        c, d, z = orig(W, group)
+        return np.minimum(c, 3).astype(np.uint8), d, z
+    monkeypatch.setattr(ow, "quantize_bit_balance", four_level)
+    with pytest.raises(AssertionError):
+        tbb.test_mirror_symmetry()
+
+
+def test_mutation_bit_balance_step_from_range(monkeypatch):
+    # the asymmetric (hi - lo) / 4 step instead of max|W| / 2
+    import test_oracle_bitbalance as tbb
+
+    def range_step(W, group=128):
+        W = np.asarray(W, np.float32)
+        N, K = W.shape
+        Wg = W.reshape(N, K // group, group).astype(np.float64)
+        d16 = common.to_f16((Wg.max(-1) - Wg.min(-1)) / 4.0)
+        t = np.clip(np.rint(Wg / np.where(d16 == 0, 1.0, d16.astype(np.float64))[..., None]), -2, 2)
+        return (t + 2).reshape(N, K).astype(np.uint8), d16, np.full(d16.shape, 2.0, np.float16)
+    monkeypatch.setattr(ow, "quantize_bit_balance", range_step)
+    with pytest.raises(AssertionError):
+        tbb.test_hand_case()
