@@ -98,6 +98,8 @@ WORKLOADS = {
     "w4a4": dict(fmt="wnam", planes=4, abits=4, data="w2a8", shape_idx=1, N=11008, K=4096),
     "w2a4": dict(fmt="wnam", planes=2, abits=4, data="w2a8", shape_idx=1, N=11008, K=4096),
     "w3a8": dict(fmt="wnam", planes=3, abits=8, data="w2a8", shape_idx=1, N=11008, K=4096),
+    # ABQ bit balance: the symmetric five-level 2-bit grid on three planes
+    "wbb": dict(fmt="wnam", planes=3, abits=8, bit_balance=True, data="w2a8", shape_idx=1, N=11008, K=4096),
     # fully binary XNOR+popcount: SIGN1 weights x sign activations (binarizer + GEMV per step)
     "xnor": dict(fmt="sign", binary=True, data="sign", shape_idx=0, N=11008, K=4096),
     # HGF: ternary layer + rank-32 gated correction (activation step with the
@@ -143,7 +145,10 @@ def cpu_baseline(wl: dict, budget_s: float = 12.0) -> dict:
             return og.gemv_w2a8(qw, delta, zero, q, d)
         what = "oracle act quantize + gemv_w2a8 (fp64 dequant + dot)"
     elif fmt == "wnam":
-        qw, delta, zero = ow.quantize_wnam(W, wl["planes"])
+        if wl.get("bit_balance"):
+            qw, delta, zero = ow.quantize_bit_balance(W)
+        else:
+            qw, delta, zero = ow.quantize_wnam(W, wl["planes"])
         def run():
             q, d = oact.quantize(xf, wl["abits"])
             return og.gemv_w2a8(qw, delta, zero, q, d)
@@ -241,7 +246,7 @@ def main():
         Ab, Bb, alpha = synth.lora_params(si, N, K, wl["rank"])
         blob = bq.quantize_weights_hgf(desc, W, Ab, Bb, alpha)
     else:
-        blob = bq.quantize_weights(desc, W)
+        blob = bq.quantize_weights(desc, W, bit_balance=bool(wl.get("bit_balance")))
     log(f"quantized+packed {fmt} {N}x{K} in {time.perf_counter() - t0:.1f}s, blob {blob.nbytes} B")
     alg_bytes = packed_bytes(fmt, N, K, wl.get("planes", 2), wl.get("rank", 0))
     gemv_bytes = kernel_bytes(wl)

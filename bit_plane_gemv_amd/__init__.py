@@ -73,7 +73,8 @@ class WDesc(ctypes.Structure):
 
 
 class QuantOpts(ctypes.Structure):
-    _fields_ = [("rabit_svid_sweeps", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7)]
+    _fields_ = [("rabit_svid_sweeps", ctypes.c_int32), ("wnam_bit_balance", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 6)]
 
 
 class Logical(ctypes.Structure):
@@ -190,15 +191,17 @@ def pack_weights(desc: WDesc, **fields) -> np.ndarray:
     return blob
 
 
-def quantize_weights(desc: WDesc, W: np.ndarray, nthreads: int = 0, svid_sweeps: int = 0) -> np.ndarray:
+def quantize_weights(desc: WDesc, W: np.ndarray, nthreads: int = 0, svid_sweeps: int = 0,
+                     bit_balance: bool = False) -> np.ndarray:
     """fp32 W [N, K] -> packed blob with the library's own offline quantizer
-    (RABIT: svid_sweeps Gauss-Seidel refinement sweeps after the greedy pass)."""
+    (RABIT: svid_sweeps Gauss-Seidel refinement sweeps after the greedy pass;
+    WNAM with 3 planes: bit_balance selects the symmetric five-level grid)."""
     W = np.ascontiguousarray(W, dtype=np.float32)
     if W.shape != (desc.N, desc.K):
         raise ValueError(f"W has shape {W.shape}, descriptor says {(desc.N, desc.K)}")
     blob = np.zeros(packed_size(desc), dtype=np.uint8)
-    if svid_sweeps:
-        opts = QuantOpts(svid_sweeps)
+    if svid_sweeps or bit_balance:
+        opts = QuantOpts(svid_sweeps, int(bit_balance))
         _check(_lib.bitq_quantize_weights_opts(ctypes.byref(desc), W.ctypes.data, ctypes.byref(opts),
                                                blob.ctypes.data, blob.nbytes, nthreads))
     else:

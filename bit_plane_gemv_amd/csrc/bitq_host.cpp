@@ -557,6 +557,33 @@ void quantize_w2a8(const bitq_wdesc& d, const float* W, std::vector<uint8_t>& q,
     });
 }
 
+// [ABQ] §3.3 bit balance: symmetric five-level grid {-2..2} per 128-group,
+// delta = fl16(max|W| / 2), code = clamp(rint(W / delta), -2, 2) + 2, z = 2;
+// a zero step gives delta = 1 and code 2.  fp64 arithmetic from the fp32
+// weights and the fp16 step.
+void quantize_bit_balance(const bitq_wdesc& d, const float* W, std::vector<uint8_t>& q,
+                          std::vector<uint16_t>& delta, std::vector<uint16_t>& zero, int nthreads) {
+    const int64_t N = d.N, K = d.K, G = K / 128;
+    q.assign(N * K, 2);
+    delta.assign(N * G, 0x3C00);
+    zero.assign(N * G, 0x4000);  // fp16 2.0
+    parallel_for(N, nthreads, [&](int64_t n) {
+        for (int64_t gi = 0; gi < G; ++gi) {
+            const float* w = W + n * K + gi * 128;
+            double amax = 0.0;
+            for (int i = 0; i < 128; ++i) amax = std::max(amax, std::fabs(static_cast<double>(w[i])));
+            const uint16_t d16 = f64_to_f16(amax / 2.0);
+            const double dl = f16_to_f64(d16);
+            if (dl == 0.0) continue;  // degenerate group: delta = 1, code 2
+            delta[n * G + gi] = d16;
+            for (int i = 0; i < 128; ++i) {
+                const double t = std::min(2.0, std::max(-2.0, std::nearbyint(static_cast<double>(w[i]) / dl)));
+                q[n * K + gi * 128 + i] = static_cast<uint8_t>(t + 2.0);
+            }
+        }
+    });
+}
+
 // [BVSR] introduction: coefficient sets are scaled/shifted subset sums of a
 // geometric series; 256 sets from 16 ratios x 16 spans (group-range quantiles).
 void bvsr_cache(const bitq_wdesc& d, const float* W, float* cache) {
@@ -838,8 +865,12 @@ bitq_status bitq_quantize_weights_opts(const bitq_wdesc* desc, const float* W, c
     bitq_status s = check_desc(desc);
     if (s) return s;
     if (!opts) return fail(BITQ_E_ARG, "opts is NULL");
-    for (int i = 0; i < 7; ++i)
+    for (int i = 0; i < 6; ++i)
         if (opts->reserved[i]) return fail(BITQ_E_ARG, "opts->reserved[%d] must be 0", i);
+    if (opts->wnam_bit_balance != 0 && opts->wnam_bit_balance != 1)
+        return fail(BITQ_E_ARG, "wnam_bit_balance must be 0 or 1");
+    if (opts->wnam_bit_balance && (desc->fmt != BITQ_WNAM || desc->planes != 3))
+        return fail(BITQ_E_ARG, "wnam_bit_balance needs the WNAM format with planes = 3 (codes 0..4)");
     if (opts->rabit_svid_sweeps < 0 || opts->rabit_svid_sweeps > 1000)
         return fail(BITQ_E_ARG, "rabit_svid_sweeps=%d out of range [0, 1000]", opts->rabit_svid_sweeps);
     if (opts->rabit_svid_sweeps && desc->fmt != BITQ_RABIT)
@@ -888,7 +919,10 @@ bitq_status bitq_quantize_weights_opts(const bitq_wdesc* desc, const float* W, c
                 break;
             case BITQ_W2A8:
             case BITQ_WNAM:
-                quantize_w2a8(d, W, u8, delta, zero, nthreads);
+                if (opts->wnam_bit_balance)
+                    quantize_bit_balance(d, W, u8, delta, zero, nthreads);
+                else
+                    quantize_w2a8(d, W, u8, delta, zero, nthreads);
                 lg.code = u8.data();
                 lg.delta = delta.data();
                 lg.zero = zero.data();

@@ -239,7 +239,14 @@ typedef struct {
                                    T = W - sum_{q != p} g_q B_q h_q (stored fp16
                                    scales): B_p = sign(T), (g_p, h_p) = rank-1
                                    fit of |T|.  0..1000 */
-    int32_t reserved[7];
+    int32_t wnam_bit_balance;   /* WNAM with planes = 3: [ABQ] §3.3 bit balance,
+                                   the 2-bit grid widened to the symmetric
+                                   {-2,-1,0,1,2}: per 128-group
+                                   delta = fl16(max|W| / 2),
+                                   code = clamp(rint(W / delta), -2, 2) + 2,
+                                   z = 2 (a zero step gives delta = 1, code 2).
+                                   0 or 1 */
+    int32_t reserved[6];
 } bitq_quant_opts;
 
 /* bitq_quantize_weights with options (NULL opts: BITQ_E_ARG). */

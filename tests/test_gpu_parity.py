@@ -360,14 +360,14 @@ def test_w2a8_batch_invariance_and_determinism():
 
 
 # ===================================================================== WnAm
-def _wnam_case(N, K, M, n, m, W, xs, xf, rows=None):
-    """n-bit weights (oracle RTN, library packer) x m-bit activations (library
-    quantizer, checked against the oracle's): exact group partials A and the
-    float output within tolerance."""
+def _wnam_case(N, K, M, n, m, W, xs, xf, rows=None, balanced=False):
+    """n-bit weights (oracle RTN, or the oracle's bit-balance grid; library
+    packer) x m-bit activations (library quantizer, checked against the
+    oracle's): exact group partials A and the float output within tolerance."""
     q, d = oact.quantize(xf, m)
     act, got = quantize_act_dev(xs, M, K, m)
     assert np.array_equal(got["q"][:, :K], q) and np.array_equal(got["d"].view(np.uint32), d.view(np.uint32))
-    qw, delta, zero = ow.quantize_wnam(W, n)
+    qw, delta, zero = ow.quantize_bit_balance(W) if balanced else ow.quantize_wnam(W, n)
     desc = bq.wdesc(bq.WNAM, N, K, planes=n, abits=m)
     bd = dev_blob(bq.pack_weights(desc, code=qw, delta=delta, zero=zero))
     r = np.arange(N) if rows is None else rows
@@ -699,3 +699,15 @@ def test_mfma_extreme_codes_and_activations():
             A = run_gemv(desc, bd, act, bq.DT_ACT, M, bq.F_ACC_INT32, M * N).reshape(M, N)
             ref = q @ code.astype(np.int64).T
         assert np.array_equal(A, ref), fmt
+
+
+@pytest.mark.parametrize("M", [1, 3, 16, 64])
+def test_wnam_bit_balance(M):
+    # the symmetric five-level grid on three planes (z = 2), M = 1/3 on the
+    # VALU kernel and 16/64 on the matrix cores
+    N, K = 11008 if M == 1 else 520, 4096
+    say("wnam bit balance", N, K, M)
+    W = synth.weights("w2a8", 1, N, K)
+    xs, xf = synth.activations("w2a8", 1, M, K)
+    rows = np.arange(0, N, 37) if N > 1024 else None
+    _wnam_case(N, K, M, 3, 8, W, xs, xf, rows=rows, balanced=True)

@@ -213,3 +213,23 @@ def test_library_hgf_quantizer_matches_oracle():
     with pytest.raises(bq.BitqError) as e:
         bq.quantize_weights_hgf(d, W, bad, Bb, alpha)
     assert e.value.status == bq.E_ARG
+
+
+def test_library_bit_balance_matches_oracle_and_validation():
+    import ctypes
+    N, K = 130, 512
+    W = _w(N, K)
+    d = bq.wdesc(bq.WNAM, N, K, planes=3, abits=8)
+    blob = bq.quantize_weights(d, W, bit_balance=True)
+    c, delta, zero = ow.quantize_bit_balance(W)
+    assert np.array_equal(blob, bq.pack_weights(d, code=c, delta=delta, zero=zero))
+    u = layout.unpack(blob)
+    assert u["q"].max() == 4 and np.all(u["zero"] == 2)
+    buf = np.zeros(bq.packed_size(d), dtype=np.uint8)
+    call = lambda desc, opts: bq._lib.bitq_quantize_weights_opts(ctypes.byref(desc), W.ctypes.data,
+                                                                 ctypes.byref(opts), buf.ctypes.data,
+                                                                 buf.nbytes, 1)
+    assert call(bq.wdesc(bq.WNAM, N, K, planes=2, abits=8), bq.QuantOpts(0, 1)) == bq.E_ARG
+    assert call(bq.wdesc(bq.W2A8, N, K), bq.QuantOpts(0, 1)) == bq.E_ARG
+    assert call(d, bq.QuantOpts(0, 2)) == bq.E_ARG
+    assert call(d, bq.QuantOpts(0, 1)) == bq.OK
