@@ -711,3 +711,37 @@ def test_wnam_bit_balance(M):
     xs, xf = synth.activations("w2a8", 1, M, K)
     rows = np.arange(0, N, 37) if N > 1024 else None
     _wnam_case(N, K, M, 3, 8, W, xs, xf, rows=rows, balanced=True)
+
+
+# ============================================================ maximum sizes
+@pytest.mark.parametrize("fmt", [bq.TERNARY, bq.W2A8])
+@pytest.mark.parametrize("M", [1, 4])
+def test_max_k_integer(fmt, M):
+    # K = 2^20 (the largest the ABI accepts): many rounds of k blocks per
+    # workgroup on the VALU kernel, 64+ blocks per wave on the matrix cores
+    N, K = 64, 1 << 20
+    say("max K", fmt, N, K, M)
+    rng = np.random.default_rng(M)
+    W = synth.gaussian_f32(rng, (N, K), 0.02)
+    xs, xf = synth.random_bf16(rng, (M, K))
+    _int_case(fmt, N, K, M, W, xs, xf)
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_large_n_integer(M):
+    # 2^20 output rows (16384 row tiles): sampled rows against the oracle
+    N, K = 1 << 20, 128
+    say("large N", N, K, M)
+    rng = np.random.default_rng(7 + M)
+    W = synth.gaussian_f32(rng, (N, K), 0.02)
+    xs, xf = synth.random_bf16(rng, (M, K))
+    rows = np.concatenate([np.arange(0, 64), rng.choice(N, 2000, replace=False), np.arange(N - 64, N)])
+    _int_case(bq.TERNARY, N, K, M, W, xs, xf, rows=rows)
+
+
+@pytest.mark.parametrize("M", [1, 3])
+def test_max_k_xnor(M):
+    N, K = 64, 64512          # the SIGN1 descriptor's largest K
+    say("max K xnor", N, K, M)
+    xs, xf = synth.random_bf16(np.random.default_rng(11 + M), (M, K))
+    _xnor_case(N, K, M, xs, xf, seed=5)
