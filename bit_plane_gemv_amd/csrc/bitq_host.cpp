@@ -794,7 +794,7 @@ Plan make_plan(const bitq_wdesc& d, int M) {
         p.rows_per_wg = rg;
         p.row_groups = static_cast<int>((d.N + rg - 1) / rg);
         p.splits = 1;
-        p.off_partials = p.off_counters = 0;
+        p.off_partials = 0;
         p.ws_bytes = 0;
         // the contraction is compute-bound on the VALU from 2 tokens on; from
         // kMfmaMinM tokens the int8 matrix-core kernel is faster and takes
@@ -815,7 +815,6 @@ Plan make_plan(const bitq_wdesc& d, int M) {
     p.blocks_per_split = kb;
     p.splits = static_cast<int>((NB + p.blocks_per_split - 1) / p.blocks_per_split);
     p.off_partials = 0;
-    p.off_counters = 0;
     p.ws_bytes = p.splits > 1 ? align256(static_cast<size_t>(M) * Np * 8) : 0;  // one split-k word per row
     return p;
 }

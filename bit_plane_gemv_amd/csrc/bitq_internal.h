@@ -57,7 +57,6 @@ struct Plan {
     int splits;            // ceil((Kp/128) / blocks_per_split)
     int M;
     size_t off_partials;   // float formats: u64 [Np] split-k words (count + fixed-point sum)
-    size_t off_counters;   // unused (0)
     size_t ws_bytes;
     bool mfma;             // integer formats, M >= kMfmaMinM: the int8 matrix-core kernel
 };

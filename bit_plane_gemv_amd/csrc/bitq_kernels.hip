@@ -1,19 +1,22 @@
-// HIP kernels of libbitq for gfx950 (MI355X): the per-token activation
-// quantizer, the sign-apply GEMV for float activations (SIGN1/RABIT) and the
-// AND+popcount GEMV for integer activations (TERNARY/W2A8/BVSR4).
+// HIP kernels of libbitq for gfx950 (MI355X):
+//   quant_act_kernel      per-token int8 / m-bit activation quantizer (and,
+//                         for HGF layers, the correction's down projection)
+//   gemv_sign_kernel      sign-apply GEMV for float activations (SIGN1, RABIT)
+//   gemv_bits_nr_kernel   AND+popcount GEMV for integer activations (TERNARY,
+//                         W2A8, BVSR4, WNAM, HGF), M = 1 and the VALU small-M path
+//   gemm_mfma_kernel      small-M GEMM on the int8 matrix cores (TERNARY,
+//                         W2A8, WNAM; M >= 4)
+//   binarize_act_kernel, gemv_xnor_kernel   the fully binary XNOR path
 //
 // Sources are cited by the short names defined in include/bitq.h:
 // [RaBiT], [HGF], [ABQ], [BVSR], [BitNet].
 //
-// Work decomposition shared by the GEMV kernels: lane l of a wave owns output
-// row n = 64 t + l of row tile t and reads that row's packed words with one
-// 16-byte load per plane and k block (the 64 lanes read 1 KB contiguously,
-// see the blob layout in bitq.h).  A workgroup covers `waves` row tiles and a
-// slice of `blocks_per_split` k blocks; the grid is (row groups, splits).
-// When the k range is split, each workgroup stores its partial outputs in the
-// workspace and the last workgroup of a row group to arrive (arrival counter,
-// device-scope fences) adds the partials in split order and writes y, so the
-// result does not depend on scheduling.
+// Weights come in the packed blob layout of bitq.h: 64-row tiles in which
+// each row owns 16 contiguous bytes per plane and 128-input block, so 64
+// lanes reading one row each load 1 KB contiguously.  Each kernel's own
+// comment gives its work decomposition.  Results never depend on workgroup
+// scheduling: integer partial sums are exact, float partials are added in a
+// fixed order or, across workgroups, as 64-bit fixed-point integers.
 
 #include <hip/hip_runtime.h>
 
