@@ -404,6 +404,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.workload} {N}x{K} M={M} ({'RaBiT 2-path residual binary, bf16 x' if fmt == 'rabit' else fmt})",
                    "N": N, "K": K, "M": M, "format": fmt, "packed_bytes": alg_bytes,
+                   "seeds": {"W": synth.seed_for(synth.CONFIGS[data]["cfg"], si, synth.ROLE_W),
+                             "x": synth.seed_for(synth.CONFIGS[data]["cfg"], si, synth.ROLE_X)},
                    "rotating_copies": copies, "rotating_bytes": copies * stride,
                    "graph_replay": graph is not None, "host_wall_s": round(wall, 4),
                    **({"weight_bits": wl["planes"], "act_bits": abits} if fmt == "wnam" else {}),
