@@ -406,6 +406,11 @@ bitq_status bitq_gemv(const bitq_wdesc* desc, const void* w_dev, const void* x_d
  * reading every weight once for all M tokens.
  *   act_dev activation buffer from bitq_quantize_act(_bits) with this M
  *           (SIGN1: from bitq_binarize_act; HGF: from bitq_quantize_act_hgf).
+ * From 4 tokens on, TERNARY, W2A8 and WNAM run on the int8 matrix cores
+ * (codes recombined from the planes, exact int32 sums): the integer partials
+ * equal those of bitq_gemv, the fp32 outputs agree within the tolerance
+ * (another summation order), and a token's output does not depend on the
+ * other tokens of the batch.
  *   y_dev   fp32 [M][N].  BITQ_F_ACC_INT32 writes [M][...] int32 partials
  *           laid out as in bitq_gemv, one block per token.
  */
