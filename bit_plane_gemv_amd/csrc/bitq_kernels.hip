@@ -310,7 +310,7 @@ __device__ __forceinline__ float abs_sum8(uint4 v) {  // |.| summed over 8 bf16 
     return s;
 }
 
-template <int P, int KB, bool RABIT, int DT>
+template <int P, int KB, bool RABIT, int DT, int XPT>
 __global__ __launch_bounds__(256) void gemv_sign_kernel(const uint8_t* __restrict__ blob, size_t off_c0,
                                                         size_t off_c1, const void* __restrict__ x, int N, int K,
                                                         int Np, int Tn, int Tb, int splits, float* __restrict__ y,
@@ -318,7 +318,9 @@ __global__ __launch_bounds__(256) void gemv_sign_kernel(const uint8_t* __restric
     constexpr int CH = KB * 32;            // 4-input chunks in the k slice
     constexpr int NT = CH * P;             // tables in the k slice
     constexpr int TPT = (NT + 255) / 256;  // tables per thread
-    constexpr int XPT = 8;                 // uint4 of x per thread for sum |x| (more: a loop)
+    // XPT: uint4 of x per thread for sum |x| (more: a loop), sized to K by
+    // the launcher: clamped duplicate loads cost memory-pipeline slots and
+    // registers (8 instead of 2 at K = 4096 measured 0.5 us slower)
     __shared__ float4 lut4[NT * 4];        // [chunk][plane][16 floats]
     __shared__ float s_xsum[4];
     const int split = blockIdx.y;
@@ -447,9 +449,9 @@ __global__ __launch_bounds__(256) void gemv_sign_kernel(const uint8_t* __restric
     float part = 0.0f;
     {
         const uint8_t* lut_bytes = reinterpret_cast<const uint8_t*>(lut4);
-        float acc[P];
+        float acc[P], acc2[P];  // even and odd nibbles: two add chains per path
 #pragma unroll
-        for (int p = 0; p < P; ++p) acc[p] = 0.0f;
+        for (int p = 0; p < P; ++p) acc[p] = acc2[p] = 0.0f;
 #pragma unroll
         for (int bb = 0; bb < KB; ++bb)
 #pragma unroll
@@ -468,10 +470,12 @@ __global__ __launch_bounds__(256) void gemv_sign_kernel(const uint8_t* __restric
                         const uint32_t a0 = nib_addr(w4, j);
                         const uint32_t a1 = nib_addr(w2, j);
                         acc[p] += *reinterpret_cast<const float*>(lut_bytes + a0 + ((c * P + p) * 64));
-                        acc[p] += *reinterpret_cast<const float*>(lut_bytes + a1 + (((c + 1) * P + p) * 64));
+                        acc2[p] += *reinterpret_cast<const float*>(lut_bytes + a1 + (((c + 1) * P + p) * 64));
                     }
                 }
             }
+#pragma unroll
+        for (int p = 0; p < P; ++p) acc[p] += acc2[p];
         if (RABIT) {
 #pragma unroll
             for (int p = 0; p < P; ++p) part += f16_bits_to_f32(graw[p]) * acc[p];
@@ -1348,14 +1352,30 @@ int launch_quantize_act_hgf(const void* x, int x_dtype, int M, int K, int rank, 
     return static_cast<int>(hipGetLastError());
 }
 
-template <int P, int KB, bool RABIT, int DT>
-static void launch_sign(const bitq_wdesc& d, const Plan& pl, const BlobLayout& L, const void* w, const void* x,
-                        float* y, void* ws, hipStream_t st) {
+template <int P, int KB, bool RABIT, int DT, int XPT>
+static void launch_sign_x(const bitq_wdesc& d, const Plan& pl, const BlobLayout& L, const void* w, const void* x,
+                          float* y, void* ws, hipStream_t st) {
     uint8_t* wsb = static_cast<uint8_t*>(ws);
-    hipLaunchKernelGGL((gemv_sign_kernel<P, KB, RABIT, DT>), dim3(pl.row_groups, pl.splits), dim3(256), 0, st,
+    hipLaunchKernelGGL((gemv_sign_kernel<P, KB, RABIT, DT, XPT>), dim3(pl.row_groups, pl.splits), dim3(256), 0, st,
                        static_cast<const uint8_t*>(w), L.off_c0, L.off_c1, x, d.N, d.K, static_cast<int>(L.Np),
                        static_cast<int>(L.Tn), static_cast<int>(L.Tb), pl.splits, y,
                        reinterpret_cast<unsigned long long*>(wsb + pl.off_partials));
+}
+
+template <int P, int KB, bool RABIT, int DT>
+static void launch_sign(const bitq_wdesc& d, const Plan& pl, const BlobLayout& L, const void* w, const void* x,
+                        float* y, void* ws, hipStream_t st) {
+    // uint4 loads of x per thread for the split-k bound: all of x in one go
+    // up to 8 per thread (16384 bf16 / 8192 fp32 inputs), the rest in a loop
+    const int n16 = DT == BITQ_DT_F32 ? d.K / 4 : d.K / 8;
+    if (n16 <= 256)
+        launch_sign_x<P, KB, RABIT, DT, 1>(d, pl, L, w, x, y, ws, st);
+    else if (n16 <= 512)
+        launch_sign_x<P, KB, RABIT, DT, 2>(d, pl, L, w, x, y, ws, st);
+    else if (n16 <= 1024)
+        launch_sign_x<P, KB, RABIT, DT, 4>(d, pl, L, w, x, y, ws, st);
+    else
+        launch_sign_x<P, KB, RABIT, DT, 8>(d, pl, L, w, x, y, ws, st);
 }
 
 template <int P, bool RABIT, int DT>
