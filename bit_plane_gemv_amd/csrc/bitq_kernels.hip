@@ -1374,6 +1374,8 @@ static void launch_sign(const bitq_wdesc& d, const Plan& pl, const BlobLayout& L
         launch_sign_x<P, KB, RABIT, DT, 2>(d, pl, L, w, x, y, ws, st);
     else if (n16 <= 1024)
         launch_sign_x<P, KB, RABIT, DT, 4>(d, pl, L, w, x, y, ws, st);
+    else if (n16 <= 1536)
+        launch_sign_x<P, KB, RABIT, DT, 6>(d, pl, L, w, x, y, ws, st);
     else
         launch_sign_x<P, KB, RABIT, DT, 8>(d, pl, L, w, x, y, ws, st);
 }
