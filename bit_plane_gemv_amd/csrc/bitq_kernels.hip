@@ -1217,8 +1217,13 @@ __global__ __launch_bounds__(256) void gemv_xnor_kernel(const uint8_t* __restric
     if (t >= (N + 63) / 64) return;               // padding workgroups of the last XCD round
     const int rowin = RG * quarter + r;
     const int NB = Tb;
-    for (int i = tid; i < 64 * RG; i += 256) (&s_cnt[0][0])[i] = 0;
-    __syncthreads();
+    // the epilogue's scales, loaded now rather than after the k loop: a
+    // thread writes row r (256 is a multiple of RG) for tokens tid / RG and
+    // (tid + 256) / RG
+    const float* beta = reinterpret_cast<const float*>(act + act_off_beta);
+    const float alpha_r = reinterpret_cast<const float*>(blob + off_c0)[min(64 * t + rowin, N - 1)];
+    const float beta0 = beta[min(tid / RG, M - 1)], beta1 = beta[min((tid + 256) / RG, M - 1)];
+    for (int i = tid; i < 64 * RG; i += 256) (&s_cnt[0][0])[i] = 0;  // visible after the barrier below
     const uint8_t* __restrict__ tile = blob + kHeaderBytes + static_cast<size_t>(t) * Tb * 1024;  // one plane
     const uint4* __restrict__ xw = reinterpret_cast<const uint4*>(act);  // [M][Kw] words = [M][NB] uint4
     const int rounds = (NB + NBW - 1) / NBW;
@@ -1247,21 +1252,27 @@ __global__ __launch_bounds__(256) void gemv_xnor_kernel(const uint8_t* __restric
             }
 #pragma unroll
             for (int sh = RG; sh < 64; sh *= 2) c += __shfl_xor(c, sh, 64);
+            if (rd == 0 && m == 0) {
+                // the empty asm keeps the scale loads up here (they have
+                // landed: loads complete in order and the k loads above were
+                // issued after them), instead of letting the compiler sink
+                // them into the epilogue
+                asm volatile("" ::"v"(alpha_r), "v"(beta0), "v"(beta1));
+                __syncthreads();  // the zeroed counters, before the first add
+            }
             if ((tid & 63) < RG) atomicAdd(&s_cnt[m][r], c);
         }
     }
     __syncthreads();
-    const float* beta = reinterpret_cast<const float*>(act + act_off_beta);
     for (int i = tid; i < M * RG; i += 256) {
-        const int m = i / RG, rr = i % RG;
+        const int m = i / RG, rr = i % RG;  // rr == r
         const int n = 64 * t + RG * quarter + rr;
         if (n >= N) continue;
         const int Y = K - 2 * s_cnt[m][rr];
         if (ACC) {
             reinterpret_cast<int32_t*>(y)[static_cast<size_t>(m) * N + n] = Y;
         } else {
-            const float alpha = reinterpret_cast<const float*>(blob + off_c0)[n];
-            y[static_cast<size_t>(m) * N + n] = (alpha * beta[m]) * static_cast<float>(Y);
+            y[static_cast<size_t>(m) * N + n] = (alpha_r * (i < 256 ? beta0 : beta1)) * static_cast<float>(Y);
         }
     }
 }
