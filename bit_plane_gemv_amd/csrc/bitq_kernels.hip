@@ -317,7 +317,11 @@ __global__ __launch_bounds__(256) void gemv_sign_kernel(const uint8_t* __restric
                                                         unsigned long long* __restrict__ ws_acc) {
     constexpr int CH = KB * 32;            // 4-input chunks in the k slice
     constexpr int NT = CH * P;             // tables in the k slice
-    constexpr int TPT = (NT + 255) / 256;  // tables per thread
+    // SPLIT (2 or 4) threads share a table when 256 is a multiple of the
+    // table count (each writes 4 / SPLIT of its 4 float4); otherwise TPT
+    // tables per thread.  Surplus threads rebuild (parts of) the last table.
+    constexpr int SPLIT = (NT < 256 && 256 % NT == 0) ? (256 / NT < 4 ? 256 / NT : 4) : 1;
+    constexpr int TPT = (NT * SPLIT + 255) / 256;  // tables per thread
     // XPT: uint4 of x per thread for sum |x| (more: a loop), sized to K by
     // the launcher: clamped duplicate loads cost memory-pipeline slots and
     // registers (8 instead of 2 at K = 4096 measured 0.5 us slower)
@@ -337,7 +341,7 @@ __global__ __launch_bounds__(256) void gemv_sign_kernel(const uint8_t* __restric
     uint2 xraw[TPT][2], hraw[TPT];
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
-        const int tbl = min(static_cast<int>(threadIdx.x) + 256 * i, NT - 1);
+        const int tbl = min(static_cast<int>(threadIdx.x) / SPLIT + 256 * i, NT - 1);
         const int c = tbl / P, p = tbl % P;
         const int k = min(k0 + 4 * c, K - 4);  // clamped; chunks past K get zero tables below
         if (DT == BITQ_DT_F32) {
@@ -404,7 +408,7 @@ __global__ __launch_bounds__(256) void gemv_sign_kernel(const uint8_t* __restric
     // last table rebuild that table and store the same values again.
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
-        const int tbl = min(static_cast<int>(threadIdx.x) + 256 * i, NT - 1);
+        const int tbl = min(static_cast<int>(threadIdx.x) / SPLIT + 256 * i, NT - 1);
         {
             const int c = tbl / P;
             float xv[4], hv[4] = {1.0f, 1.0f, 1.0f, 1.0f};
@@ -425,9 +429,12 @@ __global__ __launch_bounds__(256) void gemv_sign_kernel(const uint8_t* __restric
             const float lo[4] = {-a - bq, a - bq, -a + bq, a + bq};
             const float hi[4] = {-cc - dd, cc - dd, -cc + dd, cc + dd};
             float4* dst = &lut4[tbl * 4];
+            const int q0 = (static_cast<int>(threadIdx.x) % SPLIT) * (4 / SPLIT);
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
+            for (int qq = 0; qq < 4 / SPLIT; ++qq) {
+                const int q4 = q0 + qq;
                 dst[q4] = make_float4(lo[0] + hi[q4], lo[1] + hi[q4], lo[2] + hi[q4], lo[3] + hi[q4]);
+            }
         }
     }
     {  // sum |x|: this thread's inputs (clamped duplicates masked to zero
