@@ -1551,10 +1551,12 @@ static void launch_mfma(const bitq_wdesc& d, const BlobLayout& L, const void* w,
     // Launch shape (measured on 11008x4096 and 4096x11008 W2A8 and 4096^2
     // ternary layers, M = 2..64): 16 rows per workgroup and 8 or 16 waves
     // over k (about 4-8k waves in flight, each with one or two load chunks
-    // of 2 blocks), except that with 17+ tokens on layers of 8192+ rows the
-    // q operands are worth sharing by 64-row workgroups.
+    // of 2 blocks), except that on layers of 8192+ rows the q operands are
+    // worth sharing by 64-row workgroups from 8 tokens on (16 waves, one
+    // block per chunk, up to 16 tokens; 8 waves, two blocks, beyond).
     const int TT = (M + 15) / 16;  // token tiles of 16
     const bool wide = TT >= 2 && d.N >= 8192;
+    const bool tall16 = TT == 1 && M >= 8 && d.N >= 8192;
     const bool kw16 = d.N <= 8192;
 #define BITQ_MFMA(TT_, RS, KW, CH)                                                                               \
     hipLaunchKernelGGL((gemm_mfma_kernel<FMT, P, ACC, TT_, RS, KW, CH>), dim3(tiles * (4 / RS)), dim3(64 * KW), 0, \
@@ -1569,7 +1571,12 @@ static void launch_mfma(const bitq_wdesc& d, const BlobLayout& L, const void* w,
             BITQ_MFMA(TT_, 1, 8, 2);           \
     } while (0)
     switch (TT) {
-        case 1: BITQ_MFMA_TT(1); break;
+        case 1:
+            if (tall16)
+                BITQ_MFMA(1, 4, 16, 1);
+            else
+                BITQ_MFMA_TT(1);
+            break;
         case 2: BITQ_MFMA_TT(2); break;
         case 3: BITQ_MFMA_TT(3); break;
         default: BITQ_MFMA_TT(4); break;

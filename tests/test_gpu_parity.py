@@ -727,7 +727,7 @@ def test_max_k_integer(fmt, M):
     _int_case(fmt, N, K, M, W, xs, xf)
 
 
-@pytest.mark.parametrize("M", [1, 4])
+@pytest.mark.parametrize("M", [1, 4, 8])
 def test_large_n_integer(M):
     # 2^20 output rows (16384 row tiles): sampled rows against the oracle
     N, K = 1 << 20, 128
