@@ -216,6 +216,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch every step from the host")
     ap.add_argument("--tokens", type=int, default=1,
                     help="tokens per step (integer formats: 2..64 run the small-M path)")
+    ap.add_argument("--fuse", action="store_true",
+                    help="integer formats, one token: the activation quantizer runs inside the GEMV "
+                         "kernel (BITQ_F_FUSE_QUANT), one launch per step")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -231,6 +234,10 @@ def main():
     M = args.tokens
     if M != 1 and (fmt in ("rabit",) or (fmt == "sign" and not wl.get("binary")) or not 1 <= M <= 64):
         print("--tokens > 1 needs an integer-activation workload and at most 64 tokens", file=sys.stderr)
+        sys.exit(2)
+    fuse = args.fuse
+    if fuse and (M != 1 or fmt not in ("ternary", "w2a8", "bvsr", "wnam") or wl.get("binary")):
+        print("--fuse needs one token and a TERNARY/W2A8/BVSR4/WNAM workload", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -296,6 +303,8 @@ def main():
         elif hgf:
             bq.quantize_act_hgf(desc, w, x, x_dt, M, act, act_ws, stream=stream)
             product(w, act, bq.DT_ACT, None, stream)
+        elif fuse:
+            bq.gemv(desc, w, x, x_dt, y, None, flags=bq.F_FUSE_QUANT, stream=stream)
         elif integer:
             bq.quantize_act(x, x_dt, M, K, act, stream=stream, abits=abits)
             product(w, act, bq.DT_ACT, ws, stream)
@@ -342,7 +351,7 @@ def main():
     # per-launch time of the GEMV kernel alone (integer workloads also run the
     # activation quantizer in each step): a graph of GEMV launches only
     gemv_ms = ms_per_step
-    if integer and graph is not None:
+    if integer and graph is not None and not fuse:
         g2 = torch.cuda.CUDAGraph()
         s2 = torch.cuda.Stream()
         s2.wait_stream(torch.cuda.current_stream())
@@ -383,7 +392,7 @@ def main():
         roof["hbm_gbs"] = round(achieved, 2)
         roof["hbm_frac"] = round(achieved / HBM_PEAK_GBS, 4)
     traffic = None
-    mt = MEASURED_TRAFFIC.get(args.workload) if M == 1 else None
+    mt = MEASURED_TRAFFIC.get(args.workload + ("+fuse" if fuse else "")) if M == 1 else None
     if mt is not None and mt["kernels_sha256_16"] == kernels_sha():
         traffic = round(mt["bytes_per_launch"] / (gemv_ms * 1e-3) / 1e9, 2)
 
@@ -409,6 +418,7 @@ def main():
                    "rotating_copies": copies, "rotating_bytes": copies * stride,
                    "graph_replay": graph is not None, "host_wall_s": round(wall, 4),
                    **({"weight_bits": wl["planes"], "act_bits": abits} if fmt == "wnam" else {}),
+                   **({"fused_quantizer": True} if fuse else {}),
                    **({"rank": wl["rank"], "gemv_kernel_bytes": gemv_bytes} if hgf else {})},
         "roofline": {**roof, "traffic": traffic,
                      "traffic_bytes_per_launch": mt["bytes_per_launch"] if traffic is not None else None,

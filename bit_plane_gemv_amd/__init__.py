@@ -50,6 +50,7 @@ OK, E_ARG, E_SHAPE, E_ALIGN, E_UNSUPPORTED, E_CAPACITY, E_DEVICE = 0, -1, -2, -3
 SIGN1, RABIT, TERNARY, W2A8, BVSR4, WNAM, HGF = 1, 2, 3, 4, 5, 6, 7
 DT_F32, DT_BF16, DT_ACT, DT_BINARY = 0, 1, 2, 3
 F_ACC_INT32 = 1
+F_FUSE_QUANT = 2   # bitq_gemv: raw x, the activation quantizer runs in the GEMV kernel
 
 FORMAT_NAMES = {SIGN1: "sign", RABIT: "rabit", TERNARY: "ternary", W2A8: "w2a8", BVSR4: "bvsr",
                 WNAM: "wnam", HGF: "hgf"}

@@ -1087,7 +1087,29 @@ static bitq_status gemv_common(const bitq_wdesc* desc, const void* w_dev, const 
     if (s) return s;
     const bitq_wdesc d = *desc;
     if (!w_dev || !x_dev || !y_dev) return fail(BITQ_E_ARG, "a device pointer is NULL");
-    if (flags & ~BITQ_F_ACC_INT32) return fail(BITQ_E_ARG, "unknown flags 0x%x", flags);
+    if (flags & ~(BITQ_F_ACC_INT32 | BITQ_F_FUSE_QUANT)) return fail(BITQ_E_ARG, "unknown flags 0x%x", flags);
+    if (flags & BITQ_F_FUSE_QUANT) {  // raw x, quantized in the GEMV kernel's prologue
+        if (d.fmt != BITQ_TERNARY && d.fmt != BITQ_W2A8 && d.fmt != BITQ_BVSR4 && d.fmt != BITQ_WNAM)
+            return fail(BITQ_E_UNSUPPORTED, "BITQ_F_FUSE_QUANT supports TERNARY, W2A8, BVSR4 and WNAM");
+        if (M != 1) return fail(BITQ_E_UNSUPPORTED, "BITQ_F_FUSE_QUANT is a bitq_gemv (M = 1) option");
+        if (flags & BITQ_F_ACC_INT32)
+            return fail(BITQ_E_UNSUPPORTED, "BITQ_F_FUSE_QUANT does not combine with BITQ_F_ACC_INT32");
+        if (x_dtype != BITQ_DT_F32 && x_dtype != BITQ_DT_BF16)
+            return fail(BITQ_E_ARG, "BITQ_F_FUSE_QUANT takes raw activations (BITQ_DT_F32 or BITQ_DT_BF16)");
+        if (d.K > kMaxFusedK) return fail(BITQ_E_UNSUPPORTED, "BITQ_F_FUSE_QUANT supports K <= %d", kMaxFusedK);
+        if (!aligned(x_dev, 16)) return fail(BITQ_E_ALIGN, "x_dev must be 16-byte aligned");
+        if (!aligned(w_dev, 256)) return fail(BITQ_E_ALIGN, "w_dev must be 256-byte aligned");
+        if (!aligned(y_dev, 4)) return fail(BITQ_E_ALIGN, "y_dev must be 4-byte aligned");
+        const Plan plan = make_plan(d, 1);
+        int is950 = 0;
+        int e = current_device_is_gfx950(&is950);
+        if (e) return fail(BITQ_E_DEVICE, "HIP error %d while querying the device", e);
+        if (!is950) return fail(BITQ_E_UNSUPPORTED, "current device is not gfx950");
+        e = launch_gemv_fused(d, plan, w_dev, x_dev, x_dtype, y_dev, stream);
+        if (e == kLaunchNotBuilt) return fail(BITQ_E_UNSUPPORTED, "no fused kernel for this layer shape");
+        if (e) return fail(BITQ_E_DEVICE, "HIP launch error %d", e);
+        return ok();
+    }
     const bool binary = x_dtype == BITQ_DT_BINARY;
     if (binary) {  // fully binary XNOR path: SIGN1 weights x sign activations
         if (d.fmt != BITQ_SIGN1)

@@ -62,6 +62,8 @@ struct Plan {
 };
 Plan make_plan(const bitq_wdesc& d, int M);
 constexpr int kMfmaMinM = 4;  // tokens from which TERNARY/W2A8/WNAM use the matrix cores
+constexpr int kMaxFusedK = 16384;    // BITQ_F_FUSE_QUANT: whole k range in one round of the kernel
+constexpr int kLaunchNotBuilt = -1;  // launcher: no kernel built for this combination
 
 // Kernel launchers (bitq_kernels.hip).  Arguments are already validated.
 // Each returns hipSuccess or the HIP error code of the launch.
@@ -70,6 +72,10 @@ int launch_gemv_float(const bitq_wdesc& d, const Plan& plan, const void* w, cons
                       int x_dtype, float* y, void* ws, void* stream);
 int launch_gemv_int(const bitq_wdesc& d, const Plan& plan, const void* w, const void* act,
                     int M, float* y, void* ws, uint32_t flags, void* stream);
+// Fused activation quantizer + GEMV, one token, raw x (bf16 or fp32); returns
+// kLaunchNotBuilt when the plan has no such kernel.
+int launch_gemv_fused(const bitq_wdesc& d, const Plan& plan, const void* w, const void* x, int x_dtype, float* y,
+                      void* stream);
 int launch_quantize_act_hgf(const void* x, int x_dtype, int M, int K, int rank, const void* w, const BlobLayout& L,
                             void* act, void* ws, void* stream);
 int launch_binarize_act(const void* x, int x_dtype, int M, int K, void* act, void* stream);

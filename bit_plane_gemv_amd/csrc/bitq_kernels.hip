@@ -574,7 +574,21 @@ __device__ __forceinline__ int combine_planes(const int (&a)[8]) {
 // ternary product and the correction in one kernel): the workgroup's RG rows
 // of B^T (RG rank fp16) and the token's h (rank floats, written by the
 // activation step) are copied into LDS ahead of the weight stream.
-template <int FMT, int P, bool ACC, int BPL, int RG, bool ONE>
+//
+// XQ = 1 (bf16) or 2 (fp32): the activation quantizer runs in this kernel's
+// prologue instead of a separate launch (one token, whole k range in one
+// round).  `act` is then the raw x.  Every workgroup loads all of x (small,
+// L2-resident) ahead of its weight stream, reduces amax, and quantizes it
+// with the separate quantizer's arithmetic (s = fl32(Qm/amax), q =
+// rint(fl32(x s)), d = fl32(amax/Qm)), so planes, group sums and d are the
+// same bits as that quantizer's and y is the same bits as the two-launch
+// path.  A lane takes 8 inputs (a chunk); fl32(x s) + 1.5 2^23 rounds to the
+// nearest integer (ties to even, as rint) and leaves q in the low byte of the
+// float's bits (|q| <= Qm < 2^22).  The 8 code bytes of a chunk are bit-
+// transposed as an 8x8 bit matrix (byte j = plane j of the chunk), and the 4
+// lanes of a 32-input word assemble its 8 plane words with two byte-permute
+// exchanges.  No clamp is needed: |x| <= amax gives |fl32(x s)| < Qm + 1/2.
+template <int FMT, int P, bool ACC, int BPL, int RG, bool ONE, int XQ = 0>
 __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __restrict__ blob, size_t off_c0,
                                                            size_t off_c1, const uint8_t* __restrict__ act,
                                                            size_t act_off_S, size_t act_off_d, int M, int N, int K,
@@ -606,6 +620,8 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
     float4* const s_h = reinterpret_cast<float4*>(s_lora + RG * 8 * 4);
     __shared__ float s_red[4][16];
     __shared__ int32_t s_redi[4][16];
+    constexpr bool FQ = XQ != 0;   // fused activation quantizer
+    static_assert(!FQ || (ONE && !ACC && FMT != BITQ_HGF), "fused quantizer: whole k in one round, y output");
 
     const int tid = threadIdx.x, r = tid % RG, g = tid / RG, wave = tid >> 6;
     // the wave index as a uniform value, for branches around the LDS copies
@@ -697,11 +713,120 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
                             static_cast<size_t>(64 * t + RG * quarter) * (rank / 8);
         __builtin_amdgcn_global_load_lds(bsrc + min(tid, RG * (rank / 8) - 1), s_bt + 64 * wave_u, 16, 0, 0);
     }
+    // fused quantizer: chunks c = tid + 256 i of 8 inputs (word c / 4, byte
+    // c % 4 of its plane words); XLPC 16-byte loads each
+    constexpr int XCPT = FQ ? NBW * 16 / 256 : 1;
+    constexpr int XLPC = XQ == 2 ? 2 : 1;
+    static_assert(!FQ || (NBW * 16) % 256 == 0, "whole chunks per thread");
+    uint4 xr[XCPT][XLPC];
     __builtin_amdgcn_sched_barrier(0);
-    if (ONE) stage(0, 0);
+    if constexpr (FQ) {
+        // unconditional loads (clamped to the last chunk of x) through an
+        // address without the argument's restrict provenance, kept ahead of
+        // the weight stream by the memory clobber
+        uintptr_t xaddr = reinterpret_cast<uintptr_t>(act);
+        asm volatile("" : "+s"(xaddr));
+        const int nch = K / 8;
+#pragma unroll
+        for (int i = 0; i < XCPT; ++i) {
+            const int c = min(tid + 256 * i, nch - 1);
+#pragma unroll
+            for (int l = 0; l < XLPC; ++l) xr[i][l] = global_load16(xaddr, XLPC * c + l);
+        }
+        asm volatile("" ::: "memory");
+    } else if (ONE) {
+        stage(0, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
     if (ONE) load_weights(0);
     __builtin_amdgcn_sched_barrier(0);
+
+    float dq_fused = 0.0f;  // the token's d (fused quantizer)
+    if constexpr (FQ) {
+        __shared__ float s_amax[4];
+        // 8 inputs of chunk i as floats
+        auto chunk = [&](int i, float (&v)[8]) __attribute__((always_inline)) {
+            if (XQ == 2) {
+                v[0] = __uint_as_float(xr[i][0].x); v[1] = __uint_as_float(xr[i][0].y);
+                v[2] = __uint_as_float(xr[i][0].z); v[3] = __uint_as_float(xr[i][0].w);
+                v[4] = __uint_as_float(xr[i][XLPC - 1].x); v[5] = __uint_as_float(xr[i][XLPC - 1].y);
+                v[6] = __uint_as_float(xr[i][XLPC - 1].z); v[7] = __uint_as_float(xr[i][XLPC - 1].w);
+            } else {
+                const uint32_t u[4] = {xr[i][0].x, xr[i][0].y, xr[i][0].z, xr[i][0].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[2 * e] = __uint_as_float(u[e] << 16);
+                    v[2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
+                }
+            }
+        };
+        // amax over x (clamped duplicates do not change it)
+        float am = 0.0f;
+#pragma unroll
+        for (int i = 0; i < XCPT; ++i) {
+            float v[8];
+            chunk(i, v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(v[e]));
+        }
+        am = wave_max(am);
+        if ((tid & 63) == 0) s_amax[wave] = am;
+        barrier_after_loads<kWeightLoads>();
+        am = fmaxf(fmaxf(s_amax[0], s_amax[1]), fmaxf(s_amax[2], s_amax[3]));
+        const float qmax = FMT == BITQ_WNAM ? static_cast<float>((1 << (abits - 1)) - 1) : 127.0f;
+        const float sx = am > 0.0f ? __fdiv_rn(qmax, am) : 0.0f;
+        dq_fused = am > 0.0f ? __fdiv_rn(am, qmax) : 0.0f;
+        constexpr uint32_t kMagic = 0x4B400000u;  // bits of 1.5 2^23
+        // byte-permute selectors of the two exchanges (lane e = tid % 4 of the
+        // word): after the first, even lanes hold 16-bit halves of planes
+        // (0, 1) of lanes (e, e+1), odd lanes planes (2, 3); after the second,
+        // lane e holds the whole word of plane pl (and pl + 4 from hi)
+        const uint32_t sel1 = (tid & 1) ? 0x07030602u : 0x05010400u;
+        const uint32_t sel2 = (tid & 2) ? 0x07060302u : 0x05040100u;
+        const int pl = ((tid & 1) << 1) | ((tid >> 1) & 1);
+        const int nch = K / 8;
+#pragma unroll
+        for (int i = 0; i < XCPT; ++i) {
+            const int c = tid + 256 * i;
+            const float sc = c < nch ? sx : 0.0f;  // chunks past K quantize to 0
+            float v[8];
+            chunk(i, v);
+            uint32_t b[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) b[e] = __float_as_uint(__fadd_rn(__fmul_rn(v[e], sc), 12582912.0f));
+            // group sum of the chunk: sum (bits - magic) = sum q
+            int S = static_cast<int>((b[0] + b[1] + b[2] + b[3]) + (b[4] + b[5] + b[6] + b[7]) - 8u * kMagic);
+            // code bytes (input e in byte e % 4 of lo / hi)
+            uint32_t lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u),
+                                                __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u), 0x05040100u);
+            uint32_t hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[7], b[6], 0x0c0c0400u),
+                                                __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u), 0x05040100u);
+            // 8x8 bit transpose of the 64-bit value hi:lo (bit 8e + j <-> 8j + e)
+            uint32_t t;
+            t = (lo ^ (lo >> 7)) & 0x00AA00AAu; lo = lo ^ t ^ (t << 7);
+            t = (hi ^ (hi >> 7)) & 0x00AA00AAu; hi = hi ^ t ^ (t << 7);
+            t = (lo ^ (lo >> 14)) & 0x0000CCCCu; lo = lo ^ t ^ (t << 14);
+            t = (hi ^ (hi >> 14)) & 0x0000CCCCu; hi = hi ^ t ^ (t << 14);
+            t = (lo ^ (hi << 4)) & 0xF0F0F0F0u; lo ^= t; hi ^= t >> 4;
+            // exchange 1 (lanes e, e ^ 1): L = the lower lane's value, U = the upper's
+            uint32_t plo = __shfl_xor(lo, 1, 64), phi = __shfl_xor(hi, 1, 64);
+            lo = (tid & 1) ? __builtin_amdgcn_perm(lo, plo, sel1) : __builtin_amdgcn_perm(plo, lo, sel1);
+            hi = (tid & 1) ? __builtin_amdgcn_perm(hi, phi, sel1) : __builtin_amdgcn_perm(phi, hi, sel1);
+            // exchange 2 (lanes e, e ^ 2)
+            plo = __shfl_xor(lo, 2, 64);
+            phi = __shfl_xor(hi, 2, 64);
+            lo = (tid & 2) ? __builtin_amdgcn_perm(lo, plo, sel2) : __builtin_amdgcn_perm(plo, lo, sel2);
+            hi = (tid & 2) ? __builtin_amdgcn_perm(hi, phi, sel2) : __builtin_amdgcn_perm(phi, hi, sel2);
+            S += __shfl_xor(S, 1, 64);
+            S += __shfl_xor(S, 2, 64);
+            const int word = c >> 2;  // word of the round: block word / 4, word word % 4
+            uint32_t* dst = &s_act[(word >> 2) * BSTR + 8 * (word & 3)];
+            dst[pl] = lo;
+            dst[pl + 4] = hi;
+            if ((tid & 3) == 0) s_S[word] = S;
+        }
+        barrier_after_loads<kWeightLoads>();
+    }
 
     // one activation row; the first is peeled so that its loads need no wait
     // at a loop header
@@ -709,7 +834,7 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
         // per-token (and per-tensor) scales: uniform loads issued now, long
         // before the epilogue needs them
         const float scale = (TERN && !ACC ? *reinterpret_cast<const float*>(blob + off_c0) : 1.0f) *
-                            (ACC ? 1.0f : ad[m]);
+                            (ACC ? 1.0f : (FQ ? dq_fused : ad[m]));
         const float gate = LORA ? *reinterpret_cast<const float*>(blob + kHdrGate) : 0.0f;
         float yacc = 0.0f;
         int tacc[2][8];
@@ -728,7 +853,7 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
                 __builtin_amdgcn_sched_barrier(0);
                 barrier_after_loads<kWeightLoads>();
             } else if (first) {
-                barrier_after_loads<kWeightLoads>();  // copies issued in the prologue
+                if (!FQ) barrier_after_loads<kWeightLoads>();  // copies issued in the prologue
             } else {
                 stage(m, b_base);
                 barrier_after_loads<0>();
@@ -917,7 +1042,8 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
         }
     };
     pass(0, true);
-    for (int m = 1; m < M; ++m) pass(m, false);
+    if (!FQ)
+        for (int m = 1; m < M; ++m) pass(m, false);
 }
 
 // ============================== small-M GEMM on the int8 matrix cores
@@ -1599,6 +1725,92 @@ static void launch_mfma_fmt(const bitq_wdesc& d, const BlobLayout& L, const void
                 default: launch_mfma<BITQ_WNAM, 4, ACC>(d, L, w, act, M, y, st); break;
             }
     }
+}
+
+// Fused quantizer + GEMV of one token (XQ = 1: bf16 x, 2: fp32 x).  The host
+// admits K <= kMaxFusedK, so the plan's blocks per lane (at most 4 with 8 rows
+// per workgroup, 8 with 16) keep the whole k range in one round; other
+// combinations are not built and return false.
+template <int FMT, int P, int BPL, int RG, int XQ>
+static void launch_fq_bpl(const bitq_wdesc& d, const BlobLayout& L, const void* w, const void* x, float* y,
+                          hipStream_t st) {
+    const int tiles = static_cast<int>(L.Tn);
+    const int groups = 8 * (64 / RG) * ((tiles + 7) / 8);  // as launch_nr_bpl
+    const int abits = d.fmt == BITQ_WNAM ? d.abits : 8;
+    hipLaunchKernelGGL((gemv_bits_nr_kernel<FMT, P, false, BPL, RG, true, XQ>), dim3(groups), dim3(256), 0, st,
+                       static_cast<const uint8_t*>(w), L.off_c0, L.off_c1, static_cast<const uint8_t*>(x),
+                       static_cast<size_t>(0), static_cast<size_t>(0), 1, d.N, d.K, static_cast<int>(L.Tb), abits,
+                       L.off_c2, static_cast<size_t>(0), 0, y);
+}
+
+template <int FMT, int P, int RG, int XQ>
+static bool launch_fq_rg(const bitq_wdesc& d, const Plan& pl, const BlobLayout& L, const void* w, const void* x,
+                         float* y, hipStream_t st) {
+    if (L.Tb > static_cast<size_t>(256 / RG) * pl.blocks_per_split) return false;  // not one round
+    constexpr bool wnam = FMT == BITQ_WNAM;
+    switch (pl.blocks_per_split) {
+        case 1: launch_fq_bpl<FMT, P, 1, RG, XQ>(d, L, w, x, y, st); return true;
+        case 2: launch_fq_bpl<FMT, P, 2, RG, XQ>(d, L, w, x, y, st); return true;
+        case 3:
+            if constexpr (!wnam) {
+                launch_fq_bpl<FMT, P, 3, RG, XQ>(d, L, w, x, y, st);
+                return true;
+            }
+            return false;
+        case 4: launch_fq_bpl<FMT, P, 4, RG, XQ>(d, L, w, x, y, st); return true;
+        case 6:
+            if constexpr (!wnam && RG == 16) {
+                launch_fq_bpl<FMT, P, 6, RG, XQ>(d, L, w, x, y, st);
+                return true;
+            }
+            return false;
+        case 8:
+            if constexpr (!wnam && RG == 16) {
+                launch_fq_bpl<FMT, P, 8, RG, XQ>(d, L, w, x, y, st);
+                return true;
+            }
+            return false;
+        default: return false;
+    }
+}
+
+template <int FMT, int P, int XQ>
+static bool launch_fq_fmt(const bitq_wdesc& d, const Plan& pl, const BlobLayout& L, const void* w, const void* x,
+                          float* y, hipStream_t st) {
+    if constexpr (FMT == BITQ_WNAM) {
+        return pl.rows_per_wg == 8 && launch_fq_rg<FMT, P, 8, XQ>(d, pl, L, w, x, y, st);
+    } else {
+        return pl.rows_per_wg == 8 ? launch_fq_rg<FMT, P, 8, XQ>(d, pl, L, w, x, y, st)
+                                   : launch_fq_rg<FMT, P, 16, XQ>(d, pl, L, w, x, y, st);
+    }
+}
+
+template <int XQ>
+static bool launch_fq(const bitq_wdesc& d, const Plan& pl, const BlobLayout& L, const void* w, const void* x,
+                      float* y, hipStream_t st) {
+    switch (d.fmt) {
+        case BITQ_TERNARY: return launch_fq_fmt<BITQ_TERNARY, 2, XQ>(d, pl, L, w, x, y, st);
+        case BITQ_W2A8: return launch_fq_fmt<BITQ_W2A8, 2, XQ>(d, pl, L, w, x, y, st);
+        case BITQ_BVSR4: return launch_fq_fmt<BITQ_BVSR4, 4, XQ>(d, pl, L, w, x, y, st);
+        case BITQ_WNAM:
+            switch (d.planes) {
+                case 1: return launch_fq_fmt<BITQ_WNAM, 1, XQ>(d, pl, L, w, x, y, st);
+                case 2: return launch_fq_fmt<BITQ_WNAM, 2, XQ>(d, pl, L, w, x, y, st);
+                case 3: return launch_fq_fmt<BITQ_WNAM, 3, XQ>(d, pl, L, w, x, y, st);
+                case 4: return launch_fq_fmt<BITQ_WNAM, 4, XQ>(d, pl, L, w, x, y, st);
+                default: return false;
+            }
+        default: return false;
+    }
+}
+
+int launch_gemv_fused(const bitq_wdesc& d, const Plan& pl, const void* w, const void* x, int x_dtype, float* y,
+                      void* stream) {
+    BlobLayout L = blob_layout(d);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool built = x_dtype == BITQ_DT_BF16 ? launch_fq<1>(d, pl, L, w, x, y, st) : launch_fq<2>(d, pl, L, w, x, y, st);
+    if (!built) return kLaunchNotBuilt;
+    return static_cast<int>(hipGetLastError());
 }
 
 int launch_gemv_int(const bitq_wdesc& d, const Plan& pl, const void* w, const void* act, int M, float* y,

@@ -100,6 +100,10 @@ typedef enum {
 #define BITQ_F_ACC_INT32 1u  /* integer formats only: the production main loop
                                 writes its exact int32 partial sums to y instead
                                 of the fp32 output (see bitq_gemv). */
+#define BITQ_F_FUSE_QUANT 2u /* bitq_gemv with TERNARY/W2A8/BVSR4/WNAM weights:
+                                x_dev is the raw token (BITQ_DT_BF16 or
+                                BITQ_DT_F32) and the activation quantizer runs
+                                in the GEMV kernel (see bitq_gemv). */
 
 /* Shape/format descriptor of one weight matrix. */
 typedef struct {
@@ -395,6 +399,15 @@ bitq_status bitq_workspace_size(const bitq_wdesc* desc, int32_t M, size_t* bytes
  * flags & BITQ_F_ACC_INT32 (integer formats): y_dev receives, as int32,
  *   TERNARY/HGF Y [N]; W2A8/WNAM A [N][K/128]; BVSR4 P [N][K/32][4]; SIGN1 with
  *   binary activations Y [N]; the buffer must hold that many int32 values.
+ * flags & BITQ_F_FUSE_QUANT (TERNARY, W2A8, BVSR4, WNAM; K <= 16384): x_dev
+ *   is the raw token, x_dtype BITQ_DT_BF16 or BITQ_DT_F32, 16-byte aligned,
+ *   finite values.  The activation quantizer ([HGF] §1.2 absmax int8; [ABQ]
+ *   m-bit for WNAM with desc->abits) runs in the GEMV kernel's prologue
+ *   instead of a separate bitq_quantize_act launch, with the same arithmetic:
+ *   y is bit-identical to bitq_quantize_act followed by bitq_gemv.  Nothing
+ *   but y is written (no activation buffer, no workspace).  Errors:
+ *   BITQ_E_UNSUPPORTED for other formats (HGF included), K > 16384, or
+ *   together with BITQ_F_ACC_INT32; BITQ_E_ARG for another x_dtype.
  */
 bitq_status bitq_gemv(const bitq_wdesc* desc, const void* w_dev, const void* x_dev,
                       int32_t x_dtype, float* y_dev, void* ws_dev, size_t ws_bytes,

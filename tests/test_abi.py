@@ -180,6 +180,32 @@ def test_device_entry_points_validate_before_any_device_call():
     assert bq._lib.bitq_gemm_smallM(ctypes.byref(dw), good, good, 65, good, None, 0, 0, None) == bq.E_SHAPE
 
 
+def test_fused_quantizer_flag_validation():
+    """BITQ_F_FUSE_QUANT: accepted combinations are checked before any
+    device call; the rest return the documented errors."""
+    good = 1 << 20
+    F = bq.F_FUSE_QUANT
+    gemv = bq._lib.bitq_gemv
+    d = bq.wdesc(bq.W2A8, 128, 256)
+    # raw activations only
+    assert gemv(ctypes.byref(d), good, good, bq.DT_ACT, good, None, 0, F, None) == bq.E_ARG
+    # 16-byte alignment of x (not the activation buffer's 256)
+    assert gemv(ctypes.byref(d), good, good + 8, bq.DT_BF16, good, None, 0, F, None) == bq.E_ALIGN
+    assert gemv(ctypes.byref(d), good + 16, good + 16, bq.DT_BF16, good, None, 0, F, None) == bq.E_ALIGN
+    # not with the integer-partials flag
+    assert gemv(ctypes.byref(d), good, good, bq.DT_BF16, good, None, 0, F | bq.F_ACC_INT32,
+                None) == bq.E_UNSUPPORTED
+    # K bound of the fused kernel
+    dk = bq.wdesc(bq.TERNARY, 64, 16384 + 128)
+    assert gemv(ctypes.byref(dk), good, good, bq.DT_F32, good, None, 0, F, None) == bq.E_UNSUPPORTED
+    # formats without a fused quantizer
+    for fmt, kw in ((bq.RABIT, {}), (bq.SIGN1, {}), (bq.HGF, {"rank": 32})):
+        df = bq.wdesc(fmt, 128, 256, **kw)
+        assert gemv(ctypes.byref(df), good, good, bq.DT_BF16, good, good, 1 << 20, F, None) == bq.E_UNSUPPORTED
+    # small-M entry point: not a fused option
+    assert bq._lib.bitq_gemm_smallM(ctypes.byref(d), good, good, 4, good, None, 0, F, None) == bq.E_UNSUPPORTED
+
+
 def test_act_size_matches_documented_layout():
     for M, K in [(1, 4096), (16, 512), (64, 11008), (3, 96)]:
         assert bq.act_size(M, K) == bq.act_layout(M, K)["total"]
