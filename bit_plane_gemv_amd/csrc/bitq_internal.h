@@ -60,7 +60,7 @@ struct Plan {
     size_t ws_bytes;
     bool mfma;             // integer formats, M >= kMfmaMinM: the int8 matrix-core kernel
 };
-Plan make_plan(const bitq_wdesc& d, int M);
+Plan make_plan(const bitq_wdesc& d, int M, bool fused = false);  // fused: BITQ_F_FUSE_QUANT
 constexpr int kMfmaMinM = 4;  // tokens from which TERNARY/W2A8/WNAM use the matrix cores
 constexpr int kMaxFusedK = 16384;    // BITQ_F_FUSE_QUANT: whole k range in one round of the kernel
 constexpr int kLaunchNotBuilt = -1;  // launcher: no kernel built for this combination

@@ -547,6 +547,13 @@ __device__ __forceinline__ void barrier_after_loads() {
     asm volatile("" ::: "memory");
 }
 
+// v of another lane of the same quad (DPP quad_perm: lane i of each group of
+// 4 takes lane CTRL[2i+1:2i]).
+template <int CTRL>
+__device__ __forceinline__ uint32_t quad_swap(uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+
 // A wave-uniform value moved to a scalar register (the compiler cannot tell
 // that threadIdx.x / 64 is uniform).
 __device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -777,12 +784,13 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
         const float sx = am > 0.0f ? __fdiv_rn(qmax, am) : 0.0f;
         dq_fused = am > 0.0f ? __fdiv_rn(am, qmax) : 0.0f;
         constexpr uint32_t kMagic = 0x4B400000u;  // bits of 1.5 2^23
-        // byte-permute selectors of the two exchanges (lane e = tid % 4 of the
-        // word): after the first, even lanes hold 16-bit halves of planes
-        // (0, 1) of lanes (e, e+1), odd lanes planes (2, 3); after the second,
-        // lane e holds the whole word of plane pl (and pl + 4 from hi)
-        const uint32_t sel1 = (tid & 1) ? 0x07030602u : 0x05010400u;
-        const uint32_t sel2 = (tid & 2) ? 0x07060302u : 0x05040100u;
+        // byte-permute selectors of the two exchanges, v_perm(partner, own)
+        // (lane e = tid % 4 of the word; bytes 0-3 select own, 4-7 partner's):
+        // after the first, even lanes hold 16-bit halves of planes (0, 1) of
+        // lanes (e, e+1), odd lanes planes (2, 3) of lanes (e-1, e); after the
+        // second, lane e holds the whole word of plane pl (and pl + 4 from hi)
+        const uint32_t sel1 = (tid & 1) ? 0x03070206u : 0x05010400u;
+        const uint32_t sel2 = (tid & 2) ? 0x03020706u : 0x05040100u;
         const int pl = ((tid & 1) << 1) | ((tid >> 1) & 1);
         const int nch = K / 8;
 #pragma unroll
@@ -808,17 +816,14 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
             t = (lo ^ (lo >> 14)) & 0x0000CCCCu; lo = lo ^ t ^ (t << 14);
             t = (hi ^ (hi >> 14)) & 0x0000CCCCu; hi = hi ^ t ^ (t << 14);
             t = (lo ^ (hi << 4)) & 0xF0F0F0F0u; lo ^= t; hi ^= t >> 4;
-            // exchange 1 (lanes e, e ^ 1): L = the lower lane's value, U = the upper's
-            uint32_t plo = __shfl_xor(lo, 1, 64), phi = __shfl_xor(hi, 1, 64);
-            lo = (tid & 1) ? __builtin_amdgcn_perm(lo, plo, sel1) : __builtin_amdgcn_perm(plo, lo, sel1);
-            hi = (tid & 1) ? __builtin_amdgcn_perm(hi, phi, sel1) : __builtin_amdgcn_perm(phi, hi, sel1);
-            // exchange 2 (lanes e, e ^ 2)
-            plo = __shfl_xor(lo, 2, 64);
-            phi = __shfl_xor(hi, 2, 64);
-            lo = (tid & 2) ? __builtin_amdgcn_perm(lo, plo, sel2) : __builtin_amdgcn_perm(plo, lo, sel2);
-            hi = (tid & 2) ? __builtin_amdgcn_perm(hi, phi, sel2) : __builtin_amdgcn_perm(phi, hi, sel2);
-            S += __shfl_xor(S, 1, 64);
-            S += __shfl_xor(S, 2, 64);
+            // exchange 1 with lane e ^ 1, exchange 2 with lane e ^ 2 (DPP quad
+            // permutations 1,0,3,2 and 2,3,0,1)
+            lo = __builtin_amdgcn_perm(quad_swap<0xB1>(lo), lo, sel1);
+            hi = __builtin_amdgcn_perm(quad_swap<0xB1>(hi), hi, sel1);
+            lo = __builtin_amdgcn_perm(quad_swap<0x4E>(lo), lo, sel2);
+            hi = __builtin_amdgcn_perm(quad_swap<0x4E>(hi), hi, sel2);
+            S += static_cast<int>(quad_swap<0xB1>(static_cast<uint32_t>(S)));
+            S += static_cast<int>(quad_swap<0x4E>(static_cast<uint32_t>(S)));
             const int word = c >> 2;  // word of the round: block word / 4, word word % 4
             uint32_t* dst = &s_act[(word >> 2) * BSTR + 8 * (word & 3)];
             dst[pl] = lo;
