@@ -778,12 +778,13 @@ Plan make_plan(const bitq_wdesc& d, int M, bool fused) {
         // Rows per workgroup (16 or 8): 8 rows double the waves of layers
         // with fewer than 16384 rows, which keeps more waves per SIMD to hide
         // the popcount chains (measured faster on every such layer shape).
-        // WNAM is built for 8 rows and 1, 2, 4 or 8 blocks per lane only.
-        // With the fused activation quantizer every workgroup repeats the
-        // quantization, and 16 rows per workgroup halve that work: faster
-        // from 4096 rows on (measured 5.9 against 6.5 us at 11008x4096).
+        // WNAM is built for 8 rows (16 with the fused quantizer) and 1, 2, 4
+        // or 8 blocks per lane only.  With the fused activation quantizer
+        // every workgroup repeats the quantization, and 16 rows per workgroup
+        // halve that work: faster from 4096 rows on (measured 5.9 against
+        // 6.5 us at 11008x4096).
         const bool wnam = d.fmt == BITQ_WNAM;
-        const int rg = (d.N >= (fused ? 4096 : 16384) && !wnam) ? 16 : 8;
+        const int rg = fused ? (d.N >= 4096 ? 16 : 8) : (d.N >= 16384 && !wnam ? 16 : 8);
         const int64_t kgroups = 256 / rg;
         const int64_t need = (NB + kgroups - 1) / kgroups;
         const int sizes[6] = {1, 2, 3, 4, 6, 8};

@@ -588,10 +588,10 @@ __device__ __forceinline__ int combine_planes(const int (&a)[8]) {
 // L2-resident) ahead of its weight stream, reduces amax, and quantizes it
 // with the separate quantizer's arithmetic (s = fl32(Qm/amax), q =
 // rint(fl32(x s)), d = fl32(amax/Qm)), so planes, group sums and d are the
-// same bits as that quantizer's and y is the same bits as the two-launch
-// path.  A lane takes 8 inputs (a chunk); fl32(x s) + 1.5 2^23 rounds to the
-// nearest integer (ties to even, as rint) and leaves q in the low byte of the
-// float's bits (|q| <= Qm < 2^22).  The 8 code bytes of a chunk are bit-
+// same bits as that quantizer's (and y the same bits as the two-launch path
+// whenever both use the same rows per workgroup).  A lane takes 8 inputs (a
+// chunk); fl32(x s) + 1.5 2^23 rounds to the nearest integer (ties to even,
+// as rint) and leaves q in the low byte of the float's bits (|q| <= Qm < 2^22).  The 8 code bytes of a chunk are bit-
 // transposed as an 8x8 bit matrix (byte j = plane j of the chunk), and the 4
 // lanes of a 32-input word assemble its 8 plane words with two byte-permute
 // exchanges.  No clamp is needed: |x| <= amax gives |fl32(x s)| < Qm + 1/2.
@@ -1770,7 +1770,7 @@ static bool launch_fq_rg(const bitq_wdesc& d, const Plan& pl, const BlobLayout& 
             }
             return false;
         case 8:
-            if constexpr (!wnam && RG == 16) {
+            if constexpr (RG == 16) {
                 launch_fq_bpl<FMT, P, 8, RG, XQ>(d, L, w, x, y, st);
                 return true;
             }
@@ -1782,12 +1782,8 @@ static bool launch_fq_rg(const bitq_wdesc& d, const Plan& pl, const BlobLayout& 
 template <int FMT, int P, int XQ>
 static bool launch_fq_fmt(const bitq_wdesc& d, const Plan& pl, const BlobLayout& L, const void* w, const void* x,
                           float* y, hipStream_t st) {
-    if constexpr (FMT == BITQ_WNAM) {
-        return pl.rows_per_wg == 8 && launch_fq_rg<FMT, P, 8, XQ>(d, pl, L, w, x, y, st);
-    } else {
-        return pl.rows_per_wg == 8 ? launch_fq_rg<FMT, P, 8, XQ>(d, pl, L, w, x, y, st)
-                                   : launch_fq_rg<FMT, P, 16, XQ>(d, pl, L, w, x, y, st);
-    }
+    return pl.rows_per_wg == 8 ? launch_fq_rg<FMT, P, 8, XQ>(d, pl, L, w, x, y, st)
+                               : launch_fq_rg<FMT, P, 16, XQ>(d, pl, L, w, x, y, st);
 }
 
 template <int XQ>

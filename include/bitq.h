@@ -403,9 +403,14 @@ bitq_status bitq_workspace_size(const bitq_wdesc* desc, int32_t M, size_t* bytes
  *   is the raw token, x_dtype BITQ_DT_BF16 or BITQ_DT_F32, 16-byte aligned,
  *   finite values.  The activation quantizer ([HGF] §1.2 absmax int8; [ABQ]
  *   m-bit for WNAM with desc->abits) runs in the GEMV kernel's prologue
- *   instead of a separate bitq_quantize_act launch, with the same arithmetic:
- *   y is bit-identical to bitq_quantize_act followed by bitq_gemv.  Nothing
- *   but y is written (no activation buffer, no workspace).  Errors:
+ *   instead of a separate bitq_quantize_act launch, with the same arithmetic
+ *   (the same q, planes, group sums and d).  TERNARY y is bit-identical to
+ *   bitq_quantize_act followed by bitq_gemv (exact integer sums); so is the
+ *   y of the other formats on layers below 4096 rows.  From 4096 rows on the
+ *   fused kernel takes 16 rows per workgroup (the two-launch kernel 8 below
+ *   16384 rows, and WNAM always 8), so its fp32 group terms are added in
+ *   another order and y may differ in the last bits, within the tolerance.
+ *   Nothing but y is written (no activation buffer, no workspace).  Errors:
  *   BITQ_E_UNSUPPORTED for other formats (HGF included), K > 16384, or
  *   together with BITQ_F_ACC_INT32; BITQ_E_ARG for another x_dtype.
  */
