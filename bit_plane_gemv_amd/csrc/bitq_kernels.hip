@@ -591,10 +591,11 @@ __device__ __forceinline__ int combine_planes(const int (&a)[8]) {
 // same bits as that quantizer's (and y the same bits as the two-launch path
 // whenever both use the same rows per workgroup).  A lane takes 8 inputs (a
 // chunk); fl32(x s) + 1.5 2^23 rounds to the nearest integer (ties to even,
-// as rint) and leaves q in the low byte of the float's bits (|q| <= Qm < 2^22).  The 8 code bytes of a chunk are bit-
-// transposed as an 8x8 bit matrix (byte j = plane j of the chunk), and the 4
-// lanes of a 32-input word assemble its 8 plane words with two byte-permute
-// exchanges.  No clamp is needed: |x| <= amax gives |fl32(x s)| < Qm + 1/2.
+// as rint) and leaves q in the low byte of the float's bits (|q| <= Qm <
+// 2^22).  The 8 code bytes of a chunk are bit-transposed as an 8x8 bit matrix
+// (byte j = plane j of the chunk), and the 4 lanes of a 32-input word
+// assemble its 8 plane words with two byte-permute exchanges.  No clamp is
+// needed: |x| <= amax gives |fl32(x s)| < Qm + 1/2.
 template <int FMT, int P, bool ACC, int BPL, int RG, bool ONE, int XQ = 0>
 __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __restrict__ blob, size_t off_c0,
                                                            size_t off_c1, const uint8_t* __restrict__ act,
@@ -751,7 +752,9 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
     float dq_fused = 0.0f;  // the token's d (fused quantizer)
     if constexpr (FQ) {
         __shared__ float s_amax[4];
-        // 8 inputs of chunk i as floats
+        // 8 inputs of chunk i as floats (fp32: two 16-byte loads; the index
+        // XLPC - 1 keeps the bf16 instantiation, which never takes that
+        // branch, inside the array)
         auto chunk = [&](int i, float (&v)[8]) __attribute__((always_inline)) {
             if (XQ == 2) {
                 v[0] = __uint_as_float(xr[i][0].x); v[1] = __uint_as_float(xr[i][0].y);
@@ -824,7 +827,7 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
             hi = __builtin_amdgcn_perm(quad_swap<0x4E>(hi), hi, sel2);
             S += static_cast<int>(quad_swap<0xB1>(static_cast<uint32_t>(S)));
             S += static_cast<int>(quad_swap<0x4E>(static_cast<uint32_t>(S)));
-            const int word = c >> 2;  // word of the round: block word / 4, word word % 4
+            const int word = c >> 2;  // 32-input word of the round: block word / 4, its word word % 4
             uint32_t* dst = &s_act[(word >> 2) * BSTR + 8 * (word & 3)];
             dst[pl] = lo;
             dst[pl + 4] = hi;
