@@ -467,6 +467,11 @@ __global__ __launch_bounds__(256) void gemv_sign_kernel(const uint8_t* __restric
                 // wait for them) after the barrier, in block order
                 uint32_t words[4] = {wv[bb][p].x, wv[bb][p].y, wv[bb][p].z, wv[bb][p].w};
                 asm volatile("" : "+v"(words[0]), "+v"(words[1]), "+v"(words[2]), "+v"(words[3]));
+                // the block's 32 table reads first, then the adds (same order
+                // as reading and adding in turn): the compiler then keeps
+                // more reads in flight per wait than it does when each read
+                // feeds its add at once (6.24 -> 6.10 us at 11008x4096)
+                float tv[32];
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
                     const uint32_t w4 = words[w] << 2;   // nibble 2j in bits 2..5 of byte j
@@ -476,9 +481,15 @@ __global__ __launch_bounds__(256) void gemv_sign_kernel(const uint8_t* __restric
                         const int c = bb * 32 + w * 8 + 2 * j;
                         const uint32_t a0 = nib_addr(w4, j);
                         const uint32_t a1 = nib_addr(w2, j);
-                        acc[p] += *reinterpret_cast<const float*>(lut_bytes + a0 + ((c * P + p) * 64));
-                        acc2[p] += *reinterpret_cast<const float*>(lut_bytes + a1 + (((c + 1) * P + p) * 64));
+                        tv[w * 8 + 2 * j] = *reinterpret_cast<const float*>(lut_bytes + a0 + ((c * P + p) * 64));
+                        tv[w * 8 + 2 * j + 1] =
+                            *reinterpret_cast<const float*>(lut_bytes + a1 + (((c + 1) * P + p) * 64));
                     }
+                }
+#pragma unroll
+                for (int i = 0; i < 32; i += 2) {
+                    acc[p] += tv[i];
+                    acc2[p] += tv[i + 1];
                 }
             }
 #pragma unroll
