@@ -888,11 +888,25 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
                 // it, above the barrier, ahead of the whole weight stream.
                 uint32_t cw = coef[j];
                 asm volatile("" : "+v"(cw));
+                // ternary and W2A8: the block's 8 activation-plane reads are
+                // issued together ahead of the popcounts (one LDS wait instead
+                // of four; W2A8 11008x4096 5.18 -> 5.12 us).  Not for HGF and
+                // BVSR4, whose extra registers cost more than the wait (BVSR
+                // 28672x8192 30.4 -> 31.5 us).
+                constexpr bool HOIST = FMT == BITQ_TERNARY || FMT == BITQ_W2A8;
+                uint4 xq[4][2];
+                if (HOIST) {
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        xq[w][0] = *reinterpret_cast<const uint4*>(xa + 8 * w);
+                        xq[w][1] = *reinterpret_cast<const uint4*>(xa + 8 * w + 4);
+                    }
+                }
                 if (TERN) {
 #pragma unroll
                     for (int w = 0; w < 4; ++w) {
-                        const uint4 x0 = *reinterpret_cast<const uint4*>(xa + 8 * w);
-                        const uint4 x1 = *reinterpret_cast<const uint4*>(xa + 8 * w + 4);
+                        const uint4 x0 = HOIST ? xq[w][0] : *reinterpret_cast<const uint4*>(xa + 8 * w);
+                        const uint4 x1 = HOIST ? xq[w][1] : *reinterpret_cast<const uint4*>(xa + 8 * w + 4);
                         const uint32_t xj[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
                         const uint32_t wp = (&wv[j][0].x)[w], wm = (&wv[j][1].x)[w];
 #pragma unroll
@@ -909,8 +923,8 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
                         for (int jj = 0; jj < 8; ++jj) a[i][jj] = 0;
 #pragma unroll
                     for (int w = 0; w < 4; ++w) {
-                        const uint4 x0 = *reinterpret_cast<const uint4*>(xa + 8 * w);
-                        const uint4 x1 = *reinterpret_cast<const uint4*>(xa + 8 * w + 4);
+                        const uint4 x0 = xq[w][0];
+                        const uint4 x1 = xq[w][1];
                         const uint32_t xj[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
                         const uint32_t w0 = (&wv[j][0].x)[w], w1 = (&wv[j][1].x)[w];
 #pragma unroll
