@@ -116,6 +116,9 @@ def _check(desc, bd, ref, xs, xf, rows=None):
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("fmt,N,K", [
+    (bq.TERNARY, 1, 32),        # one row, one 32-input word
+    (bq.W2A8, 1, 128),          # one row, one group
+    (bq.BVSR4, 3, 32),
     (bq.TERNARY, 70, 224),      # ragged k: the last block is partial
     (bq.TERNARY, 4096, 4096),
     (bq.TERNARY, 16448, 512),   # 16 rows per workgroup
