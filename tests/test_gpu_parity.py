@@ -339,9 +339,11 @@ def test_w2a8_batch_invariance_and_determinism():
     y16a = run_gemv(desc, bd, act16, bq.DT_ACT, 16, ws=ws)
     y16b = run_gemv(desc, bd, act16, bq.DT_ACT, 16, ws=ws)
     assert np.array_equal(y16a.view(np.uint32), y16b.view(np.uint32)), "run-to-run"
-    # M >= 2 runs on the matrix cores: a token gets the same bits whatever the
-    # batch and its place in it (M = 1 runs the VALU kernel: its integer
-    # partials are the same, y agrees within the tolerance)
+    # a token gets the same bits whatever the batch and its place in it: M =
+    # 16 and 40 run on the matrix cores, M = 2 on the VALU kernel (another
+    # fp32 order, but on this layer's data the group terms delta (A - z S)
+    # share one quantum and every partial sum is exact, so the bits agree);
+    # the integer partials of M = 1 equal those of M = 16
     for m in (0, 9, 15):
         sub = np.ascontiguousarray(xs[[(m + 5) % 16, m]])
         act2, _ = quantize_act_dev(sub, 2, K)
