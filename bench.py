@@ -56,9 +56,9 @@ KERNEL_SRC = os.path.join(ROOT, "bit_plane_gemv_amd", "csrc", "bitq_kernels.hip"
 # for the kernel source it was measured on (first 16 hex digits of the
 # sha256 of bitq_kernels.hip); otherwise traffic is reported as null.
 MEASURED_TRAFFIC = {
-    "rabit": {"kernels_sha256_16": "f7fba622fe51c243", "bytes_per_launch": 13451264},
-    "w2a8": {"kernels_sha256_16": "f7fba622fe51c243", "bytes_per_launch": 12827648},
-    "w2a8+fuse": {"kernels_sha256_16": "f7fba622fe51c243", "bytes_per_launch": 12880896},
+    "rabit": {"kernels_sha256_16": "bdb103df4f0f03f2", "bytes_per_launch": 13451264},
+    "w2a8": {"kernels_sha256_16": "bdb103df4f0f03f2", "bytes_per_launch": 12829696},
+    "w2a8+fuse": {"kernels_sha256_16": "bdb103df4f0f03f2", "bytes_per_launch": 12880896},
 }
 
 

@@ -1105,10 +1105,15 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
 // at a time, so one memory latency is paid per CH blocks: a wave's time is
 // about (its blocks / CH) latencies, which is why the launcher prefers many
 // short waves (RS 1, KW 8 or 16) and keeps q reuse (RS 4) for many tokens on
-// tall layers.  Per 128-group (W2A8, WNAM) the exact int32 sums go
-// through the group epilogue delta (A - z S128) in fp32; TERNARY keeps int32
-// sums over all of k.  The waves' partials are added in wave order through
-// LDS.
+// tall layers.  Per 128-group (W2A8, WNAM) the fp32 output takes delta
+// (A - z S128).  Except in the 64-row, 16-wave shape, the zero point is
+// folded into the A operand (code - z as a signed byte, row by row), so the
+// matrix cores return A - z S128 itself, exactly, and neither the group sums
+// S nor the subtraction are needed (the same value, and the same fp32 bits,
+// as delta (A - z S) computed from the exact A and S); the int32 output of
+// BITQ_F_ACC_INT32 keeps the unshifted A.
+// TERNARY keeps int32 sums over all of k.  The waves' partials are added in
+// wave order through LDS.
 typedef int v4i32_t __attribute__((ext_vector_type(4)));
 
 // Bits 4j .. 4j + 3 of v moved to bit 0 of bytes 0..3 (nibble times
@@ -1135,12 +1140,13 @@ __device__ __forceinline__ uint32_t codes4(const uint32_t (&w)[P], int lo, int j
 }
 
 // Everything one wave reads for one 128-input block.
-template <int P, int RS, int TT, bool GRP>
+template <int P, int RS, int TT, bool GRP, bool FOLD>
 struct MfmaBlock {
     uint32_t wp[RS][P];  // plane word g of rows 16 R + li
     v4i32_t qv[2][TT];   // q operands of the two k steps
     uint4 cz[GRP ? RS : 1];
-    int4 s4[GRP ? TT : 1];
+    uint32_t zr[FOLD ? RS : 1];          // coefficient word of row 16 R + li (its zero point)
+    int4 s4[GRP && !FOLD ? TT : 1];      // group sums (zero point not folded)
 };
 
 template <int FMT, int P, bool ACC, int TT, int RS, int KW, int CH>
@@ -1149,7 +1155,12 @@ __global__ __launch_bounds__(64 * KW) void gemm_mfma_kernel(const uint8_t* __res
                                                             size_t act_off_q, size_t act_off_d, int M, int N,
                                                             int Tb, float* __restrict__ y) {
     constexpr bool GRP = FMT != BITQ_TERNARY;  // per-128-group epilogue (W2A8, WNAM)
-    constexpr bool LOADC = GRP && !ACC;        // coefficients and group sums needed
+    constexpr bool LOADC = GRP && !ACC;        // coefficients needed
+    // zero point folded into the codes; not in the 64-row, 16-wave shape
+    // (8-16 tokens on tall layers), where the extra per-row coefficient
+    // loads cost more than the saved epilogue (W2A8 11008x4096, M = 8:
+    // 11.4 -> 11.9 us folded)
+    constexpr bool FOLD = LOADC && !(RS == 4 && KW == 16);
     // waves 1..KW-1 hand their partials to wave 0: RS row sub-tiles x TT
     // token tiles x 4 values per lane
     constexpr int NV = RS * TT * 4;
@@ -1181,7 +1192,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_mfma_kernel(const uint8_t* __res
             for (int i = 0; i < 4; ++i) yacc[R][tt][i] = 0.0f;
         }
 
-    auto load = [&](MfmaBlock<P, RS, TT, GRP>& L, int b) __attribute__((always_inline)) {
+    auto load = [&](MfmaBlock<P, RS, TT, GRP, FOLD>& L, int b) __attribute__((always_inline)) {
 #pragma unroll
         for (int R = 0; R < RS; ++R)
 #pragma unroll
@@ -1196,22 +1207,35 @@ __global__ __launch_bounds__(64 * KW) void gemm_mfma_kernel(const uint8_t* __res
                                                                 32 * g + 16 * s);
         if constexpr (LOADC) {
 #pragma unroll
-            for (int R = 0; R < RS; ++R)
+            for (int R = 0; R < RS; ++R) {
                 L.cz[R] = *reinterpret_cast<const uint4*>(tile_coef + b * 64 + r0 + 16 * R + 4 * g);
+                if (FOLD) L.zr[R] = tile_coef[b * 64 + r0 + 16 * R + li];
+            }
+            if (!FOLD) {
 #pragma unroll
-            for (int tt = 0; tt < TT; ++tt)
-                L.s4[tt] = *reinterpret_cast<const int4*>(S + static_cast<size_t>(mrow[tt]) * Kw + 4 * b);
+                for (int tt = 0; tt < TT; ++tt)
+                    L.s4[tt] = *reinterpret_cast<const int4*>(S + static_cast<size_t>(mrow[tt]) * Kw + 4 * b);
+            }
         }
     };
 
-    auto compute = [&](const MfmaBlock<P, RS, TT, GRP>& L, int b) __attribute__((always_inline)) {
+    auto compute = [&](const MfmaBlock<P, RS, TT, GRP, FOLD>& L, int b) __attribute__((always_inline)) {
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
 #pragma unroll
             for (int R = 0; R < RS; ++R) {
                 v4i32_t a;
+                if constexpr (FOLD) {
+                    // codes minus the row's zero point, as signed bytes: (c | 0x80) - z
+                    // cannot borrow (c, z < 16), and ^ 0x80 turns c - z + 128 into c - z
+                    const uint32_t zb = static_cast<uint32_t>(f16_bits_to_f32(L.zr[R] >> 16)) * 0x01010101u;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) a[j] = static_cast<int>(codes4<FMT, P>(L.wp[R], 16 * s, j));
+                    for (int j = 0; j < 4; ++j)
+                        a[j] = static_cast<int>(((codes4<FMT, P>(L.wp[R], 16 * s, j) | 0x80808080u) - zb) ^ 0x80808080u);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) a[j] = static_cast<int>(codes4<FMT, P>(L.wp[R], 16 * s, j));
+                }
 #pragma unroll
                 for (int tt = 0; tt < TT; ++tt)
                     acc[R][tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, L.qv[s][tt], acc[R][tt], 0, 0, 0);
@@ -1232,14 +1256,20 @@ __global__ __launch_bounds__(64 * KW) void gemm_mfma_kernel(const uint8_t* __res
             } else {
 #pragma unroll
                 for (int tt = 0; tt < TT; ++tt) {
-                    const float S128 = static_cast<float>((L.s4[tt].x + L.s4[tt].y) + (L.s4[tt].z + L.s4[tt].w));
+                    const float S128 =
+                        FOLD ? 0.0f : static_cast<float>((L.s4[tt].x + L.s4[tt].y) + (L.s4[tt].z + L.s4[tt].w));
 #pragma unroll
                     for (int R = 0; R < RS; ++R) {
                         const uint32_t c[4] = {L.cz[R].x, L.cz[R].y, L.cz[R].z, L.cz[R].w};
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            const float delta = f16_bits_to_f32(c[i]), z = f16_bits_to_f32(c[i] >> 16);
-                            yacc[R][tt][i] += delta * (static_cast<float>(acc[R][tt][i]) - z * S128);
+                            const float delta = f16_bits_to_f32(c[i]);
+                            if (FOLD) {
+                                yacc[R][tt][i] += delta * static_cast<float>(acc[R][tt][i]);  // acc = A - z S
+                            } else {
+                                const float z = f16_bits_to_f32(c[i] >> 16);
+                                yacc[R][tt][i] += delta * (static_cast<float>(acc[R][tt][i]) - z * S128);
+                            }
                         }
                     }
                 }
@@ -1254,7 +1284,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_mfma_kernel(const uint8_t* __res
     for (int c0 = bbeg; c0 < bend; c0 += CH) {
         // the chunk's loads are issued together (surplus slots re-read the
         // last block and are skipped below)
-        MfmaBlock<P, RS, TT, GRP> L[CH];
+        MfmaBlock<P, RS, TT, GRP, FOLD> L[CH];
 #pragma unroll
         for (int i = 0; i < CH; ++i) load(L[i], min(c0 + i, bend - 1));
 #pragma unroll
