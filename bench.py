@@ -5,31 +5,39 @@
 
 A step is one batch-1 GEMV y = W^ x over one Llama-2-7B gate/up layer
 (11008 x 4096): the RaBiT 2-path residual-binary layer by default (the
-workload the headline metric is quoted on), or the W2A8 bit-plane layer
-(activation quantizer + AND+popcount GEMV) with --workload w2a8; the other
-workloads are listed in WORKLOADS.  --tokens M (integer formats, 2..64) runs
-the small-M path instead: M tokens per step, each weight read once, and the
-roofline is then the contraction's (int8 matrix cores from 4 tokens on,
-else VALU lane-operations).
+workload the headline metric is quoted on).  The default run also measures
+the same layer in the W2A8 bit-plane format (the activation quantizer plus
+the AND+popcount GEMV, and the GEMV with the quantizer fused into it) and
+reports it under the key "w2a8".  --workload picks another layer (the table
+WORKLOADS); --tokens M (integer formats, 2..64) runs the small-M path
+instead: M tokens per step, each weight read once, and the roofline is then
+the contraction's (int8 matrix cores from the library's switch on, else VALU
+lane-operations).
 
 Measurement:
   * The packed layer is replicated into >= 1 GiB of distinct device copies and
     step i reads copy i mod C, so every step streams its weights from HBM
     (the 256 MB Infinity Cache and the L2s cannot hold the rotation).
   * Inputs are resident in HBM before timing starts.  The K timed steps are
-    captured once into a HIP graph and replayed, so host launch overhead is
-    not part of the measurement; HIP events recorded on the launch stream
-    bracket the replay.
-  * value = packed weight bytes x K / elapsed (GB/s); roofline.achieved is the
-    same algorithmic byte count divided by the per-launch time of the GEMV
-    kernel measured the same way (equal to ms_per_step when the step is that
-    single kernel).
+    captured once into a HIP graph.  A bounded wait kernel is queued ahead of
+    the replay, so the GPU starts the first step only once the host has
+    submitted the graph; HIP events recorded on the launch stream bracket the
+    replay.  The measured time is GPU time of the K steps.
+  * value = packed weight bytes x K / elapsed (GB/s).  roofline.achieved is
+    the algorithmic bytes of the product kernel divided by its per-launch time,
+    measured the same way on a graph of that kernel alone.
+  * roofline.floor_us and empty_us come from two context kernels of the
+    library, timed the same way on the same rotation: one that only streams
+    the same bytes with the product kernel's grid (and writes one fp32 per
+    output row), and one that does nothing with that grid.  frac_of_floor =
+    floor_us / kernel_us.
   * cpu_baseline: the CPU oracle (explicit fp64 dequantization + dot product)
     on the same layer, timed on the host for a bounded number of repetitions.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -48,24 +56,28 @@ INT8_MFMA_PEAK_TOPS = 5000.0      # MI355X dense int8 matrix-core peak
 VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 MFMA_MIN_TOKENS = 4               # the library's switch to the matrix-core kernel
 ROTATE_BYTES = 1 << 30
-KERNEL_SRC = os.path.join(ROOT, "bit_plane_gemv_amd", "csrc", "bitq_kernels.hip")
+CSRC = os.path.join(ROOT, "bit_plane_gemv_amd", "csrc")
+METRIC = "packed-weight GB/s & % HBM peak, bit-plane GEMV 11008x4096 M=1; us/layer"
 
-# HBM bytes moved per launch of the GEMV kernel, from rocprofv3 counter runs
+# HBM bytes moved per launch of a product kernel, from rocprofv3 counter runs
 # (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0; factors calibrated on a plain copy
 # kernel of known size; profiles/ holds the runs).  Each entry is valid only
 # for the kernel source it was measured on (first 16 hex digits of the
-# sha256 of bitq_kernels.hip); otherwise traffic is reported as null.
-MEASURED_TRAFFIC = {
-    "rabit": {"kernels_sha256_16": "bdb103df4f0f03f2", "bytes_per_launch": 13451264},
-    "w2a8": {"kernels_sha256_16": "bdb103df4f0f03f2", "bytes_per_launch": 12829696},
-    "w2a8+fuse": {"kernels_sha256_16": "bdb103df4f0f03f2", "bytes_per_launch": 12880896},
-}
+# sha256 of that source file); otherwise traffic is reported as null.
+MEASURED_TRAFFIC: dict = {}
 
 
-def kernels_sha() -> str:
-    import hashlib
-    with open(KERNEL_SRC, "rb") as f:
+def source_sha(name: str) -> str:
+    with open(os.path.join(CSRC, name), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(key: str):
+    mt = MEASURED_TRAFFIC.get(key)
+    if mt is None or mt["sha16"] != source_sha(mt["source"]):
+        return None
+    return mt
+
 
 # Algorithmic packed bytes of one layer (planes + coefficients), by format.
 # HGF: the ternary planes and gamma, A (read by the activation step) and B
@@ -124,6 +136,34 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def host_description() -> dict:
+    """The host the CPU baseline ran on: CPU model, logical CPUs, CPUs in
+    this process's affinity mask, and the BLAS thread pools."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    blas = []
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [{"api": i.get("user_api"), "lib": i.get("internal_api"), "threads": i.get("num_threads")}
+                for i in threadpool_info()]
+    except Exception:
+        pass
+    return {"cpu_model": model, "cpu_count": os.cpu_count(), "affinity_cpus": affinity, "blas": blas,
+            "env_threads": {k: os.environ[k] for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
+                            if k in os.environ}}
+
+
 def cpu_baseline(wl: dict, budget_s: float = 12.0) -> dict:
     """The oracle as it stands, timed on the host: explicit fp64 dequantization
     and dot product for one GEMV of the workload layer, repeated until about
@@ -134,6 +174,7 @@ def cpu_baseline(wl: dict, budget_s: float = 12.0) -> dict:
     data = wl.get("data", fmt)
     W = synth.weights(data, si, N, K)
     xs, xf = synth.activations(data, si, 1, K)
+    blas_gemm = True   # the fp64 dot is a BLAS matmul (threads = the BLAS pool)
     if fmt == "rabit":
         # the GEMV step only: the logical form is built once, outside the timing
         B, g, h = ow.quantize_rabit(W)
@@ -186,11 +227,10 @@ def cpu_baseline(wl: dict, budget_s: float = 12.0) -> dict:
         what = "oracle act quantize + gemv_bvsr (fp64 dequant + dot)"
     else:
         raise ValueError(fmt)
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
+    host = host_description()
+    threads = max([b["threads"] or 1 for b in host["blas"]] or [1])
+    if host["affinity_cpus"]:
+        threads = min(threads, host["affinity_cpus"])
     times = []
     t_all = time.perf_counter()
     while True:
@@ -200,11 +240,218 @@ def cpu_baseline(wl: dict, budget_s: float = 12.0) -> dict:
         if time.perf_counter() - t_all > budget_s or len(times) >= 50:
             break
     med = float(np.median(times))
-    return {"value": packed_bytes(fmt, N, K, wl.get("planes", 2), wl.get("rank", 0)) / med / 1e9, "unit": "GB/s",
-            "cores": int(threads),
+    return {"value": round(packed_bytes(fmt, N, K, wl.get("planes", 2), wl.get("rank", 0)) / med / 1e9, 4),
+            "unit": "GB/s",
+            "cores": int(threads) if blas_gemm else 1,
             "kind": "oracle",
-            "sample": f"{what}, {fmt} {N}x{K} M=1, {len(times)} runs, median {med * 1e3:.1f} ms "
-                      f"per GEMV; host has {os.cpu_count()} cpus"}
+            "sample": f"{what}, {fmt} {N}x{K} M=1, one GEMV per run, {len(times)} runs in "
+                      f"{time.perf_counter() - t_all:.1f} s, median {med * 1e3:.1f} ms per GEMV",
+            "us_per_gemv": round(med * 1e6, 1),
+            "host": host}
+
+
+class Timer:
+    """Per-step GPU time of a sequence of K steps captured in one HIP graph.
+
+    The graph is replayed once untimed.  For the timed replay a bounded wait
+    kernel (bitq_ctx_spin) is queued first, long enough to cover the host's
+    submission of the graph, so the first step starts right after the start
+    event and the events measure GPU time only."""
+
+    def __init__(self, torch, bq):
+        self.torch, self.bq = torch, bq
+
+    def per_step_ms(self, step, K: int, warmup: int) -> float:
+        torch, bq = self.torch, self.bq
+        for i in range(warmup):
+            step(i, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                st = torch.cuda.current_stream()
+                for i in range(K):
+                    step(i, st)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()                          # untimed; also measures the host submission time
+        host_us = (time.perf_counter() - t0) * 1e6
+        torch.cuda.synchronize()
+        spin_us = int(min(10000, max(200, 2 * host_us + 100)))
+        stream = torch.cuda.current_stream()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        bq.ctx_spin(spin_us, stream=stream)
+        ev0.record(stream)
+        g.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        del g
+        return ev0.elapsed_time(ev1) / K
+
+
+class Layer:
+    """One workload layer on the device: the rotation of packed copies, the
+    activations and the buffers of its steps."""
+
+    def __init__(self, torch, bq, synth, wl: dict, M: int):
+        self.wl, self.M = wl, M
+        self.fmt, self.N, self.K, si = wl["fmt"], wl["N"], wl["K"], wl["shape_idx"]
+        N, K = self.N, self.K
+        dev = torch.device("cuda:0")
+        self.bq = bq
+        t0 = time.perf_counter()
+        data = wl.get("data", self.fmt)
+        self.data = data
+        W = synth.weights(data, si, N, K)
+        self.desc = bq.wdesc(self.fmt, N, K, planes=wl.get("planes"), abits=wl.get("abits"), rank=wl.get("rank"))
+        self.abits = wl.get("abits", 8)
+        self.hgf = self.fmt == "hgf"
+        if self.hgf:
+            Ab, Bb, alpha = synth.lora_params(si, N, K, wl["rank"])
+            blob = bq.quantize_weights_hgf(self.desc, W, Ab, Bb, alpha)
+        else:
+            blob = bq.quantize_weights(self.desc, W, bit_balance=bool(wl.get("bit_balance")))
+        log(f"quantized+packed {self.fmt} {N}x{K} in {time.perf_counter() - t0:.1f}s, blob {blob.nbytes} B")
+        self.alg_bytes = packed_bytes(self.fmt, N, K, wl.get("planes", 2), wl.get("rank", 0))
+        self.gemv_bytes = kernel_bytes(wl)
+        self.copies = max(2, math.ceil(ROTATE_BYTES / blob.nbytes))
+        base = torch.empty(blob.nbytes, dtype=torch.uint8, device=dev)
+        base.copy_(torch.from_numpy(blob))
+        self.stride = (blob.nbytes + 4095) // 4096 * 4096
+        self.pool = torch.empty(self.copies * self.stride, dtype=torch.uint8, device=dev)
+        for c in range(self.copies):
+            self.pool[c * self.stride:c * self.stride + blob.nbytes].copy_(base)
+        del base
+        self.blobs = [self.pool[c * self.stride:c * self.stride + blob.nbytes] for c in range(self.copies)]
+        xs, _ = synth.activations(data, si, M, K)
+        if xs.dtype == np.float32:      # fp32 activations (the sign workloads' inputs)
+            self.x, self.x_dt = torch.from_numpy(np.ascontiguousarray(xs)).to(dev), bq.DT_F32
+        else:                           # bf16 bit patterns
+            self.x, self.x_dt = torch.from_numpy(np.ascontiguousarray(xs).view(np.int16)).to(dev), bq.DT_BF16
+        self.y = torch.empty(M * N, dtype=torch.float32, device=dev)
+        self.ws = torch.zeros(bq.workspace_size(self.desc, M), dtype=torch.uint8, device=dev)
+        self.binary = bool(wl.get("binary"))
+        self.integer = self.fmt in ("ternary", "w2a8", "bvsr", "wnam", "hgf") or self.binary
+        if self.binary:
+            self.act = torch.zeros(bq.binact_size(M, K), dtype=torch.uint8, device=dev)
+        elif self.hgf:
+            act_bytes, act_ws_bytes = bq.hgf_act_size(self.desc, M)
+            self.act = torch.zeros(act_bytes, dtype=torch.uint8, device=dev)
+            self.act_ws = torch.zeros(act_ws_bytes, dtype=torch.uint8, device=dev)
+        else:
+            self.act = torch.zeros(bq.act_size(M, K), dtype=torch.uint8, device=dev) if self.integer else None
+        self.act_dt = bq.DT_BINARY if self.binary else bq.DT_ACT
+        self.seeds = {"W": synth.seed_for(synth.CONFIGS[data]["cfg"], si, synth.ROLE_W),
+                      "x": synth.seed_for(synth.CONFIGS[data]["cfg"], si, synth.ROLE_X)}
+
+    # ---- the pieces of a step
+    def activation_step(self, st):
+        bq = self.bq
+        if self.binary:
+            bq.binarize_act(self.x, self.x_dt, self.M, self.K, self.act, stream=st)
+        elif self.hgf:
+            bq.quantize_act_hgf(self.desc, self.blobs[0], self.x, self.x_dt, self.M, self.act, self.act_ws, stream=st)
+        else:
+            bq.quantize_act(self.x, self.x_dt, self.M, self.K, self.act, stream=st, abits=self.abits)
+
+    def product(self, i, st):
+        """The GEMV (one token) or the small-M GEMM (M tokens) on copy i."""
+        bq, w = self.bq, self.blobs[i % self.copies]
+        if not self.integer:
+            bq.gemv(self.desc, w, self.x, self.x_dt, self.y, self.ws, stream=st)
+        elif self.M == 1:
+            bq.gemv(self.desc, w, self.act, self.act_dt, self.y, None if self.binary else self.ws, stream=st)
+        else:
+            bq.gemm_smallM(self.desc, w, self.act, self.M, self.y, None if self.binary else self.ws, stream=st)
+
+    def step(self, i, st):
+        if self.integer:
+            if self.hgf:   # the activation step reads A from the copy this step uses
+                self.bq.quantize_act_hgf(self.desc, self.blobs[i % self.copies], self.x, self.x_dt, self.M,
+                                         self.act, self.act_ws, stream=st)
+            else:
+                self.activation_step(st)
+        self.product(i, st)
+
+    def fused_step(self, i, st):
+        self.bq.gemv(self.desc, self.blobs[i % self.copies], self.x, self.x_dt, self.y, None,
+                     flags=self.bq.F_FUSE_QUANT, stream=st)
+
+    def context_floor(self, timer: Timer, K: int, warmup: int, nbytes: int, fused: bool = False) -> dict:
+        """Per-launch time of the stream-read and empty context kernels with
+        the product kernel's grid, over the same rotation."""
+        bq = self.bq
+        flags = bq.F_FUSE_QUANT if fused else 0
+        x_dt = self.x_dt if (fused or not self.integer) else self.act_dt
+        grid, block = bq.ctx_launch_shape(self.desc, self.M, x_dt, flags)
+        n16 = nbytes // 16 * 16
+        floor_ms = timer.per_step_ms(
+            lambda i, st: bq.ctx_stream(self.blobs[i % self.copies], n16, grid, self.y, self.N, stream=st),
+            K, warmup)
+        empty_ms = timer.per_step_ms(lambda i, st: bq.ctx_empty(grid, stream=st), K, warmup)
+        return {"floor_us": round(floor_ms * 1e3, 3), "empty_us": round(empty_ms * 1e3, 3),
+                "floor_bytes": n16, "grid": grid, "block": block}
+
+
+def hbm_roofline(nbytes: int, us: float, kernel: str, ctx: dict | None, traffic_key: str | None) -> dict:
+    achieved = nbytes / (us * 1e-6) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "traffic_bytes_per_launch": None,
+            "kernel": kernel, "kernel_us": round(us, 3), "alg_bytes": nbytes}
+    mt = measured_traffic(traffic_key) if traffic_key else None
+    if mt is not None:
+        roof["traffic"] = round(mt["bytes_per_launch"] / (us * 1e-6) / 1e9, 2)
+        roof["traffic_bytes_per_launch"] = mt["bytes_per_launch"]
+    if ctx is not None:
+        roof.update(ctx)
+        roof["frac_of_floor"] = round(ctx["floor_us"] / us, 4)
+    return roof
+
+
+def product_kernel_name(layer: Layer, mfma: bool) -> str:
+    if layer.binary:
+        return "gemv_xnor_kernel"
+    if layer.fmt in ("rabit", "sign"):
+        return "gemv_sign_kernel"
+    return "gemm_mfma_kernel" if mfma else "gemv_bits_nr_kernel"
+
+
+def w2a8_headline(torch, bq, synth, timer: Timer, K_steps: int, warmup: int, cpu: bool) -> dict:
+    """The W2A8 11008x4096 M=1 layer: GEMV kernel alone, the two-launch step
+    (quantizer + GEMV) and the fused step, each with its roofline."""
+    wl = WORKLOADS["w2a8"]
+    L = Layer(torch, bq, synth, wl, 1)
+    gemv_ms = timer.per_step_ms(L.product, K_steps, warmup)
+    step_ms = timer.per_step_ms(L.step, K_steps, warmup)
+    fused_ms = timer.per_step_ms(L.fused_step, K_steps, warmup)
+    ctx = L.context_floor(timer, K_steps, warmup, L.gemv_bytes)
+    ctx_f = L.context_floor(timer, K_steps, warmup, L.gemv_bytes, fused=True)
+    out = {
+        "workload": f"w2a8 {L.N}x{L.K} M=1 (2-bit asymmetric weights, group 128, int8 per-token activations)",
+        "packed_bytes": L.alg_bytes,
+        "gemv": {"us": round(gemv_ms * 1e3, 3), "GB/s": round(L.alg_bytes / (gemv_ms * 1e-3) / 1e9, 2),
+                 "roofline": hbm_roofline(L.gemv_bytes, gemv_ms * 1e3, "gemv_bits_nr_kernel", ctx, "w2a8")},
+        "step_two_launch": {"us": round(step_ms * 1e3, 3),
+                            "GB/s": round(L.alg_bytes / (step_ms * 1e-3) / 1e9, 2),
+                            "kernels": ["quant_act_kernel", "gemv_bits_nr_kernel"]},
+        "fused_step": {"us": round(fused_ms * 1e3, 3), "GB/s": round(L.alg_bytes / (fused_ms * 1e-3) / 1e9, 2),
+                       "roofline": hbm_roofline(L.gemv_bytes, fused_ms * 1e3, "gemv_bits_nr_kernel (fused quantizer)",
+                                                ctx_f, "w2a8+fuse")},
+        "seeds": L.seeds, "rotating_copies": L.copies,
+    }
+    del L
+    torch.cuda.empty_cache()
+    if cpu:
+        try:
+            out["cpu_baseline"] = cpu_baseline(wl, budget_s=8.0)
+        except Exception as e:  # reported, never fatal for the GPU figure
+            out["cpu_baseline"] = {"error": repr(e)}
+    return out
 
 
 def main():
@@ -214,7 +461,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="rabit", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-graph", action="store_true", help="launch every step from the host")
+    ap.add_argument("--no-second", action="store_true", help="skip the W2A8 headline of the default run")
+    ap.add_argument("--no-context", action="store_true", help="skip the context kernels (floor, empty)")
     ap.add_argument("--tokens", type=int, default=1,
                     help="tokens per step (integer formats: 2..64 run the small-M path)")
     ap.add_argument("--fuse", action="store_true",
@@ -225,13 +473,8 @@ def main():
         print("bench.py measures one GPU: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
-
-    import torch
-    import bit_plane_gemv_amd as bq
-    import synth
-
     wl = WORKLOADS[args.workload]
-    fmt, N, K, si = wl["fmt"], wl["N"], wl["K"], wl["shape_idx"]
+    fmt = wl["fmt"]
     M = args.tokens
     if M != 1 and (fmt in ("rabit",) or (fmt == "sign" and not wl.get("binary")) or not 1 <= M <= 64):
         print("--tokens > 1 needs an integer-activation workload and at most 64 tokens", file=sys.stderr)
@@ -240,165 +483,58 @@ def main():
     if fuse and (M != 1 or fmt not in ("ternary", "w2a8", "bvsr", "wnam") or wl.get("binary")):
         print("--fuse needs one token and a TERNARY/W2A8/BVSR4/WNAM workload", file=sys.stderr)
         sys.exit(2)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
 
-    # ---- weights: library quantizer + packer (offline, untimed)
-    t0 = time.perf_counter()
-    data = wl.get("data", fmt)
-    W = synth.weights(data, si, N, K)
-    desc = bq.wdesc(fmt, N, K, planes=wl.get("planes"), abits=wl.get("abits"), rank=wl.get("rank"))
-    abits = wl.get("abits", 8)
-    hgf = fmt == "hgf"
-    if hgf:
-        Ab, Bb, alpha = synth.lora_params(si, N, K, wl["rank"])
-        blob = bq.quantize_weights_hgf(desc, W, Ab, Bb, alpha)
-    else:
-        blob = bq.quantize_weights(desc, W, bit_balance=bool(wl.get("bit_balance")))
-    log(f"quantized+packed {fmt} {N}x{K} in {time.perf_counter() - t0:.1f}s, blob {blob.nbytes} B")
-    alg_bytes = packed_bytes(fmt, N, K, wl.get("planes", 2), wl.get("rank", 0))
-    gemv_bytes = kernel_bytes(wl)
-    copies = max(2, math.ceil(ROTATE_BYTES / blob.nbytes))
-    base = torch.empty(blob.nbytes, dtype=torch.uint8, device=dev)
-    base.copy_(torch.from_numpy(blob))
-    stride = (blob.nbytes + 4095) // 4096 * 4096
-    pool = torch.empty(copies * stride, dtype=torch.uint8, device=dev)
-    for c in range(copies):
-        pool[c * stride:c * stride + blob.nbytes].copy_(base)
-    del base
-    blobs = [pool[c * stride:c * stride + blob.nbytes] for c in range(copies)]
+    import torch
+    import bit_plane_gemv_amd as bq
+    import synth
 
-    # ---- activations / outputs / workspace
-    xs, xf = synth.activations(data, si, M, K)
-    if xs.dtype == np.float32:      # fp32 activations (the sign workloads' inputs)
-        x, x_dt = torch.from_numpy(np.ascontiguousarray(xs)).to(dev), bq.DT_F32
-    else:                           # bf16 bit patterns
-        x, x_dt = torch.from_numpy(np.ascontiguousarray(xs).view(np.int16)).to(dev), bq.DT_BF16
-    y = torch.empty(M * N, dtype=torch.float32, device=dev)
-    ws = torch.zeros(bq.workspace_size(desc, M), dtype=torch.uint8, device=dev)
-    binary = bool(wl.get("binary"))
-    integer = fmt in ("ternary", "w2a8", "bvsr", "wnam", "hgf") or binary
-    if binary:
-        act = torch.zeros(bq.binact_size(M, K), dtype=torch.uint8, device=dev)
-    elif hgf:
-        act_bytes, act_ws_bytes = bq.hgf_act_size(desc, M)
-        act = torch.zeros(act_bytes, dtype=torch.uint8, device=dev)
-        act_ws = torch.zeros(act_ws_bytes, dtype=torch.uint8, device=dev)
-    else:
-        act = torch.zeros(bq.act_size(M, K), dtype=torch.uint8, device=dev) if integer else None
-    act_dt = bq.DT_BINARY if binary else bq.DT_ACT
-    stream = torch.cuda.current_stream()
-
-    def product(w, a, a_dt, ws_, st):
-        """The GEMV (one token) or the small-M GEMM (M tokens)."""
-        if M == 1:
-            bq.gemv(desc, w, a, a_dt, y, ws_, stream=st)
-        else:
-            bq.gemm_smallM(desc, w, a, M, y, ws_, stream=st)
-
-    def step(i):
-        w = blobs[i % copies]
-        if binary:
-            bq.binarize_act(x, x_dt, M, K, act, stream=stream)
-            product(w, act, bq.DT_BINARY, None, stream)
-        elif hgf:
-            bq.quantize_act_hgf(desc, w, x, x_dt, M, act, act_ws, stream=stream)
-            product(w, act, bq.DT_ACT, None, stream)
-        elif fuse:
-            bq.gemv(desc, w, x, x_dt, y, None, flags=bq.F_FUSE_QUANT, stream=stream)
-        elif integer:
-            bq.quantize_act(x, x_dt, M, K, act, stream=stream, abits=abits)
-            product(w, act, bq.DT_ACT, ws, stream)
-        else:
-            bq.gemv(desc, w, x, x_dt, y, ws, stream=stream)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
+    torch.cuda.set_device(torch.device("cuda:0"))
+    timer = Timer(torch, bq)
+    L = Layer(torch, bq, synth, wl, M)
     K_steps = args.steps
-    graph = None
-    if not args.no_graph:
-        graph = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            with torch.cuda.graph(graph, stream=s):
-                stream = torch.cuda.current_stream()
-                for i in range(K_steps):
-                    step(i)
-        torch.cuda.current_stream().wait_stream(s)
-        stream = torch.cuda.current_stream()
-        graph.replay()                      # one untimed replay
-        torch.cuda.synchronize()
+    N, K = L.N, L.K
 
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    # ---- the timed steps (the contract's K steps)
+    step = L.fused_step if fuse else L.step
     t_wall = time.perf_counter()
-    ev0.record(stream)
-    if graph is not None:
-        graph.replay()
-    else:
-        for i in range(K_steps):
-            step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
+    ms_per_step = timer.per_step_ms(step, K_steps, args.warmup)
     wall = time.perf_counter() - t_wall
-    ms_total = ev0.elapsed_time(ev1)
-    ms_per_step = ms_total / K_steps
-    value = alg_bytes / (ms_per_step * 1e-3) / 1e9
+    value = L.alg_bytes / (ms_per_step * 1e-3) / 1e9
 
-    # per-launch time of the GEMV kernel alone (integer workloads also run the
-    # activation quantizer in each step): a graph of GEMV launches only
-    gemv_ms = ms_per_step
-    if integer and graph is not None and not fuse:
-        g2 = torch.cuda.CUDAGraph()
-        s2 = torch.cuda.Stream()
-        s2.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s2):
-            with torch.cuda.graph(g2, stream=s2):
-                st2 = torch.cuda.current_stream()
-                for i in range(K_steps):
-                    product(blobs[i % copies], act, act_dt, None if binary else ws, st2)
-        torch.cuda.current_stream().wait_stream(s2)
-        g2.replay()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(torch.cuda.current_stream())
-        g2.replay()
-        e1.record(torch.cuda.current_stream())
-        torch.cuda.synchronize()
-        gemv_ms = e0.elapsed_time(e1) / K_steps
-    achieved = gemv_bytes / (gemv_ms * 1e-3) / 1e9
-    roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    # ---- the product kernel alone (integer workloads also run an activation
+    #      step in each two-launch step)
+    kernel_ms = ms_per_step
+    if L.integer and not fuse:
+        kernel_ms = timer.per_step_ms(L.product, K_steps, args.warmup)
     mfma = M >= MFMA_MIN_TOKENS and fmt in ("ternary", "w2a8", "wnam")
+    kname = product_kernel_name(L, mfma) + (" (fused quantizer)" if fuse else "")
+    ctx = None if args.no_context else L.context_floor(timer, K_steps, args.warmup, L.gemv_bytes, fused=fuse)
+    traffic_key = (args.workload + ("+fuse" if fuse else "")) if M == 1 else None
+    roof = hbm_roofline(L.gemv_bytes, kernel_ms * 1e3, kname, ctx, traffic_key)
     if M > 1:
         # the small-M contraction: int8 ops (2 M N K) on the matrix cores, or,
         # on the VALU, the AND and popcount lane-operations of the bit planes
         # (2 per weight plane x activation plane x 32 weights x token)
+        hbm = roof
         if mfma:
-            tops = 2.0 * M * N * K / (gemv_ms * 1e-3) / 1e12
+            tops = 2.0 * M * N * K / (kernel_ms * 1e-3) / 1e12
             roof = {"bound": "mfma", "achieved": round(tops, 2), "peak": INT8_MFMA_PEAK_TOPS, "unit": "TOP/s",
                     "frac": round(tops / INT8_MFMA_PEAK_TOPS, 4)}
         else:
             wplanes = {"ternary": 2, "w2a8": 2, "bvsr": 4, "hgf": 2}.get(fmt, wl.get("planes", 1))
-            aplanes = 1 if binary else abits
+            aplanes = 1 if L.binary else L.abits
             ops = M * N * K * wplanes * aplanes * 2 / 32
-            tops = ops / (gemv_ms * 1e-3) / 1e12
+            tops = ops / (kernel_ms * 1e-3) / 1e12
             roof = {"bound": "alu", "achieved": round(tops, 2), "peak": round(VALU_PEAK_TOPS, 2),
                     "unit": "Tlane-op/s", "frac": round(tops / VALU_PEAK_TOPS, 4)}
-        roof["hbm_gbs"] = round(achieved, 2)
-        roof["hbm_frac"] = round(achieved / HBM_PEAK_GBS, 4)
-    traffic = None
-    mt = MEASURED_TRAFFIC.get(args.workload + ("+fuse" if fuse else "")) if M == 1 else None
-    if mt is not None and mt["kernels_sha256_16"] == kernels_sha():
-        traffic = round(mt["bytes_per_launch"] / (gemv_ms * 1e-3) / 1e9, 2)
+        roof.update({"kernel": kname, "kernel_us": hbm["kernel_us"], "hbm_gbs": hbm["achieved"],
+                     "hbm_frac": hbm["frac"], "traffic": None})
+        for k in ("floor_us", "empty_us", "frac_of_floor", "grid", "block"):
+            if k in hbm:
+                roof[k] = hbm[k]
 
     out = {
-        "metric": "packed-weight GB/s & % HBM peak, bit-plane GEMV 11008x4096 M=1; us/layer",
+        "metric": METRIC,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -410,25 +546,23 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if fmt == "rabit" or (fmt == "sign" and not binary) else "int32",
+        "dtype": "f32" if fmt == "rabit" or (fmt == "sign" and not L.binary) else "int32",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload} {N}x{K} M={M} ({'RaBiT 2-path residual binary, bf16 x' if fmt == 'rabit' else fmt})",
-                   "N": N, "K": K, "M": M, "format": fmt, "packed_bytes": alg_bytes,
-                   "seeds": {"W": synth.seed_for(synth.CONFIGS[data]["cfg"], si, synth.ROLE_W),
-                             "x": synth.seed_for(synth.CONFIGS[data]["cfg"], si, synth.ROLE_X)},
-                   "rotating_copies": copies, "rotating_bytes": copies * stride,
-                   "graph_replay": graph is not None, "host_wall_s": round(wall, 4),
-                   **({"weight_bits": wl["planes"], "act_bits": abits} if fmt == "wnam" else {}),
+        "config": {"workload": f"{args.workload} {N}x{K} M={M} "
+                               f"({'RaBiT 2-path residual binary, bf16 x' if fmt == 'rabit' else fmt})",
+                   "N": N, "K": K, "M": M, "format": fmt, "packed_bytes": L.alg_bytes, "seeds": L.seeds,
+                   "rotating_copies": L.copies, "rotating_bytes": L.copies * L.stride,
+                   "graph_replay": True, "host_wall_s": round(wall, 4),
+                   **({"weight_bits": wl["planes"], "act_bits": L.abits} if fmt == "wnam" else {}),
                    **({"fused_quantizer": True} if fuse else {}),
-                   **({"rank": wl["rank"], "gemv_kernel_bytes": gemv_bytes} if hgf else {})},
-        "roofline": {**roof, "traffic": traffic,
-                     "traffic_bytes_per_launch": mt["bytes_per_launch"] if traffic is not None else None,
-                     "kernel": ("gemv_xnor_kernel" if binary else
-                                "gemv_sign_kernel" if fmt in ("rabit", "sign") else
-                                "gemm_mfma_kernel" if mfma else "gemv_bits_nr_kernel"),
-                     "kernel_us": round(gemv_ms * 1e3, 3)},
+                   **({"rank": wl["rank"], "gemv_kernel_bytes": L.gemv_bytes} if L.hgf else {})},
+        "roofline": roof,
         "cpu_baseline": None,
     }
+    del L
+    torch.cuda.empty_cache()
+    if args.workload == "rabit" and M == 1 and not fuse and not args.no_second:
+        out["w2a8"] = w2a8_headline(torch, bq, synth, timer, K_steps, args.warmup, not args.no_cpu_baseline)
     if not args.no_cpu_baseline and M == 1:
         try:
             out["cpu_baseline"] = cpu_baseline(wl)

@@ -109,6 +109,12 @@ _sigs = {
     "bitq_workspace_size": ([ctypes.POINTER(WDesc), _I32, ctypes.POINTER(_SZ)], _I32),
     "bitq_gemv": ([ctypes.POINTER(WDesc), _P, _P, _I32, _P, _P, _SZ, _U32, _P], _I32),
     "bitq_gemm_smallM": ([ctypes.POINTER(WDesc), _P, _P, _I32, _P, _P, _SZ, _U32, _P], _I32),
+    # measurement context kernels (include/bitq_ctx.h)
+    "bitq_ctx_empty": ([_I32, _P], _I32),
+    "bitq_ctx_stream": ([_P, _SZ, _I32, _P, _I32, _P], _I32),
+    "bitq_ctx_spin": ([_I32, _P], _I32),
+    "bitq_ctx_launch_shape": ([ctypes.POINTER(WDesc), _I32, _I32, _U32, ctypes.POINTER(_I32), ctypes.POINTER(_I32)],
+                              _I32),
 }
 for _name, (_args, _ret) in _sigs.items():
     _f = getattr(_lib, _name)
@@ -305,6 +311,31 @@ def gemm_smallM(desc: WDesc, w, act, M: int, y, ws, ws_bytes: int | None = None,
     nbytes = _nbytes(ws) if ws_bytes is None else ws_bytes
     _check(_lib.bitq_gemm_smallM(ctypes.byref(desc), _ptr(w), _ptr(act), M, _ptr(y), _ptr(ws),
                                  nbytes, flags, _stream(stream)))
+
+
+# ------------------------------------------- measurement context kernels
+def ctx_empty(grid: int, stream=None):
+    """A launch of `grid` workgroups that does nothing (bitq_ctx_empty)."""
+    _check(_lib.bitq_ctx_empty(grid, _stream(stream)))
+
+
+def ctx_stream(src, nbytes: int, grid: int, out, nout: int, stream=None):
+    """Read nbytes of src once with `grid` workgroups and write nout floats
+    (bitq_ctx_stream): the streaming floor of a GEMV over those bytes."""
+    _check(_lib.bitq_ctx_stream(_ptr(src), nbytes, grid, _ptr(out), nout, _stream(stream)))
+
+
+def ctx_launch_shape(desc: WDesc, M: int, x_dtype: int, flags: int = 0) -> tuple:
+    """(workgroups, lanes per workgroup) of the kernel bitq_gemv (M = 1) or
+    bitq_gemm_smallM launches for these arguments."""
+    g, b = _I32(0), _I32(0)
+    _check(_lib.bitq_ctx_launch_shape(ctypes.byref(desc), M, x_dtype, flags, ctypes.byref(g), ctypes.byref(b)))
+    return g.value, b.value
+
+
+def ctx_spin(microseconds: int, stream=None):
+    """One wave that waits the given wall-clock time (bitq_ctx_spin)."""
+    _check(_lib.bitq_ctx_spin(microseconds, _stream(stream)))
 
 
 def act_layout(M: int, K: int, rank: int = 0) -> dict:

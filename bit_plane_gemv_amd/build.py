@@ -7,7 +7,7 @@ This file is loaded by path (not as part of the package), so it works before
 libbitq.so exists; importing the package itself requires the built library.
 
 The shared library holds the host code (validation, packer, quantizers) and
-the HIP kernels.  Host code is compiled without floating-point contraction so
+the HIP kernels (one source per kernel family, compiled in parallel).  Host code is compiled without floating-point contraction so
 that the offline quantizers follow the documented arithmetic order.
 """
 from __future__ import annotations
@@ -41,27 +41,56 @@ def _run(cmd):
     return r
 
 
-def build(asm: bool = False, verbose: bool = False) -> str:
-    objs = []
+def _run_all(cmds, jobs: int):
+    """Run the compile commands, at most `jobs` at a time; raise on the first failure."""
+    pending, running = list(cmds), []
+    failed = None
+    while pending or running:
+        while pending and len(running) < jobs and failed is None:
+            cmd = pending.pop(0)
+            running.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                                  text=True)))
+        cmd, p = running.pop(0)
+        out, _ = p.communicate()
+        if p.returncode != 0 and failed is None:
+            sys.stderr.write(out)
+            failed = cmd
+        if failed is not None:
+            pending.clear()
+    if failed is not None:
+        raise RuntimeError("command failed: " + " ".join(failed))
+
+
+def kernel_sources() -> list:
+    """The HIP sources of the library (one per kernel family)."""
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+
+
+def build(asm: bool = False, verbose: bool = False, jobs: int | None = None) -> str:
+    jobs = jobs or max(1, min(8, os.cpu_count() or 1))
     host_src = os.path.join(CSRC, "bitq_host.cpp")
-    kern_src = os.path.join(CSRC, "bitq_kernels.hip")
+    cmds, objs = [], []
     host_obj = os.path.join(CSRC, "bitq_host.o")
-    kern_obj = os.path.join(CSRC, "bitq_kernels.o")
-    _run([HIPCC, *COMMON, "-c", host_src, "-o", host_obj])
+    cmds.append([HIPCC, *COMMON, "-c", host_src, "-o", host_obj])
     objs.append(host_obj)
-    _run([HIPCC, *COMMON, *DEVICE_FLAGS, "-x", "hip", "-c", kern_src, "-o", kern_obj])
-    objs.append(kern_obj)
+    for src in kernel_sources():
+        obj = src[:-4] + ".o"
+        cmds.append([HIPCC, *COMMON, *DEVICE_FLAGS, "-x", "hip", "-c", src, "-o", obj])
+        objs.append(obj)
+    # the largest sources first, so that they start early
+    cmds.sort(key=lambda c: -os.path.getsize(c[-3]))
+    _run_all(cmds, jobs)
     tmp = LIB + ".tmp"
     _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
     os.replace(tmp, LIB)
     for o in objs:
         os.remove(o)
     if asm:
-        out = os.path.join(CSRC, f"bitq_kernels-hip-amdgcn-amd-amdhsa-{ARCH}.s")
-        _run([HIPCC, *COMMON, *DEVICE_FLAGS, "-x", "hip", "--cuda-device-only", "-S",
-              kern_src, "-o", out])
-        if verbose:
-            print("assembly:", out)
+        for src in kernel_sources():
+            out = src[:-4] + f"-hip-amdgcn-amd-amdhsa-{ARCH}.s"
+            _run([HIPCC, *COMMON, *DEVICE_FLAGS, "-x", "hip", "--cuda-device-only", "-S", src, "-o", out])
+            if verbose:
+                print("assembly:", out)
     if verbose:
         print("built", LIB)
     return LIB

@@ -823,6 +823,51 @@ Plan make_plan(const bitq_wdesc& d, int M, bool fused) {
     return p;
 }
 
+MfmaShape mfma_shape(const bitq_wdesc& d, int M) {
+    // Measured on 11008x4096 and 4096x11008 W2A8 and 4096^2 ternary layers,
+    // M = 2..64: 16 rows per workgroup and 8 or 16 waves over k (about
+    // 4-8k waves in flight, each with one or two load chunks of 2 blocks),
+    // except that on layers of 8192+ rows the q operands are worth sharing
+    // by 64-row workgroups from 8 tokens on (16 waves, one block per chunk,
+    // up to 16 tokens; 8 waves, two blocks, beyond).
+    MfmaShape s{};
+    s.TT = std::min(4, (M + 15) / 16);
+    const bool wide = s.TT >= 2 && d.N >= 8192;
+    const bool tall16 = s.TT == 1 && M >= 8 && d.N >= 8192;
+    if (tall16) {
+        s.RS = 4, s.KW = 16, s.CH = 1;
+    } else if (wide) {
+        s.RS = 4, s.KW = 8, s.CH = 2;
+    } else {
+        s.RS = 1, s.KW = d.N <= 8192 ? 16 : 8, s.CH = 2;
+    }
+    const int64_t tiles = round_up(d.N, kRowTile) / kRowTile;
+    s.grid = static_cast<int>(tiles * (4 / s.RS));
+    s.block = 64 * s.KW;
+    return s;
+}
+
+LaunchShape launch_shape(const bitq_wdesc& d, int M, int x_dtype, uint32_t flags) {
+    LaunchShape ls{0, 256};
+    const int64_t tiles = round_up(d.N, kRowTile) / kRowTile;
+    if (x_dtype == BITQ_DT_BINARY) {  // XNOR kernel: 8 rows per workgroup
+        ls.grid = xcd_row_groups(tiles, 8);
+        return ls;
+    }
+    const bool fused = (flags & BITQ_F_FUSE_QUANT) != 0;
+    const Plan p = make_plan(d, M, fused);
+    if (d.fmt == BITQ_SIGN1 || d.fmt == BITQ_RABIT) {
+        ls.grid = p.row_groups * p.splits;
+    } else if (p.mfma) {
+        const MfmaShape m = mfma_shape(d, M);
+        ls.grid = m.grid;
+        ls.block = m.block;
+    } else {
+        ls.grid = xcd_row_groups(tiles, p.rows_per_wg);
+    }
+    return ls;
+}
+
 }  // namespace bitq
 
 using namespace bitq;
@@ -1177,6 +1222,64 @@ bitq_status bitq_gemm_smallM(const bitq_wdesc* desc, const void* w_dev, const vo
     if (M < 2 || M > 64) return fail(BITQ_E_SHAPE, "M=%d out of range [2, 64]", M);
     const int32_t dt = desc->fmt == BITQ_SIGN1 ? BITQ_DT_BINARY : BITQ_DT_ACT;
     return gemv_common(desc, w_dev, act_dev, dt, M, y_dev, ws_dev, ws_bytes, flags, stream);
+}
+
+// ------------------------------------------------- measurement context kernels
+bitq_status bitq_ctx_launch_shape(const bitq_wdesc* desc, int32_t M, int32_t x_dtype, uint32_t flags,
+                                  int32_t* grid, int32_t* block) {
+    bitq_status s = check_desc(desc);
+    if (s) return s;
+    if (!grid || !block) return fail(BITQ_E_ARG, "grid/block is NULL");
+    if (M < 1 || M > 64) return fail(BITQ_E_SHAPE, "M=%d out of range [1, 64]", M);
+    if (x_dtype < BITQ_DT_F32 || x_dtype > BITQ_DT_BINARY) return fail(BITQ_E_ARG, "unknown x_dtype %d", x_dtype);
+    if (flags & ~(BITQ_F_ACC_INT32 | BITQ_F_FUSE_QUANT)) return fail(BITQ_E_ARG, "unknown flags 0x%x", flags);
+    const LaunchShape ls = launch_shape(*desc, M, x_dtype, flags);
+    *grid = ls.grid;
+    *block = ls.block;
+    return ok();
+}
+
+static bitq_status ctx_device_ok() {
+    int is950 = 0;
+    int e = current_device_is_gfx950(&is950);
+    if (e) return fail(BITQ_E_DEVICE, "HIP error %d while querying the device", e);
+    if (!is950) return fail(BITQ_E_UNSUPPORTED, "current device is not gfx950");
+    return BITQ_OK;
+}
+
+bitq_status bitq_ctx_empty(int32_t grid, void* stream) {
+    if (grid < 1 || grid > (1 << 20)) return fail(BITQ_E_SHAPE, "grid=%d out of range [1, 2^20]", grid);
+    bitq_status s = ctx_device_ok();
+    if (s) return s;
+    int e = launch_ctx_empty(grid, stream);
+    if (e) return fail(BITQ_E_DEVICE, "HIP launch error %d", e);
+    return ok();
+}
+
+bitq_status bitq_ctx_stream(const void* src_dev, size_t bytes, int32_t grid, float* out_dev, int32_t nout,
+                            void* stream) {
+    if (!src_dev) return fail(BITQ_E_ARG, "src_dev is NULL");
+    if (bytes == 0 || bytes % 16) return fail(BITQ_E_SHAPE, "bytes=%zu must be a positive multiple of 16", bytes);
+    if (grid < 1 || grid > (1 << 20)) return fail(BITQ_E_SHAPE, "grid=%d out of range [1, 2^20]", grid);
+    if (nout < 0 || nout > (1 << 24)) return fail(BITQ_E_SHAPE, "nout=%d out of range [0, 2^24]", nout);
+    if (nout > 0 && !out_dev) return fail(BITQ_E_ARG, "out_dev is NULL");
+    if (!aligned(src_dev, 16)) return fail(BITQ_E_ALIGN, "src_dev must be 16-byte aligned");
+    if (out_dev && !aligned(out_dev, 4)) return fail(BITQ_E_ALIGN, "out_dev must be 4-byte aligned");
+    bitq_status s = ctx_device_ok();
+    if (s) return s;
+    int e = launch_ctx_stream(src_dev, bytes, grid, out_dev, nout, stream);
+    if (e) return fail(BITQ_E_DEVICE, "HIP launch error %d", e);
+    return ok();
+}
+
+bitq_status bitq_ctx_spin(int32_t microseconds, void* stream) {
+    if (microseconds < 1 || microseconds > 10000)
+        return fail(BITQ_E_SHAPE, "microseconds=%d out of range [1, 10000]", microseconds);
+    bitq_status s = ctx_device_ok();
+    if (s) return s;
+    int e = launch_ctx_spin(microseconds, stream);
+    if (e) return fail(BITQ_E_DEVICE, "HIP launch error %d", e);
+    return ok();
 }
 
 }  // extern "C"

@@ -6,6 +6,7 @@
 #include <cstdint>
 
 #include "../../include/bitq.h"
+#include "../../include/bitq_ctx.h"
 
 namespace bitq {
 
@@ -61,15 +62,38 @@ struct Plan {
     bool mfma;             // integer formats, M >= kMfmaMinM: the int8 matrix-core kernel
 };
 Plan make_plan(const bitq_wdesc& d, int M, bool fused = false);  // fused: BITQ_F_FUSE_QUANT
+
+// Launch shape of the matrix-core kernel for M tokens: TT token tiles of 16,
+// RS row sub-tiles of 16 per workgroup, KW waves over k, CH k blocks per load
+// chunk; grid = row tiles x (4 / RS) workgroups of 64 KW lanes.
+struct MfmaShape {
+    int TT, RS, KW, CH;
+    int grid, block;
+};
+MfmaShape mfma_shape(const bitq_wdesc& d, int M);
+
+// Workgroups and lanes per workgroup of the kernel a bitq_gemv /
+// bitq_gemm_smallM call launches (x_dtype and flags as in that call).
+struct LaunchShape {
+    int grid, block;
+};
+LaunchShape launch_shape(const bitq_wdesc& d, int M, int x_dtype, uint32_t flags);
+// Workgroups of the AND+popcount / XNOR kernels: 64/RG row groups per 64-row
+// tile, tiles dealt round-robin to the 8 XCDs (padded to whole rounds).
+inline int xcd_row_groups(int64_t tiles, int RG) { return static_cast<int>(8 * (64 / RG) * ((tiles + 7) / 8)); }
 constexpr int kMfmaMinM = 4;  // tokens from which TERNARY/W2A8/WNAM use the matrix cores
 constexpr int kMaxFusedK = 16384;    // BITQ_F_FUSE_QUANT: whole k range in one round of the kernel
 constexpr int kLaunchNotBuilt = -1;  // launcher: no kernel built for this combination
 
-// Kernel launchers (bitq_kernels.hip).  Arguments are already validated.
+// Kernel launchers (bitq_act.hip, bitq_sign.hip, bitq_bits.hip, bitq_mfma.hip,
+// bitq_xnor.hip).  Arguments are already validated.
 // Each returns hipSuccess or the HIP error code of the launch.
 int launch_quantize_act(const void* x, int x_dtype, int M, int K, int abits, void* act, void* stream);
 int launch_gemv_float(const bitq_wdesc& d, const Plan& plan, const void* w, const void* x,
                       int x_dtype, float* y, void* ws, void* stream);
+// Small-M GEMM on the int8 matrix cores (plans with mfma set).
+int launch_gemm_mfma(const bitq_wdesc& d, const void* w, const void* act, int M, float* y, uint32_t flags,
+                     void* stream);
 int launch_gemv_int(const bitq_wdesc& d, const Plan& plan, const void* w, const void* act,
                     int M, float* y, void* ws, uint32_t flags, void* stream);
 // Fused activation quantizer + GEMV, one token, raw x (bf16 or fp32); returns
@@ -82,7 +106,12 @@ int launch_binarize_act(const void* x, int x_dtype, int M, int K, void* act, voi
 int launch_gemv_xnor(const bitq_wdesc& d, const void* w, const void* act, int M, float* y, uint32_t flags,
                      void* stream);
 
-// Device checks (bitq_kernels.hip): is the current device a gfx950?
+// Measurement context kernels (bitq_ctx.hip); arguments already validated.
+int launch_ctx_empty(int grid, void* stream);
+int launch_ctx_stream(const void* src, size_t bytes, int grid, float* out, int nout, void* stream);
+int launch_ctx_spin(int microseconds, void* stream);
+
+// Device check (bitq_act.hip): is the current device a gfx950?
 int current_device_is_gfx950(int* is_gfx950);
 
 }  // namespace bitq

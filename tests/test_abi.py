@@ -13,9 +13,14 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared_symbols():
-    text = open(os.path.join(ROOT, "include", "bitq.h")).read()
-    return sorted(set(re.findall(r"^\s*(?:bitq_status|const char\*|int32_t)\s+(bitq_\w+)\s*\(",
-                                 text, re.M)))
+    """Every entry point declared in the headers under include/."""
+    syms = set()
+    inc = os.path.join(ROOT, "include")
+    for name in sorted(os.listdir(inc)):
+        if name.endswith(".h"):
+            text = open(os.path.join(inc, name)).read()
+            syms |= set(re.findall(r"^\s*(?:bitq_status|const char\*|int32_t)\s+(bitq_\w+)\s*\(", text, re.M))
+    return sorted(syms)
 
 
 def test_every_declared_symbol_is_exported():
@@ -286,3 +291,19 @@ def test_hgf_act_size_and_validation():
     # the GEMV takes the HGF activation buffer; no workspace
     assert bq.workspace_size(d, 1) == 0
     assert bq._lib.bitq_gemv(ctypes.byref(d), good, good, bq.DT_BF16, good, None, 0, 0, None) == bq.E_ARG
+
+
+def test_context_kernels_validate_before_any_device_call():
+    good = 1 << 20                              # fake, aligned addresses: never dereferenced
+    assert bq._lib.bitq_ctx_empty(0, None) == bq.E_SHAPE
+    assert bq._lib.bitq_ctx_empty((1 << 20) + 1, None) == bq.E_SHAPE
+    assert bq._lib.bitq_ctx_stream(None, 4096, 16, good, 64, None) == bq.E_ARG
+    assert bq._lib.bitq_ctx_stream(good, 0, 16, good, 64, None) == bq.E_SHAPE
+    assert bq._lib.bitq_ctx_stream(good, 4100, 16, good, 64, None) == bq.E_SHAPE
+    assert bq._lib.bitq_ctx_stream(good, 4096, 0, good, 64, None) == bq.E_SHAPE
+    assert bq._lib.bitq_ctx_stream(good, 4096, 16, None, 64, None) == bq.E_ARG
+    assert bq._lib.bitq_ctx_stream(good, 4096, 16, good, -1, None) == bq.E_SHAPE
+    assert bq._lib.bitq_ctx_stream(good + 8, 4096, 16, good, 64, None) == bq.E_ALIGN
+    assert bq._lib.bitq_ctx_stream(good, 4096, 16, good + 2, 64, None) == bq.E_ALIGN
+    assert bq._lib.bitq_ctx_spin(0, None) == bq.E_SHAPE
+    assert bq._lib.bitq_ctx_spin(10001, None) == bq.E_SHAPE
