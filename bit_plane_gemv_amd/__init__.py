@@ -17,7 +17,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libbitq.so")
+# BITQ_LIBRARY selects another build of the same library (the sanitizer
+# build of build.py --sanitize); by default the in-tree libbitq.so
+LIB_PATH = os.environ.get("BITQ_LIBRARY") or os.path.join(_HERE, "libbitq.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"libbitq.so not found at {LIB_PATH}; build it with "
@@ -176,8 +178,36 @@ def packed_size(desc: WDesc) -> int:
     return n.value
 
 
+def _logical_shapes(desc: WDesc) -> dict:
+    """Shape of each array field of bitq_logical that the descriptor's format
+    reads (include/bitq.h, "Logical (unpacked) quantized form")."""
+    N, K, P = desc.N, desc.K, desc.planes
+    if desc.fmt == SIGN1:
+        return {"sign": (N, K), "alpha": (N,)}
+    if desc.fmt == RABIT:
+        return {"sign": (P, N, K), "g": (P, N), "h": (P, K)}
+    if desc.fmt == TERNARY:
+        return {"tern": (N, K)}
+    if desc.fmt in (W2A8, WNAM):
+        return {"code": (N, K), "delta": (N, K // 128), "zero": (N, K // 128)}
+    if desc.fmt == BVSR4:
+        return {"code": (N, K), "idx": (N, K // 32), "cache": (256, 5)}
+    if desc.fmt == HGF:
+        return {"tern": (N, K), "lora_a": (K, desc.rank), "lora_b": (desc.rank, N)}
+    return {}
+
+
 def pack_weights(desc: WDesc, **fields) -> np.ndarray:
-    """Pack a logical form (numpy arrays named as in bitq_logical) into a blob."""
+    """Pack a logical form (numpy arrays named as in bitq_logical) into a blob.
+    Every array the format reads must be given, with the shape the header
+    documents (ValueError otherwise): the C packer takes no lengths."""
+    need = _logical_shapes(desc)
+    for name, shape in need.items():
+        if name not in fields or fields[name] is None:
+            raise ValueError(f"{FORMAT_NAMES.get(desc.fmt, desc.fmt)} needs the field {name!r}")
+        got = np.shape(fields[name])
+        if tuple(got) != tuple(shape):
+            raise ValueError(f"field {name!r} has shape {tuple(got)}, the descriptor needs {tuple(shape)}")
     keep = []
     lg = Logical()
     conv = {"sign": np.int8, "tern": np.int8, "code": np.uint8, "alpha": np.float32,

@@ -2,6 +2,7 @@
 
     python bit_plane_gemv_amd/build.py          # build (always recompiles)
     python bit_plane_gemv_amd/build.py --asm    # also dump the gfx950 assembly
+    python bit_plane_gemv_amd/build.py --sanitize   # host code under ASan/UBSan
 
 This file is loaded by path (not as part of the package), so it works before
 libbitq.so exists; importing the package itself requires the built library.
@@ -96,5 +97,44 @@ def build(asm: bool = False, verbose: bool = False, jobs: int | None = None) -> 
     return LIB
 
 
+SAN_LIB = os.path.join(HERE, "libbitq_san.so")
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"]
+
+
+def build_sanitized(verbose: bool = False, jobs: int | None = None) -> str:
+    """libbitq_san.so: the host code (validation, packer, quantizers) built by
+    g++ with AddressSanitizer and UndefinedBehaviorSanitizer, linked with the
+    ordinary gfx950 kernel objects.  For the CPU test suite:
+
+        python bit_plane_gemv_amd/build.py --sanitize
+        ASAN_OPTIONS=detect_leaks=0 LD_PRELOAD=$(g++ -print-file-name=libasan.so) \
+            BITQ_LIBRARY=bit_plane_gemv_amd/libbitq_san.so python -m pytest tests -m "not gpu"
+
+    The kernels themselves are not instrumented (device code); only host code is."""
+    jobs = jobs or max(1, min(8, os.cpu_count() or 1))
+    host_src = os.path.join(CSRC, "bitq_host.cpp")
+    host_obj = os.path.join(CSRC, "bitq_host_san.o")
+    inc = f"-I{os.path.join(HERE, '..', 'include')}"
+    cmds = [["g++", "-O1", "-g", "-std=c++17", "-fPIC", "-ffp-contract=off", "-D__HIP_PLATFORM_AMD__", inc,
+             "-I/opt/rocm/include", *SAN_FLAGS, "-c", host_src, "-o", host_obj]]
+    objs = [host_obj]
+    for src in kernel_sources():
+        obj = src[:-4] + "_san.o"
+        cmds.append([HIPCC, *COMMON, *DEVICE_FLAGS, "-x", "hip", "-c", src, "-o", obj])
+        objs.append(obj)
+    _run_all(cmds, jobs)
+    tmp = SAN_LIB + ".tmp"
+    _run(["g++", "-shared", *SAN_FLAGS, *objs, "-L/opt/rocm/lib", "-lamdhip64", "-o", tmp])
+    os.replace(tmp, SAN_LIB)
+    for o in objs:
+        os.remove(o)
+    if verbose:
+        print("built", SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    build(asm="--asm" in sys.argv, verbose=True)
+    if "--sanitize" in sys.argv:
+        build_sanitized(verbose=True)
+    else:
+        build(asm="--asm" in sys.argv, verbose=True)

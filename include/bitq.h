@@ -195,7 +195,14 @@ typedef struct {
  *   when a format has no c1 section.
  */
 
-/* Bytes of the packed blob for a descriptor. */
+/*
+ * Bytes of the packed blob for a descriptor: the header, the plane tiles and
+ * the coefficient sections of the layout above, each section rounded up to
+ * 256 bytes.  The plane tiles keep the bitvectors of consecutive output rows
+ * next to each other, the coalesced layout of [BVSR] introduction; the
+ * coefficient sections are those of each format's definition (see
+ * bitq_format).  Host only; BITQ_E_SHAPE / BITQ_E_ARG for a bad descriptor.
+ */
 bitq_status bitq_packed_size(const bitq_wdesc* desc, size_t* bytes);
 
 /*
@@ -421,7 +428,11 @@ bitq_status bitq_gemv(const bitq_wdesc* desc, const void* w_dev, const void* x_d
 /*
  * Small-batch GEMM y[M][N] = x W^T for 2 <= M <= 64, integer formats
  * (TERNARY, W2A8, BVSR4, WNAM, HGF) and SIGN1 with binary activations,
- * reading every weight once for all M tokens.
+ * reading every weight once for all M tokens.  [ABQ] §1: in decoding the
+ * GEMM degenerates into a GEMV and small batches (fewer than 8 tokens) are
+ * padded on matrix units, wasting most of the multiply; here a batch of M
+ * tokens is one pass over the weights, on the VALU for the fewest tokens
+ * and on the int8 matrix cores once the contraction is compute-bound.
  *   act_dev activation buffer from bitq_quantize_act(_bits) with this M
  *           (SIGN1: from bitq_binarize_act; HGF: from bitq_quantize_act_hgf).
  * From 4 tokens on, TERNARY, W2A8 and WNAM run on the int8 matrix cores

@@ -253,11 +253,19 @@ def test_hgf_pack_and_quantize_validation():
     bad = A.copy()
     bad[3, 1] = np.float16(np.inf)
     for kw in (dict(lora_a=bad, lora_b=B, lora_alpha=0.1),
-               dict(lora_a=A, lora_b=B, lora_alpha=float("nan")),
-               dict(lora_a=A, lora_alpha=0.1)):               # lora_b missing
+               dict(lora_a=A, lora_b=B, lora_alpha=float("nan"))):
         with pytest.raises(bq.BitqError) as e:
             bq.pack_weights(d, tern=T, gamma=0.5, **kw)
         assert e.value.status == bq.E_ARG
+    with pytest.raises(ValueError):                           # lora_b missing: the binding refuses
+        bq.pack_weights(d, tern=T, gamma=0.5, lora_a=A, lora_alpha=0.1)
+    # ... and so does the C ABI (NULL lora_b), for callers that bypass the binding
+    t8 = np.ascontiguousarray(T, dtype=np.int8)
+    a16 = np.ascontiguousarray(A.view(np.uint16) if A.dtype == np.float16 else A, dtype=np.uint16)
+    lg = bq.Logical()
+    lg.tern, lg.gamma, lg.lora_a, lg.lora_alpha = t8.ctypes.data, 0.5, a16.ctypes.data, 0.1
+    out = np.zeros(bq.packed_size(d), np.uint8)
+    assert bq._lib.bitq_pack_weights(ctypes.byref(d), ctypes.byref(lg), out.ctypes.data, out.nbytes) == bq.E_ARG
     with pytest.raises(bq.BitqError) as e:                    # A, B and alpha are trained inputs
         bq.quantize_weights(d, np.zeros((N, K), np.float32))
     assert e.value.status == bq.E_UNSUPPORTED
@@ -307,3 +315,24 @@ def test_context_kernels_validate_before_any_device_call():
     assert bq._lib.bitq_ctx_stream(good, 4096, 16, good + 2, 64, None) == bq.E_ALIGN
     assert bq._lib.bitq_ctx_spin(0, None) == bq.E_SHAPE
     assert bq._lib.bitq_ctx_spin(10001, None) == bq.E_SHAPE
+
+
+def test_pack_weights_checks_field_shapes():
+    d = bq.wdesc(bq.W2A8, 64, 256)
+    ok = dict(code=np.zeros((64, 256), np.uint8), delta=np.ones((64, 2), np.float16),
+              zero=np.zeros((64, 2), np.float16))
+    bq.pack_weights(d, **ok)
+    for name, bad in (("code", np.zeros((64, 128), np.uint8)), ("delta", np.ones((64, 1), np.float16)),
+                      ("zero", np.zeros((32, 2), np.float16))):
+        with pytest.raises(ValueError):
+            bq.pack_weights(d, **{**ok, name: bad})
+    with pytest.raises(ValueError):
+        bq.pack_weights(d, code=ok["code"], delta=ok["delta"])           # zero missing
+    dr = bq.wdesc(bq.RABIT, 64, 256, planes=2)
+    with pytest.raises(ValueError):                                       # one path of signs for two paths
+        bq.pack_weights(dr, sign=np.ones((1, 64, 256), np.int8), g=np.ones((2, 64), np.float16),
+                        h=np.ones((2, 256), np.float16))
+    db = bq.wdesc(bq.BVSR4, 64, 256)
+    with pytest.raises(ValueError):
+        bq.pack_weights(db, code=np.zeros((64, 256), np.uint8), idx=np.zeros((64, 8), np.uint8),
+                        cache=np.zeros((255, 5), np.float32))
