@@ -106,6 +106,7 @@ _sigs = {
     "bitq_quantize_act_bits": ([_P, _I32, _I32, _I32, _I32, _P, _SZ, _P], _I32),
     "bitq_hgf_act_size": ([ctypes.POINTER(WDesc), _I32, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)], _I32),
     "bitq_quantize_act_hgf": ([ctypes.POINTER(WDesc), _P, _P, _I32, _I32, _P, _SZ, _P, _SZ, _P], _I32),
+    "bitq_quantize_act_hgf_noalloc": ([ctypes.POINTER(WDesc), _P, _P, _I32, _I32, _P, _SZ, _P], _I32),
     "bitq_binact_size": ([_I32, _I32, ctypes.POINTER(_SZ)], _I32),
     "bitq_binarize_act": ([_P, _I32, _I32, _I32, _P, _SZ, _P], _I32),
     "bitq_workspace_size": ([ctypes.POINTER(WDesc), _I32, ctypes.POINTER(_SZ)], _I32),
@@ -322,6 +323,15 @@ def quantize_act_hgf(desc: WDesc, w, x, x_dtype: int, M: int, act, ws, act_bytes
     wbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
     _check(_lib.bitq_quantize_act_hgf(ctypes.byref(desc), _ptr(w), _ptr(x), x_dtype, M, _ptr(act), abytes,
                                       _ptr(ws), wbytes, _stream(stream)))
+
+
+def quantize_act_hgf_noalloc(desc: WDesc, w, x, x_dtype: int, M: int, act, act_bytes: int | None = None,
+                             stream=None):
+    """bitq_quantize_act_hgf without a workspace (the library's static device
+    scratch holds the down projection's words; nothing is allocated)."""
+    abytes = act.numel() * act.element_size() if act_bytes is None else act_bytes
+    _check(_lib.bitq_quantize_act_hgf_noalloc(ctypes.byref(desc), _ptr(w), _ptr(x), x_dtype, M, _ptr(act), abytes,
+                                              _stream(stream)))
 
 
 def _nbytes(buf) -> int:

@@ -3,6 +3,7 @@
 // binary path.  Also the per-device gfx950 check used by the host code.
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include <hip/hip_runtime.h>
 
@@ -311,6 +312,57 @@ int launch_quantize_act_hgf(const void* x, int x_dtype, int M, int K, int rank, 
     else
         launch_quant_hgf_rank<BITQ_DT_BF16>(rank, grid, st, x, K, Kw, planes, S, q, d, blob, L.off_c1, Kp, wsw, h);
     return static_cast<int>(hipGetLastError());
+}
+
+// ------------------------------------------- the no-allocation activation step
+// Scratch of bitq_quantize_act_hgf_noalloc: the 64-bit fixed-point words of
+// the HGF down projection (one per token and rank column), for the largest
+// call (64 tokens x rank 64 = 32 KB).  Each GPU the library runs on holds
+// its own copy until the process ends.  In host code the name `scratch` is
+// not a device address: the address comes from hipGetSymbolAddress, once
+// per device, and only that address is passed to kernels.
+static __device__ __align__(256) unsigned long long scratch[kNoAllocScratchWords];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];  // per device: the device address of `scratch`, or null before set-up
+}  // namespace
+
+__global__ __launch_bounds__(256) void zero_words_kernel(unsigned long long* __restrict__ w, int n) {
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) w[i] = 0ull;
+}
+
+int noalloc_scratch(void** ptr, void* stream) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return static_cast<int>(e);
+    if (dev < 0 || dev >= 64) return static_cast<int>(hipErrorInvalidDevice);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return static_cast<int>(e);
+        if (p == nullptr) return static_cast<int>(hipErrorInvalidSymbol);
+        // The words start at zero (device globals are zero-initialized, and
+        // every completed call leaves them zero); cleared once more here at
+        // set-up with a fill kernel, which is also valid under graph capture.
+        hipLaunchKernelGGL(zero_words_kernel, dim3((kNoAllocScratchWords + 255) / 256), dim3(256), 0,
+                           static_cast<hipStream_t>(stream), static_cast<unsigned long long*>(p),
+                           kNoAllocScratchWords);
+        e = hipGetLastError();
+        if (e != hipSuccess) return static_cast<int>(e);
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return 0;
+}
+
+int launch_quantize_act_hgf_noalloc(const void* x, int x_dtype, int M, int K, int rank, const void* w,
+                                    const BlobLayout& L, void* act, void* stream) {
+    void* ws = nullptr;
+    const int e = noalloc_scratch(&ws, stream);
+    if (e) return e;
+    return launch_quantize_act_hgf(x, x_dtype, M, K, rank, w, L, act, ws, stream);
 }
 
 int launch_binarize_act(const void* x, int x_dtype, int M, int K, void* act, void* stream) {

@@ -1092,6 +1092,34 @@ bitq_status bitq_quantize_act_hgf(const bitq_wdesc* desc, const void* w_dev, con
     return ok();
 }
 
+bitq_status bitq_quantize_act_hgf_noalloc(const bitq_wdesc* desc, const void* w_dev, const void* x_dev,
+                                          int32_t x_dtype, int32_t M, void* act_dev, size_t act_bytes,
+                                          void* stream) {
+    size_t need_act = 0, need_ws = 0;
+    bitq_status s = bitq_hgf_act_size(desc, M, &need_act, &need_ws);
+    if (s) return s;
+    const size_t words = static_cast<size_t>(M) * static_cast<size_t>(desc->rank);
+    if (words > static_cast<size_t>(kNoAllocScratchWords))
+        return fail(BITQ_E_CAPACITY, "M * rank = %zu exceeds the library scratch of %d words", words,
+                    kNoAllocScratchWords);
+    if (!w_dev || !x_dev || !act_dev) return fail(BITQ_E_ARG, "a device pointer is NULL");
+    if (x_dtype != BITQ_DT_F32 && x_dtype != BITQ_DT_BF16)
+        return fail(BITQ_E_ARG, "x_dtype must be BITQ_DT_F32 or BITQ_DT_BF16");
+    if (!aligned(x_dev, 16)) return fail(BITQ_E_ALIGN, "x_dev must be 16-byte aligned");
+    if (!aligned(w_dev, 256) || !aligned(act_dev, 256))
+        return fail(BITQ_E_ALIGN, "w_dev and act_dev must be 256-byte aligned");
+    if (act_bytes < need_act)
+        return fail(BITQ_E_CAPACITY, "act buffer has %zu bytes, needs %zu", act_bytes, need_act);
+    int is950 = 0;
+    int e = current_device_is_gfx950(&is950);
+    if (e) return fail(BITQ_E_DEVICE, "HIP error %d while querying the device", e);
+    if (!is950) return fail(BITQ_E_UNSUPPORTED, "current device is not gfx950");
+    e = launch_quantize_act_hgf_noalloc(x_dev, x_dtype, M, desc->K, desc->rank, w_dev, blob_layout(*desc), act_dev,
+                                        stream);
+    if (e) return fail(BITQ_E_DEVICE, "HIP error %d while setting up the scratch or launching", e);
+    return ok();
+}
+
 bitq_status bitq_binact_size(int32_t M, int32_t K, size_t* bytes) {
     if (!bytes) return fail(BITQ_E_ARG, "bytes is NULL");
     if (M < 1 || M > 64) return fail(BITQ_E_SHAPE, "M=%d out of range [1, 64]", M);

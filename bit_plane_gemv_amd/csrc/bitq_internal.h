@@ -102,6 +102,12 @@ int launch_gemv_fused(const bitq_wdesc& d, const Plan& plan, const void* w, cons
                       void* stream);
 int launch_quantize_act_hgf(const void* x, int x_dtype, int M, int K, int rank, const void* w, const BlobLayout& L,
                             void* act, void* ws, void* stream);
+// The HGF activation step with its workspace in the library's static device
+// scratch (bitq_quantize_act_hgf_noalloc): at most kNoAllocScratchWords
+// 64-bit words (M * rank), allocates nothing.
+constexpr int kNoAllocScratchWords = 64 * 64;
+int launch_quantize_act_hgf_noalloc(const void* x, int x_dtype, int M, int K, int rank, const void* w,
+                                    const BlobLayout& L, void* act, void* stream);
 int launch_binarize_act(const void* x, int x_dtype, int M, int K, void* act, void* stream);
 int launch_gemv_xnor(const bitq_wdesc& d, const void* w, const void* act, int M, float* y, uint32_t flags,
                      void* stream);

@@ -22,7 +22,8 @@
  *     row-major; outputs y are [M, N] row-major fp32.
  *   - Ownership: the caller owns every buffer.  The library allocates no
  *     memory (host or device) and keeps no state between calls other than a
- *     per-thread error string and a per-device "is gfx950" check.
+ *     per-thread error string, a per-device "is gfx950" check and the static
+ *     device scratch of bitq_quantize_act_hgf_noalloc.
  *   - Validation: every argument is checked before anything is enqueued or
  *     written.  On error nothing is written, a negative bitq_status is
  *     returned and bitq_last_error() describes it.  No C++ exception crosses
@@ -333,6 +334,24 @@ bitq_status bitq_hgf_act_size(const bitq_wdesc* desc, int32_t M, size_t* act_byt
 bitq_status bitq_quantize_act_hgf(const bitq_wdesc* desc, const void* w_dev, const void* x_dev,
                                   int32_t x_dtype, int32_t M, void* act_dev, size_t act_bytes,
                                   void* ws_dev, size_t ws_bytes, void* stream);
+
+/*
+ * bitq_quantize_act_hgf without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, arithmetic and outputs
+ * as bitq_quantize_act_hgf; the fixed-point words of the down projection live
+ * in the library's own static device array of 64 x 64 words (32 KB per GPU,
+ * held until the process ends), which covers every valid call
+ * (M * rank <= 4096; larger gives BITQ_E_CAPACITY).  Nothing is allocated:
+ * the array's device address is looked up on the first call on each device,
+ * which also clears it with a small kernel on the given stream; every
+ * completed call leaves it zero again.  All calls on one GPU share the array:
+ * calls that may overlap in time on one GPU (different streams without
+ * ordering, concurrent graphs) race and give wrong h; order them.
+ */
+bitq_status bitq_quantize_act_hgf_noalloc(const bitq_wdesc* desc, const void* w_dev, const void* x_dev,
+                                          int32_t x_dtype, int32_t M, void* act_dev, size_t act_bytes,
+                                          void* stream);
 
 /*
  * Binary activation buffer (written by bitq_binarize_act, read by the SIGN1
