@@ -258,14 +258,24 @@ class Timer:
     submission of the graph, so the first step starts right after the start
     event and the events measure GPU time only."""
 
-    def __init__(self, torch, bq):
-        self.torch, self.bq = torch, bq
+    def __init__(self, torch, bq, graph: bool = True):
+        self.torch, self.bq, self.graph = torch, bq, graph
 
     def per_step_ms(self, step, K: int, warmup: int) -> float:
         torch, bq = self.torch, self.bq
         for i in range(warmup):
             step(i, torch.cuda.current_stream())
         torch.cuda.synchronize()
+        if not self.graph:        # launched one by one from the host (for counter runs)
+            stream = torch.cuda.current_stream()
+            ev0 = torch.cuda.Event(enable_timing=True)
+            ev1 = torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            for i in range(K):
+                step(i, stream)
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            return ev0.elapsed_time(ev1) / K
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
@@ -463,6 +473,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-second", action="store_true", help="skip the W2A8 headline of the default run")
     ap.add_argument("--no-context", action="store_true", help="skip the context kernels (floor, empty)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch every step from the host instead of a graph replay (for profiler counter runs; "
+                         "the per-step time then includes host launch gaps)")
     ap.add_argument("--tokens", type=int, default=1,
                     help="tokens per step (integer formats: 2..64 run the small-M path)")
     ap.add_argument("--fuse", action="store_true",
@@ -489,7 +502,7 @@ def main():
     import synth
 
     torch.cuda.set_device(torch.device("cuda:0"))
-    timer = Timer(torch, bq)
+    timer = Timer(torch, bq, graph=not args.no_graph)
     L = Layer(torch, bq, synth, wl, M)
     K_steps = args.steps
     N, K = L.N, L.K
@@ -552,7 +565,7 @@ def main():
                                f"({'RaBiT 2-path residual binary, bf16 x' if fmt == 'rabit' else fmt})",
                    "N": N, "K": K, "M": M, "format": fmt, "packed_bytes": L.alg_bytes, "seeds": L.seeds,
                    "rotating_copies": L.copies, "rotating_bytes": L.copies * L.stride,
-                   "graph_replay": True, "host_wall_s": round(wall, 4),
+                   "graph_replay": not args.no_graph, "host_wall_s": round(wall, 4),
                    **({"weight_bits": wl["planes"], "act_bits": L.abits} if fmt == "wnam" else {}),
                    **({"fused_quantizer": True} if fuse else {}),
                    **({"rank": wl["rank"], "gemv_kernel_bytes": L.gemv_bytes} if L.hgf else {})},

@@ -58,13 +58,70 @@ __device__ __forceinline__ void lora_arrive(unsigned long long* word, float part
     __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int DT, int RANK>
+// Where the matrix-core kernel reads input i of a 32-input word in the
+// permuted copy qm of q: input 8j + 2c + s sits at byte 16s + 4c + j, so
+// each 16 bytes of qm are one MFMA operand (see the matrix-core kernel).
+__device__ __forceinline__ int qm_pos(int i) { return 16 * (i & 1) + 4 * ((i >> 1) & 3) + (i >> 3); }
+
+// amax of a long row (K > kAmaxOnePassK) in a launch of its own: one
+// workgroup of 1024 lanes per token, four 16-byte loads in flight per lane.
+// The quantizer then reads only its own inputs instead of the whole row.
+template <int DT>
+__global__ __launch_bounds__(1024) void act_amax_kernel(const void* __restrict__ x, int K, float* __restrict__ amax) {
+    constexpr int VEC = (DT == BITQ_DT_F32) ? 4 : 8;
+    __shared__ float s_red[16];
+    const int m = blockIdx.x, tid = threadIdx.x;
+    const uint4* xv = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(x) +
+                                                     static_cast<size_t>(m) * K * (DT == BITQ_DT_F32 ? 4 : 2));
+    const int nvec = K / VEC;
+    float a = 0.0f;
+    for (int i0 = 0; i0 < nvec; i0 += 4096) {
+        uint4 v[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const int i = i0 + tid + 1024 * h;
+            v[h] = i < nvec ? xv[i] : make_uint4(0, 0, 0, 0);   // zeros do not change the max of |x|
+        }
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const uint32_t u[4] = {v[h].x, v[h].y, v[h].z, v[h].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (DT == BITQ_DT_F32)
+                    a = fmaxf(a, fabsf(__uint_as_float(u[e])));
+                else
+                    a = fmaxf(a, fmaxf(fabsf(__uint_as_float(u[e] << 16)), fabsf(__uint_as_float(u[e] & 0xFFFF0000u))));
+            }
+        }
+    }
+    a = wave_max(a);
+    if ((tid & 63) == 0) s_red[tid >> 6] = a;
+    __syncthreads();
+    if (tid == 0) {
+        float t = s_red[0];
+        for (int w = 1; w < 16; ++w) t = fmaxf(t, s_red[w]);
+        amax[m] = t;
+    }
+}
+
+// Pointers to the sections of an activation buffer (include/bitq.h).
+struct ActOut {
+    uint32_t* planes;
+    int32_t* S;
+    int8_t* q;
+    int8_t* qm;
+    float* d;
+    float* amax;
+    float* h;
+};
+
+// PRE: amax comes from act_amax_kernel (out.amax, written by the previous
+// launch on the stream) and the workgroup reads only its own 256 inputs.
+template <int DT, int RANK, bool PRE>
 __global__ __launch_bounds__(256) void quant_act_kernel(const void* __restrict__ x, int K, int Kw, float qmax,
-                                                        uint32_t* __restrict__ planes, int32_t* __restrict__ S,
-                                                        int8_t* __restrict__ q, float* __restrict__ dq,
-                                                        const uint8_t* __restrict__ blob, size_t off_at, int Kp,
-                                                        unsigned long long* __restrict__ ws,
-                                                        float* __restrict__ hout) {
+                                                        ActOut out, const uint8_t* __restrict__ blob, size_t off_at,
+                                                        int Kp, unsigned long long* __restrict__ ws) {
+    static_assert(!(PRE && RANK > 0), "the HGF activation step has K <= 16128: one pass");
     constexpr int VEC = (DT == BITQ_DT_F32) ? 4 : 8;  // inputs per 16-byte load
     constexpr int HOLD = 4;                            // 16-byte loads kept per thread
     __shared__ float s_red[4];
@@ -77,22 +134,21 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const void* __restrict__
     const int nvec = K / VEC;           // K is a multiple of 32
     const int lo = 256 * blockIdx.x;    // first input of this workgroup
 
-    // ---- one pass over the row: amax, and this workgroup's inputs to LDS
     float amax = 0.0f;
-    auto take = [&](int i, const uint4& u) {
+    auto take = [&](int i, const uint4& u, bool reduce) {
         const uint32_t a[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float v0, v1;
             if (DT == BITQ_DT_F32) {
                 v0 = __uint_as_float(a[e]);
-                amax = fmaxf(amax, fabsf(v0));
+                if (reduce) amax = fmaxf(amax, fabsf(v0));
                 const int k = i * VEC + e;
                 if (k >= lo && k < lo + 256) s_slice[k - lo] = v0;
             } else {
                 v0 = __uint_as_float(a[e] << 16);
                 v1 = __uint_as_float(a[e] & 0xFFFF0000u);
-                amax = fmaxf(amax, fmaxf(fabsf(v0), fabsf(v1)));
+                if (reduce) amax = fmaxf(amax, fmaxf(fabsf(v0), fabsf(v1)));
                 const int k = i * VEC + 2 * e;
                 if (k >= lo && k < lo + 256) {
                     s_slice[k - lo] = v0;
@@ -101,22 +157,32 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const void* __restrict__
             }
         }
     };
-    {
-        uint4 hold[HOLD];
+    if constexpr (PRE) {
+        // ---- amax from the separate pass; this workgroup's inputs to LDS
+        const int i = lo / VEC + tid;
+        if (tid < 256 / VEC && i < nvec) take(i, xv[i], false);
+        amax = out.amax[m];
+        __syncthreads();
+    } else {
+        // ---- one pass over the row: amax, and this workgroup's inputs to LDS
+        {
+            uint4 hold[HOLD];
 #pragma unroll
-        for (int h = 0; h < HOLD; ++h) {  // all loads of the first pass in flight together
-            const int i = tid + 256 * h;
-            hold[h] = (i < nvec) ? xv[i] : make_uint4(0, 0, 0, 0);
+            for (int h = 0; h < HOLD; ++h) {  // all loads of the first pass in flight together
+                const int i = tid + 256 * h;
+                hold[h] = (i < nvec) ? xv[i] : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int h = 0; h < HOLD; ++h)
+                if (tid + 256 * h < nvec) take(tid + 256 * h, hold[h], true);
         }
-#pragma unroll
-        for (int h = 0; h < HOLD; ++h)
-            if (tid + 256 * h < nvec) take(tid + 256 * h, hold[h]);
+        for (int i = tid + 256 * HOLD; i < nvec; i += 256) take(i, xv[i], true);
+        amax = wave_max(amax);
+        if (lane == 0) s_red[wave] = amax;
+        __syncthreads();
+        amax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+        if (blockIdx.x == 0 && tid == 0) out.amax[m] = amax;
     }
-    for (int i = tid + 256 * HOLD; i < nvec; i += 256) take(i, xv[i]);
-    amax = wave_max(amax);
-    if (lane == 0) s_red[wave] = amax;
-    __syncthreads();
-    amax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
     if constexpr (RANK > 0) {
         __shared__ float s_part[256];
         const int c = tid / RANK, j = tid % RANK;
@@ -145,12 +211,12 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const void* __restrict__
             for (int cc = 0; cc < 256 / RANK; ++cc) col += s_part[RANK * cc + tid];
             const double bound = static_cast<double>(K) * static_cast<double>(amax) * static_cast<double>(amax_a);
             lora_arrive(&ws[static_cast<size_t>(m) * RANK + tid], col, bound, static_cast<int>(gridDim.x),
-                        &hout[static_cast<size_t>(m) * RANK + tid]);
+                        &out.h[static_cast<size_t>(m) * RANK + tid]);
         }
     }
     float s = 0.0f;
     if (amax > 0.0f) s = __fdiv_rn(qmax, amax);
-    if (blockIdx.x == 0 && tid == 0) dq[m] = (amax > 0.0f) ? __fdiv_rn(amax, qmax) : 0.0f;
+    if (blockIdx.x == 0 && tid == 0) out.d[m] = (amax > 0.0f) ? __fdiv_rn(amax, qmax) : 0.0f;
 
     // ---- this wave's 64 inputs = words w0 and w0 + 1
     const int w0 = 8 * blockIdx.x + 2 * wave;
@@ -161,7 +227,9 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const void* __restrict__
         const float r = rintf(__fmul_rn(s_slice[k - lo], s));
         qi = static_cast<int>(fminf(fmaxf(r, -qmax), qmax));
     }
-    q[static_cast<size_t>(m) * (Kw * 32) + k] = static_cast<int8_t>(qi);
+    out.q[static_cast<size_t>(m) * (Kw * 32) + k] = static_cast<int8_t>(qi);
+    out.qm[static_cast<size_t>(m) * (Kw * 32 + 128) + 32 * (w0 + (lane >> 5)) + qm_pos(lane & 31)] =
+        static_cast<int8_t>(qi);
     // planes: lane j (< 8) keeps plane j of word w0, lane 8 + j of word w0 + 1
     uint32_t mine = 0;
 #pragma unroll
@@ -170,13 +238,13 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const void* __restrict__
         if (lane == j) mine = static_cast<uint32_t>(b);
         if (lane == 8 + j) mine = static_cast<uint32_t>(b >> 32);
     }
-    if (lane < 16) planes[(static_cast<size_t>(m) * Kw + w0) * 8 + lane] = mine;
+    if (lane < 16) out.planes[(static_cast<size_t>(m) * Kw + w0) * 8 + lane] = mine;
     // group sums of the two words: reductions inside each half of the wave
     int sum = qi;
 #pragma unroll
     for (int o = 1; o < 32; o <<= 1) sum += __shfl_xor(sum, o, 64);
-    if (lane == 0) S[static_cast<size_t>(m) * Kw + w0] = sum;
-    if (lane == 32) S[static_cast<size_t>(m) * Kw + w0 + 1] = sum;
+    if (lane == 0) out.S[static_cast<size_t>(m) * Kw + w0] = sum;
+    if (lane == 32) out.S[static_cast<size_t>(m) * Kw + w0 + 1] = sum;
 }
 
 // ================================================== binary activations (XNOR)
@@ -253,54 +321,70 @@ int current_device_is_gfx950(int* is_gfx950) {
     return 0;
 }
 
+static ActOut act_out(void* act, const ActLayout& A) {
+    uint8_t* base = static_cast<uint8_t*>(act);
+    ActOut o;
+    o.planes = reinterpret_cast<uint32_t*>(base + A.off_planes);
+    o.S = reinterpret_cast<int32_t*>(base + A.off_S);
+    o.q = reinterpret_cast<int8_t*>(base + A.off_q);
+    o.qm = reinterpret_cast<int8_t*>(base + A.off_qm);
+    o.d = reinterpret_cast<float*>(base + A.off_d);
+    o.amax = reinterpret_cast<float*>(base + A.off_amax);
+    o.h = reinterpret_cast<float*>(base + A.off_h);
+    return o;
+}
+
+template <int DT>
+static void launch_quant_plain(const void* x, int M, int K, int Kw, float qmax, const ActOut& o, hipStream_t st) {
+    const dim3 grid((Kw + 7) / 8, M);
+    if (K > kAmaxOnePassK) {
+        hipLaunchKernelGGL((act_amax_kernel<DT>), dim3(M), dim3(1024), 0, st, x, K, o.amax);
+        hipLaunchKernelGGL((quant_act_kernel<DT, 0, true>), grid, dim3(256), 0, st, x, K, Kw, qmax, o,
+                           static_cast<const uint8_t*>(nullptr), static_cast<size_t>(0), 0,
+                           static_cast<unsigned long long*>(nullptr));
+    } else {
+        hipLaunchKernelGGL((quant_act_kernel<DT, 0, false>), grid, dim3(256), 0, st, x, K, Kw, qmax, o,
+                           static_cast<const uint8_t*>(nullptr), static_cast<size_t>(0), 0,
+                           static_cast<unsigned long long*>(nullptr));
+    }
+}
+
 int launch_quantize_act(const void* x, int x_dtype, int M, int K, int abits, void* act, void* stream) {
     ActLayout A = act_layout(M, K);
-    uint8_t* base = static_cast<uint8_t*>(act);
-    auto* planes = reinterpret_cast<uint32_t*>(base + A.off_planes);
-    auto* S = reinterpret_cast<int32_t*>(base + A.off_S);
-    auto* q = reinterpret_cast<int8_t*>(base + A.off_q);
-    auto* d = reinterpret_cast<float*>(base + A.off_d);
+    const ActOut o = act_out(act, A);
     const int Kw = static_cast<int>(A.Kw);
-    const dim3 grid((Kw + 7) / 8, M);
     const float qmax = static_cast<float>((1 << (abits - 1)) - 1);  // 127 for int8
+    hipStream_t st = static_cast<hipStream_t>(stream);
     if (x_dtype == BITQ_DT_F32)
-        hipLaunchKernelGGL((quant_act_kernel<BITQ_DT_F32, 0>), grid, dim3(256), 0, static_cast<hipStream_t>(stream),
-                           x, K, Kw, qmax, planes, S, q, d, nullptr, 0, 0, nullptr, nullptr);
+        launch_quant_plain<BITQ_DT_F32>(x, M, K, Kw, qmax, o, st);
     else
-        hipLaunchKernelGGL((quant_act_kernel<BITQ_DT_BF16, 0>), grid, dim3(256), 0, static_cast<hipStream_t>(stream),
-                           x, K, Kw, qmax, planes, S, q, d, nullptr, 0, 0, nullptr, nullptr);
+        launch_quant_plain<BITQ_DT_BF16>(x, M, K, Kw, qmax, o, st);
     return static_cast<int>(hipGetLastError());
 }
 
 template <int DT, int RANK>
-static void launch_quant_hgf(dim3 grid, hipStream_t st, const void* x, int K, int Kw, uint32_t* planes, int32_t* S,
-                             int8_t* q, float* d, const uint8_t* blob, size_t off_at, int Kp,
-                             unsigned long long* ws, float* h) {
-    hipLaunchKernelGGL((quant_act_kernel<DT, RANK>), grid, dim3(256), 0, st, x, K, Kw, 127.0f, planes, S, q, d, blob,
-                       off_at, Kp, ws, h);
+static void launch_quant_hgf(dim3 grid, hipStream_t st, const void* x, int K, int Kw, const ActOut& o,
+                             const uint8_t* blob, size_t off_at, int Kp, unsigned long long* ws) {
+    hipLaunchKernelGGL((quant_act_kernel<DT, RANK, false>), grid, dim3(256), 0, st, x, K, Kw, 127.0f, o, blob,
+                       off_at, Kp, ws);
 }
 
 template <int DT>
 static void launch_quant_hgf_rank(int rank, dim3 grid, hipStream_t st, const void* x, int K, int Kw,
-                                  uint32_t* planes, int32_t* S, int8_t* q, float* d, const uint8_t* blob,
-                                  size_t off_at, int Kp, unsigned long long* ws, float* h) {
+                                  const ActOut& o, const uint8_t* blob, size_t off_at, int Kp,
+                                  unsigned long long* ws) {
     switch (rank) {
-        case 8: launch_quant_hgf<DT, 8>(grid, st, x, K, Kw, planes, S, q, d, blob, off_at, Kp, ws, h); break;
-        case 16: launch_quant_hgf<DT, 16>(grid, st, x, K, Kw, planes, S, q, d, blob, off_at, Kp, ws, h); break;
-        case 32: launch_quant_hgf<DT, 32>(grid, st, x, K, Kw, planes, S, q, d, blob, off_at, Kp, ws, h); break;
-        default: launch_quant_hgf<DT, 64>(grid, st, x, K, Kw, planes, S, q, d, blob, off_at, Kp, ws, h); break;
+        case 8: launch_quant_hgf<DT, 8>(grid, st, x, K, Kw, o, blob, off_at, Kp, ws); break;
+        case 16: launch_quant_hgf<DT, 16>(grid, st, x, K, Kw, o, blob, off_at, Kp, ws); break;
+        case 32: launch_quant_hgf<DT, 32>(grid, st, x, K, Kw, o, blob, off_at, Kp, ws); break;
+        default: launch_quant_hgf<DT, 64>(grid, st, x, K, Kw, o, blob, off_at, Kp, ws); break;
     }
 }
 
 int launch_quantize_act_hgf(const void* x, int x_dtype, int M, int K, int rank, const void* w, const BlobLayout& L,
                             void* act, void* ws, void* stream) {
     ActLayout A = act_layout(M, K, rank);
-    uint8_t* base = static_cast<uint8_t*>(act);
-    auto* planes = reinterpret_cast<uint32_t*>(base + A.off_planes);
-    auto* S = reinterpret_cast<int32_t*>(base + A.off_S);
-    auto* q = reinterpret_cast<int8_t*>(base + A.off_q);
-    auto* d = reinterpret_cast<float*>(base + A.off_d);
-    auto* h = reinterpret_cast<float*>(base + A.off_h);
+    const ActOut o = act_out(act, A);
     const int Kw = static_cast<int>(A.Kw);
     const dim3 grid((Kw + 7) / 8, M);
     const uint8_t* blob = static_cast<const uint8_t*>(w);  // A^T and amax_a are read by the kernel
@@ -308,9 +392,9 @@ int launch_quantize_act_hgf(const void* x, int x_dtype, int M, int K, int rank, 
     auto* wsw = static_cast<unsigned long long*>(ws);
     const int Kp = static_cast<int>(L.Kp);
     if (x_dtype == BITQ_DT_F32)
-        launch_quant_hgf_rank<BITQ_DT_F32>(rank, grid, st, x, K, Kw, planes, S, q, d, blob, L.off_c1, Kp, wsw, h);
+        launch_quant_hgf_rank<BITQ_DT_F32>(rank, grid, st, x, K, Kw, o, blob, L.off_c1, Kp, wsw);
     else
-        launch_quant_hgf_rank<BITQ_DT_BF16>(rank, grid, st, x, K, Kw, planes, S, q, d, blob, L.off_c1, Kp, wsw, h);
+        launch_quant_hgf_rank<BITQ_DT_BF16>(rank, grid, st, x, K, Kw, o, blob, L.off_c1, Kp, wsw);
     return static_cast<int>(hipGetLastError());
 }
 

@@ -94,3 +94,4 @@ __device__ __forceinline__ int combine_planes(const int (&a)[8]) {
 }
 
 }  // namespace bitq
+

@@ -748,8 +748,11 @@ ActLayout act_layout(int M, int K, int rank) {
     A.off_planes = 0;
     A.off_S = align256(static_cast<size_t>(M * A.Kw) * 32);
     A.off_q = align256(A.off_S + static_cast<size_t>(M * A.Kw) * 4);
-    A.off_d = align256(A.off_q + static_cast<size_t>(M * A.Kp));
-    A.off_h = align256(A.off_d + 4 * static_cast<size_t>(M));
+    A.qm_pitch = A.Kp + 128;
+    A.off_qm = align256(A.off_q + static_cast<size_t>(M * A.Kp));
+    A.off_d = align256(A.off_qm + static_cast<size_t>(M * A.qm_pitch));
+    A.off_amax = align256(A.off_d + 4 * static_cast<size_t>(M));
+    A.off_h = align256(A.off_amax + 4 * static_cast<size_t>(M));
     A.total = align256(A.off_h + 4 * static_cast<size_t>(M) * rank);
     return A;
 }
@@ -824,25 +827,21 @@ Plan make_plan(const bitq_wdesc& d, int M, bool fused) {
 }
 
 MfmaShape mfma_shape(const bitq_wdesc& d, int M) {
-    // Measured on 11008x4096 and 4096x11008 W2A8 and 4096^2 ternary layers,
-    // M = 2..64: 16 rows per workgroup and 8 or 16 waves over k (about
-    // 4-8k waves in flight, each with one or two load chunks of 2 blocks),
-    // except that on layers of 8192+ rows the q operands are worth sharing
-    // by 64-row workgroups from 8 tokens on (16 waves, one block per chunk,
-    // up to 16 tokens; 8 waves, two blocks, beyond).
+    // TT token tiles of 16.  One workgroup per CU (at most kWholeRowGrid, at most
+    // one per 16-row sub-tile) of KW = 8 waves over k: two waves per SIMD,
+    // each with up to 256 registers.  Each wave issues the loads of CH
+    // blocks together: its NB / KW blocks in as few rounds as possible (of
+    // at most 4 blocks for one token tile, 2 for more), evenly filled.
     MfmaShape s{};
     s.TT = std::min(4, (M + 15) / 16);
-    const bool wide = s.TT >= 2 && d.N >= 8192;
-    const bool tall16 = s.TT == 1 && M >= 8 && d.N >= 8192;
-    if (tall16) {
-        s.RS = 4, s.KW = 16, s.CH = 1;
-    } else if (wide) {
-        s.RS = 4, s.KW = 8, s.CH = 2;
-    } else {
-        s.RS = 1, s.KW = d.N <= 8192 ? 16 : 8, s.CH = 2;
-    }
-    const int64_t tiles = round_up(d.N, kRowTile) / kRowTile;
-    s.grid = static_cast<int>(tiles * (4 / s.RS));
+    s.RS = kMfmaSubs;
+    const int64_t NB = round_up(d.K, kKBlock) / kKBlock;
+    const int64_t nsub = round_up(d.N, kRowTile) / 16;
+    s.KW = 8;
+    const int64_t cmax = s.TT == 1 ? 4 : 2;
+    const int64_t nbw = (NB + s.KW - 1) / s.KW, rounds = (nbw + cmax - 1) / cmax;
+    s.CH = static_cast<int>((nbw + rounds - 1) / rounds);
+    s.grid = static_cast<int>(std::min<int64_t>(kWholeRowGrid, nsub));
     s.block = 64 * s.KW;
     return s;
 }

@@ -16,6 +16,10 @@ constexpr int kHeaderBytes = 256;
 constexpr uint32_t kMagic = 0x51544942u;
 constexpr int kHdrHBound = 72;    // header: f32 [3] max_k |h_p[k]| (SIGN1: 1)
 constexpr int kMaxFloatK = 63 * 8 * kKBlock;  // float formats: <= 63 splits of <= 8 k blocks
+constexpr int kWholeRowGrid = 256;  // whole-row kernels: workgroups (one per CU of the MI355X)
+// LDS a whole-row kernel's workgroup claims at least: more than half of a
+// CU's 160 KB, so the 256 workgroups land on 256 distinct CUs
+constexpr int kOneWgPerCuLds = 84 * 1024;
 // HGF header fields: u64 off_c2, u32 rank, f32 alpha, f32 gate, f32 amax_a
 constexpr int kHdrOffC2 = 88, kHdrRank = 96, kHdrAlpha = 100, kHdrGate = 104, kHdrAmaxA = 108;
 constexpr int kMaxHgfK = 63 * 256;  // HGF: <= 63 runs of 256 inputs meet in one fixed-point word
@@ -38,8 +42,12 @@ BlobLayout blob_layout(const bitq_wdesc& d);
 // adds the HGF section h f32 [M][rank].
 struct ActLayout {
     int64_t M, K, Kp, Kw;
-    size_t off_planes, off_S, off_q, off_d, off_h, total;
+    int64_t qm_pitch;  // bytes between token rows of the qm section (Kp + 128)
+    size_t off_planes, off_S, off_q, off_qm, off_d, off_amax, off_h, total;
 };
+// Rows longer than this get their amax from a separate pass (act_amax_kernel)
+// instead of every workgroup of the quantizer reading the whole row.
+constexpr int kAmaxOnePassK = 16384;
 ActLayout act_layout(int M, int K, int rank = 0);
 
 // Byte layout of a binary activation buffer (see bitq_binarize_act).
@@ -64,8 +72,10 @@ struct Plan {
 Plan make_plan(const bitq_wdesc& d, int M, bool fused = false);  // fused: BITQ_F_FUSE_QUANT
 
 // Launch shape of the matrix-core kernel for M tokens: TT token tiles of 16,
-// RS row sub-tiles of 16 per workgroup, KW waves over k, CH k blocks per load
-// chunk; grid = row tiles x (4 / RS) workgroups of 64 KW lanes.
+// RS = kMfmaSubs sub-tiles of 16 rows per pass of a workgroup, KW waves over
+// k, CH k blocks whose loads a wave issues together; grid = one workgroup
+// per CU (at most one per sub-tile), of 64 KW lanes.
+constexpr int kMfmaSubs = 3;
 struct MfmaShape {
     int TT, RS, KW, CH;
     int grid, block;

@@ -1,302 +1,388 @@
 // Small-M GEMM of libbitq on the int8 matrix cores (TERNARY, W2A8, WNAM).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "bitq_device.h"
 
 namespace bitq {
 
 // ============================== small-M GEMM on the int8 matrix cores
-// With M tokens the AND+popcount work grows M-fold and the VALU path becomes
-// compute-bound from M = 2 on (measured: W2A8 11008x4096 takes 2.1 us more
-// per token; from 4 tokens on this kernel is faster).  The same integer contraction then goes to
-// v_mfma_i32_16x16x64_i8: D[16 rows][16 tokens] += A[16][64] B[64][16], with
-// A = the weight codes unpacked from their bit planes to int8 and B = the
-// int8 activations q ([ABQ] computes with the binary decomposition because
-// its target has 1-bit tensor cores; gfx950 has int8 ones, so the planes are
-// recombined into codes in registers instead).
+// With M tokens the AND+popcount work of the VALU kernel grows M-fold, so
+// from two tokens on the contraction is compute-bound there.  The same
+// integer contraction then goes to v_mfma_i32_16x16x64_i8:
+//   D[16 rows][16 tokens] += A[16][64] B[64][16]
+// with A = the weight codes unpacked from their bit planes to int8 and B =
+// the int8 activations q ([ABQ] computes with the binary decomposition
+// because its target has 1-bit tensor cores; gfx950 has int8 ones, so the
+// planes are recombined into codes instead, each weight once per launch).
 //
 // Operand layout of the instruction (checked on the device): lane l holds 16
-// int8 of A for row l % 16 and 16 int8 of B for column l % 16; byte e of
-// lanes with l / 16 = g meets byte e of B lanes with the same g (one k
+// int8 of A for row l % 16 and 16 int8 of B for column l % 16; byte e of the
+// lanes with l / 16 = g meets byte e of the B lanes with the same g (one k
 // position); D element i of lane l is row 4 (l / 16) + i, column l % 16.
-// The k position of (g, e) is chosen so that each lane reads one plane word
-// per 128-input block: in k step s (0, 1) of block b, lane group g covers
-// inputs 128 b + 32 g + 16 s + e, i.e. bits 16 s .. 16 s + 15 of plane word g
-// of its row, and the matching 16 bytes of q are one 16-byte load.
+// The k position of (g, e) is free as long as A and B agree.  Lane group g
+// takes plane word g of each 128-input block (inputs 32 g .. 32 g + 31), so
+// every lane loads one 4-byte word per plane and block and the 64 lanes read
+// 256 contiguous bytes.
 //
-// A workgroup of KW waves owns RS row sub-tiles of 16 rows and all
-// M <= 16 TT tokens; wave w takes the k blocks [NB w / KW, NB (w + 1) / KW)
-// for its RS x TT output tiles, so every lane loads distinct weight words and
-// each q operand serves RS sub-tiles.  The wave's loads are issued CH blocks
-// at a time, so one memory latency is paid per CH blocks: a wave's time is
-// about (its blocks / CH) latencies, which is why the launcher prefers many
-// short waves (RS 1, KW 8 or 16) and keeps q reuse (RS 4) for many tokens on
-// tall layers.  Per 128-group (W2A8, WNAM) the fp32 output takes delta
-// (A - z S128).  Except in the 64-row, 16-wave shape, the zero point is
-// folded into the A operand (code - z as a signed byte, row by row), so the
-// matrix cores return A - z S128 itself, exactly, and neither the group sums
-// S nor the subtraction are needed (the same value, and the same fp32 bits,
-// as delta (A - z S) computed from the exact A and S); the int32 output of
-// BITQ_F_ACC_INT32 keeps the unshifted A.
-// TERNARY keeps int32 sums over all of k.  The waves' partials are added in
-// wave order through LDS.
+// Unpack.  The planes of the word are interleaved into 2-bit fields with
+// one bit-field insert each: Z_s = (P0 >> s) with (P1 << (1 - s)) in the odd
+// bits, so field f of Z_s holds the two low code bits of input 2 f + s.  Then
+// register c of k-step s is (Z_s >> 2c) & 0x03030303, whose byte j is the
+// code of input 8 j + 2 c + s (three and four planes: nibble fields built
+// the same way, (Q >> 4i) & 0x0F0F0F0F).  A byte permute through a table
+// maps each code to its operand byte: c - z of the row's zero point (W2A8,
+// WNAM; the matrix cores then return A - z S128 itself, exactly), or the
+// ternary value (fields p + 2m: 0 -> 0, 1 -> +1, 2 -> -1).  So a code costs
+// about one VALU operation.  The activation buffer's qm section holds q in
+// the same order (input 8j + 2c + s at byte 16s + 4c + j of its word), so a
+// B operand is one 16-byte load.
+//
+// Work decomposition.  One workgroup per CU (grid = 256) owns a contiguous
+// range of 16-row sub-tiles over the whole k range, up to kMfmaSubs of them
+// per pass, and all M <= 16 TT tokens; its KW waves take the k blocks
+// w, w + KW, ...  A workgroup reads q (M K bytes, from L2) once per pass
+// and applies it to all its sub-tiles, so q costs about 256 M K bytes of L2
+// reads per launch; the weights are read once.  Ranges are dealt so that
+// the workgroups of one XCD (round-robin dispatch) hold adjacent rows and
+// share their coefficient lines in one L2.  A wave issues the loads of C
+// blocks together before computing them.  Per 128-group (W2A8, WNAM) the
+// exact group sum becomes delta (A - z S128) in fp32, added in block order;
+// TERNARY keeps int32 sums over all of k.  The waves' partials are then
+// added in wave order through LDS: y does not depend on scheduling.
 typedef int v4i32_t __attribute__((ext_vector_type(4)));
 
-// Bits 4j .. 4j + 3 of v moved to bit 0 of bytes 0..3 (nibble times
-// 1 + 2^7 + 2^14 + 2^21: the four copies do not overlap, so there are no
-// carries, and bit e of copy e lands on bit 8e).
-__device__ __forceinline__ uint32_t spread_nibble(uint32_t v, int j) {
-    return (__builtin_amdgcn_ubfe(v, 4 * j, 4) * 0x204081u) & 0x01010101u;
-}
+__device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b) { return (mask & a) | (~mask & b); }
 
-// Four int8 codes (bytes) for inputs 4j .. 4j + 3 of a 16-bit slice
-// starting at bit `lo` of the P plane words w[]: unsigned codes sum_p 2^p
-// bit_p (W2A8, WNAM) or ternary T = plus - minus (bytes 0x01 / 0xFF).
-template <int FMT, int P>
-__device__ __forceinline__ uint32_t codes4(const uint32_t (&w)[P], int lo, int j) {
-    if constexpr (FMT == BITQ_TERNARY) {
-        const uint32_t pl = spread_nibble(w[0] >> lo, j), mi = spread_nibble(w[1] >> lo, j);
-        return pl | ((mi << 8) - mi);
-    } else {
-        uint32_t c = spread_nibble(w[0] >> lo, j);
+// Code bytes of the 32 inputs of one plane word: r[4 s + c] byte j = code
+// of input 8 j + 2 c + s.  TERNARY: w = (plus, minus), code p + 2m.
+template <int P>
+__device__ __forceinline__ void unpack_codes(const uint32_t (&w)[P], uint32_t (&r)[8]) {
+    if constexpr (P <= 2) {
+        const uint32_t hi = P == 2 ? w[1] : 0u;
+        uint32_t z[2] = {bfi(0x55555555u, w[0], hi << 1), bfi(0x55555555u, w[0] >> 1, hi)};
+        // (materialized here: otherwise the compiler folds the first mask
+        // into the interleave and computes it twice)
+        asm volatile("" : "+v"(z[0]), "+v"(z[1]));
 #pragma unroll
-        for (int p = 1; p < P; ++p) c |= spread_nibble(w[p] >> lo, j) << p;
-        return c;
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) r[4 * s + c] = (z[s] >> (2 * c)) & 0x03030303u;
+    } else {
+        const uint32_t w3 = P == 4 ? w[3] : 0u;
+        const uint32_t z[2] = {bfi(0x55555555u, w[0], w[1] << 1), bfi(0x55555555u, w[0] >> 1, w[1])};
+        const uint32_t yv[2] = {bfi(0x55555555u, w[2], w3 << 1), bfi(0x55555555u, w[2] >> 1, w3)};
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            // nibble a of q[h] = code of input 4a + 2h + s (low two bits from
+            // Z_s field 2a + h, high two from the same field of Y_s)
+            const uint32_t q[2] = {bfi(0x33333333u, z[s], yv[s] << 2), bfi(0x33333333u, z[s] >> 2, yv[s])};
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 2; ++i) r[4 * s + 2 * i + h] = (q[h] >> (4 * i)) & 0x0F0F0F0Fu;
+        }
     }
 }
 
-// Everything one wave reads for one 128-input block.
-template <int P, int RS, int TT, bool GRP, bool FOLD>
+// What one wave reads for one 128-input block besides its weights.
+template <int P, int S, int TT, bool LOADC>
 struct MfmaBlock {
-    uint32_t wp[RS][P];  // plane word g of rows 16 R + li
-    v4i32_t qv[2][TT];   // q operands of the two k steps
-    uint4 cz[GRP ? RS : 1];
-    uint32_t zr[FOLD ? RS : 1];          // coefficient word of row 16 R + li (its zero point)
-    int4 s4[GRP && !FOLD ? TT : 1];      // group sums (zero point not folded)
+    v4i32_t qv[2][TT];          // B operands of the two k steps
+    uint32_t zr[LOADC ? S : 1];  // coefficient word of row li (its zero point)
+    uint4 cz[LOADC ? S : 1];    // coefficient words of rows 4 g .. 4 g + 3 (their delta)
 };
 
-template <int FMT, int P, bool ACC, int TT, int RS, int KW, int CH>
+template <int FMT, int P, bool ACC, int TT, int KW, int C>
 __global__ __launch_bounds__(64 * KW) void gemm_mfma_kernel(const uint8_t* __restrict__ blob, size_t off_c0,
-                                                            const uint8_t* __restrict__ act, size_t act_off_S,
-                                                            size_t act_off_q, size_t act_off_d, int M, int N,
-                                                            int Tb, float* __restrict__ y) {
+                                                            const uint8_t* __restrict__ act, size_t act_off_qm,
+                                                            size_t act_off_d, int M, int N, int Tb, int nsub,
+                                                            float* __restrict__ y) {
+    constexpr int S = kMfmaSubs;
     constexpr bool GRP = FMT != BITQ_TERNARY;  // per-128-group epilogue (W2A8, WNAM)
-    constexpr bool LOADC = GRP && !ACC;        // coefficients needed
-    // zero point folded into the codes; not in the 64-row, 16-wave shape
-    // (8-16 tokens on tall layers), where the extra per-row coefficient
-    // loads cost more than the saved epilogue (W2A8 11008x4096, M = 8:
-    // 11.4 -> 11.9 us folded)
-    constexpr bool FOLD = LOADC && !(RS == 4 && KW == 16);
-    // waves 1..KW-1 hand their partials to wave 0: RS row sub-tiles x TT
-    // token tiles x 4 values per lane
-    constexpr int NV = RS * TT * 4;
-    __shared__ float s_part[KW - 1][NV][64];
+    constexpr bool LOADC = GRP && !ACC;        // coefficients needed (fold + delta)
+    constexpr bool PERM = FMT == BITQ_TERNARY || (LOADC && P <= 3);  // codes through a byte table
+    constexpr int NV = S * TT * 4;             // partial outputs per lane
+    // the waves' partials; at least kOneWgPerCuLds bytes, so that no CU
+    // holds a second workgroup while another CU holds none
+    constexpr int PART = KW * NV * 64;
+    __shared__ float s_part_mem[PART * 4 > kOneWgPerCuLds ? PART : kOneWgPerCuLds / 4];
+    float (*s_part)[NV][64] = reinterpret_cast<float (*)[NV][64]>(s_part_mem);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // (the wave index through readfirstlane: the compiler then knows it is
+    // uniform and keeps the block and tile arithmetic in scalar registers)
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, li = lane & 15;
-    const int t = blockIdx.x / (4 / RS);           // 64-row tile
-    const int r0 = 16 * RS * (blockIdx.x % (4 / RS));  // first row of the group inside the tile
-    const int NB = Tb, Kp = Tb * 128, Kw = Tb * 4;
-    const int bbeg = (NB * wave) / KW, bend = (NB * (wave + 1)) / KW;
-    const uint8_t* tile_planes = blob + kHeaderBytes + static_cast<size_t>(t) * Tb * P * 1024;
-    const uint32_t* tile_coef = reinterpret_cast<const uint32_t*>(blob + off_c0) + static_cast<size_t>(t) * Tb * 64;
-    const int8_t* q = reinterpret_cast<const int8_t*>(act + act_off_q);
-    const int32_t* S = reinterpret_cast<const int32_t*>(act + act_off_S);
+    // sub-tile range: the workgroups of XCD x (blockIdx % 8 = x) take the
+    // ranges 32 x .. 32 x + 31 in order (nsub <= 2^16, grid <= 256)
+    const uint32_t G = gridDim.x, ns_u = static_cast<uint32_t>(nsub);
+    const uint32_t per = G / 8, rid = G % 8 == 0 ? (blockIdx.x % 8) * per + blockIdx.x / 8 : blockIdx.x;
+    const int s_beg = static_cast<int>(ns_u * rid / G), s_end = static_cast<int>(ns_u * (rid + 1) / G);
+    const int nbw = wave < Tb ? (Tb - wave + KW - 1) / KW : 0;  // k blocks of this wave
+    const int Kp = Tb * 128;
+    const int8_t* qm = reinterpret_cast<const int8_t*>(act + act_off_qm);
     const float* ad = reinterpret_cast<const float*>(act + act_off_d);
+    const uint32_t* coef = reinterpret_cast<const uint32_t*>(blob + off_c0);
     int mrow[TT];  // this lane's token of each token tile (clamped for loads)
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) mrow[tt] = min(16 * tt + li, M - 1);
 
-    v4i32_t acc[RS][TT];
-    float yacc[RS][TT][4];
+    for (int sb = s_beg; sb < s_end; sb += S) {
+        const int ns = min(S, s_end - sb);
+        // per sub-tile: its 64-row tile and first row inside it (surplus
+        // sub-tiles re-read the last one and store nothing)
+        int tl[S], r0[S];
 #pragma unroll
-    for (int R = 0; R < RS; ++R)
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-            acc[R][tt] = v4i32_t{0, 0, 0, 0};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) yacc[R][tt][i] = 0.0f;
+        for (int R = 0; R < S; ++R) {
+            const int sg = sb + min(R, ns - 1);
+            tl[R] = sg >> 2;
+            r0[R] = 16 * (sg & 3);
         }
-
-    auto load = [&](MfmaBlock<P, RS, TT, GRP, FOLD>& L, int b) __attribute__((always_inline)) {
+        v4i32_t acc[S][TT];
+        float yacc[S][TT][4];
 #pragma unroll
-        for (int R = 0; R < RS; ++R)
+        for (int R = 0; R < S; ++R)
 #pragma unroll
-            for (int p = 0; p < P; ++p)
-                L.wp[R][p] = *reinterpret_cast<const uint32_t*>(tile_planes + (b * P + p) * 1024 +
-                                                                (r0 + 16 * R + li) * 16 + 4 * g);
+            for (int tt = 0; tt < TT; ++tt) {
+                acc[R][tt] = v4i32_t{0, 0, 0, 0};
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int tt = 0; tt < TT; ++tt)
-                L.qv[s][tt] = *reinterpret_cast<const v4i32_t*>(q + static_cast<size_t>(mrow[tt]) * Kp + 128 * b +
-                                                                32 * g + 16 * s);
-        if constexpr (LOADC) {
-#pragma unroll
-            for (int R = 0; R < RS; ++R) {
-                L.cz[R] = *reinterpret_cast<const uint4*>(tile_coef + b * 64 + r0 + 16 * R + 4 * g);
-                if (FOLD) L.zr[R] = tile_coef[b * 64 + r0 + 16 * R + li];
+                for (int i = 0; i < 4; ++i) yacc[R][tt][i] = 0.0f;
             }
-            if (!FOLD) {
+
+        using Blk = MfmaBlock<P, S, TT, LOADC>;
+        auto load = [&](Blk& L, int b) __attribute__((always_inline)) {
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
                 for (int tt = 0; tt < TT; ++tt)
-                    L.s4[tt] = *reinterpret_cast<const int4*>(S + static_cast<size_t>(mrow[tt]) * Kw + 4 * b);
-            }
-        }
-    };
-
-    auto compute = [&](const MfmaBlock<P, RS, TT, GRP, FOLD>& L, int b) __attribute__((always_inline)) {
+                    L.qv[s2][tt] = *reinterpret_cast<const v4i32_t*>(
+                        qm + static_cast<size_t>(mrow[tt]) * (Kp + 128) + 128 * b + 32 * g + 16 * s2);
+            if constexpr (LOADC) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-#pragma unroll
-            for (int R = 0; R < RS; ++R) {
-                v4i32_t a;
-                if constexpr (FOLD) {
-                    // codes minus the row's zero point, as signed bytes: (c | 0x80) - z
-                    // cannot borrow (c, z < 16), and ^ 0x80 turns c - z + 128 into c - z
-                    const uint32_t zb = static_cast<uint32_t>(f16_bits_to_f32(L.zr[R] >> 16)) * 0x01010101u;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        a[j] = static_cast<int>(((codes4<FMT, P>(L.wp[R], 16 * s, j) | 0x80808080u) - zb) ^ 0x80808080u);
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) a[j] = static_cast<int>(codes4<FMT, P>(L.wp[R], 16 * s, j));
+                for (int R = 0; R < S; ++R) {
+                    const uint32_t* c = coef + (static_cast<size_t>(tl[R]) * Tb + b) * 64 + r0[R];
+                    L.zr[R] = c[li];
+                    L.cz[R] = *reinterpret_cast<const uint4*>(c + 4 * g);
                 }
-#pragma unroll
-                for (int tt = 0; tt < TT; ++tt)
-                    acc[R][tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, L.qv[s][tt], acc[R][tt], 0, 0, 0);
             }
-        }
-        if constexpr (GRP) {
-            if constexpr (ACC) {  // exact group sums A[m][n][b]
+        };
+
+        auto compute = [&](Blk& L, int b, auto word) __attribute__((always_inline)) {
+            // every loaded value passes an empty asm here, so no use of this
+            // block's data (and no wait for it) moves above the previous block's
 #pragma unroll
-                for (int R = 0; R < RS; ++R)
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                for (int tt = 0; tt < TT; ++tt) asm volatile("" : "+v"(L.qv[s2][tt]));
+            if constexpr (LOADC) {
+#pragma unroll
+                for (int R = 0; R < S; ++R) asm volatile("" : "+v"(L.zr[R]), "+v"(L.cz[R].x), "+v"(L.cz[R].y),
+                                                         "+v"(L.cz[R].z), "+v"(L.cz[R].w));
+            }
+#pragma unroll
+            for (int R = 0; R < S; ++R) {
+                uint32_t r[8];
+                uint32_t wq[P];
+#pragma unroll
+                for (int p = 0; p < P; ++p) wq[p] = word(R, p);
+                unpack_codes<P>(wq, r);
+                if constexpr (PERM) {
+                    // operand byte of each code through a byte table (v_perm_b32)
+                    uint32_t tlo, thi = 0u;
+                    if constexpr (FMT == BITQ_TERNARY) {
+                        tlo = 0x00FF0100u;  // p + 2m = 0, 1, 2 -> 0, +1, -1
+                    } else {
+                        // bytes e - z for e = 0..7 ((e | 0x80) - z cannot borrow; ^ 0x80 takes 0x80 off);
+                        // z in every byte by a byte permute; codes of one or two planes are below 4
+                        const uint32_t z = static_cast<uint32_t>(f16_bits_to_f32(L.zr[R] >> 16));
+                        const uint32_t zb = __builtin_amdgcn_perm(0u, z, 0x00000000u);
+                        tlo = (0x83828180u - zb) ^ 0x80808080u;
+                        if constexpr (P >= 3) thi = (0x87868584u - zb) ^ 0x80808080u;
+                    }
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) r[e] = __builtin_amdgcn_perm(thi, tlo, r[e]);
+                } else if constexpr (LOADC) {  // four planes: codes up to 15, c - z by arithmetic
+                    const uint32_t z = static_cast<uint32_t>(f16_bits_to_f32(L.zr[R] >> 16));
+                    const uint32_t zb = __builtin_amdgcn_perm(0u, z, 0x00000000u);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) r[e] = ((r[e] | 0x80808080u) - zb) ^ 0x80808080u;
+                }
+                // (ACC: the unshifted codes, so the int32 output is A itself)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const v4i32_t a = v4i32_t{static_cast<int>(r[4 * s2]), static_cast<int>(r[4 * s2 + 1]),
+                                              static_cast<int>(r[4 * s2 + 2]), static_cast<int>(r[4 * s2 + 3])};
 #pragma unroll
                     for (int tt = 0; tt < TT; ++tt)
+                        acc[R][tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, L.qv[s2][tt], acc[R][tt], 0, 0, 0);
+                }
+            }
+            if constexpr (GRP) {
+                if constexpr (ACC) {  // exact group sums A[m][n][b]
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int n = 64 * t + r0 + 16 * R + 4 * g + i, m = 16 * tt + li;
-                            if (n < N && m < M)
-                                reinterpret_cast<int32_t*>(y)[(static_cast<size_t>(m) * N + n) * NB + b] = acc[R][tt][i];
-                        }
-            } else {
+                    for (int R = 0; R < S; ++R)
 #pragma unroll
-                for (int tt = 0; tt < TT; ++tt) {
-                    const float S128 =
-                        FOLD ? 0.0f : static_cast<float>((L.s4[tt].x + L.s4[tt].y) + (L.s4[tt].z + L.s4[tt].w));
+                        for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-                    for (int R = 0; R < RS; ++R) {
+                            for (int i = 0; i < 4; ++i) {
+                                const int n = 16 * (sb + R) + 4 * g + i, m = 16 * tt + li;
+                                if (R < ns && n < N && m < M)
+                                    reinterpret_cast<int32_t*>(y)[(static_cast<size_t>(m) * N + n) * Tb + b] =
+                                        acc[R][tt][i];
+                            }
+                } else {
+#pragma unroll
+                    for (int R = 0; R < S; ++R) {
                         const uint32_t c[4] = {L.cz[R].x, L.cz[R].y, L.cz[R].z, L.cz[R].w};
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             const float delta = f16_bits_to_f32(c[i]);
-                            if (FOLD) {
-                                yacc[R][tt][i] += delta * static_cast<float>(acc[R][tt][i]);  // acc = A - z S
-                            } else {
-                                const float z = f16_bits_to_f32(c[i] >> 16);
-                                yacc[R][tt][i] += delta * (static_cast<float>(acc[R][tt][i]) - z * S128);
-                            }
+#pragma unroll
+                            for (int tt = 0; tt < TT; ++tt)  // acc = A - z S128 (one fused multiply-add)
+                                yacc[R][tt][i] = __builtin_fmaf(delta, static_cast<float>(acc[R][tt][i]), yacc[R][tt][i]);
                         }
                     }
                 }
+#pragma unroll
+                for (int R = 0; R < S; ++R)
+#pragma unroll
+                    for (int tt = 0; tt < TT; ++tt) acc[R][tt] = v4i32_t{0, 0, 0, 0};
             }
+        };
+
+        // Weights as 16-byte loads: the pieces (block i of the round, sub-tile
+        // R, plane p), m = (i S + R) P + p, go 4 to a load, lane (j, r) taking
+        // row r of piece 4 t + j (its 4 plane words).  A 4 x 4 transpose across
+        // the lane groups (two 32-lane and two 16-lane swaps) then gives lane
+        // (g, li) word g of row li of each of the 4 pieces: the operand layout.
+        auto round = [&](auto cint, int i0) __attribute__((always_inline)) {
+            constexpr int CC = decltype(cint)::value;
+            constexpr int NPC = CC * S * P, NI = (NPC + 3) / 4;
+            // loads, all unconditional: each block's q and coefficients
+            // (L2-resident, small) first, then the weight stream
+            Blk L[CC];
 #pragma unroll
-            for (int R = 0; R < RS; ++R)
+            for (int i = 0; i < CC; ++i) load(L[i], wave + KW * (i0 + i));
+            uint4 wr[NI];
 #pragma unroll
-                for (int tt = 0; tt < TT; ++tt) acc[R][tt] = v4i32_t{0, 0, 0, 0};
+            for (int t = 0; t < NI; ++t) {
+                const int m = min(4 * t + g, NPC - 1);  // (surplus slots re-read the last piece)
+                const int i = m / (S * P), R = (m / P) % S, p = m % P;
+                const int sg = sb + min(R, ns - 1), b = wave + KW * (i0 + i);
+                const size_t off = ((static_cast<size_t>(sg >> 2) * Tb + b) * P + p) * 1024 + (16 * (sg & 3) + li) * 16;
+                wr[t] = *reinterpret_cast<const uint4*>(blob + kHeaderBytes + off);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            uint32_t wt[NI][4];
+#pragma unroll
+            for (int i = 0; i < CC; ++i) {
+                // transpose the loads whose first piece belongs to block i
+                // (the wait for them is here)
+#pragma unroll
+                for (int t = 0; t < NI; ++t) {
+                    if ((4 * t) / (S * P) != i) continue;
+                    uint32_t a0 = wr[t].x, a1 = wr[t].y, a2 = wr[t].z, a3 = wr[t].w;
+                    asm volatile("" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3));
+                    const auto s02 = __builtin_amdgcn_permlane32_swap(a0, a2, false, false);
+                    const auto s13 = __builtin_amdgcn_permlane32_swap(a1, a3, false, false);
+                    const auto s01 = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
+                    const auto s23 = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
+                    wt[t][0] = s01[0];
+                    wt[t][1] = s01[1];
+                    wt[t][2] = s23[0];
+                    wt[t][3] = s23[1];
+                }
+                compute(L[i], wave + KW * (i0 + i), [&](int R, int p) __attribute__((always_inline)) {
+                    const int m = (i * S + R) * P + p;
+                    return wt[m / 4][m % 4];
+                });
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        // whole rounds of C blocks, then the wave's remaining blocks one at
+        // a time: no slot is ever surplus, so nothing is predicated
+        int i0 = 0;
+        for (; i0 + C <= nbw; i0 += C) round(std::integral_constant<int, C>{}, i0);
+        for (; i0 < nbw; ++i0) round(std::integral_constant<int, 1>{}, i0);
+
+        if constexpr (!(GRP && ACC)) {
+            // ---- the waves' partials, added in wave order
+#pragma unroll
+            for (int R = 0; R < S; ++R)
+#pragma unroll
+                for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        s_part[wave][(R * TT + tt) * 4 + i][lane] =
+                            GRP ? yacc[R][tt][i] : __int_as_float(acc[R][tt][i]);
+            __syncthreads();
+            const float gamma = (FMT == BITQ_TERNARY && !ACC) ? *reinterpret_cast<const float*>(blob + off_c0) : 1.0f;
+            for (int idx = tid; idx < NV * 64; idx += 64 * KW) {
+                const int k = idx >> 6, l = idx & 63;
+                const int R = k / (4 * TT), tt = (k / 4) % TT, i = k % 4;
+                const int n = 16 * (sb + R) + 4 * (l >> 4) + i, m = 16 * tt + (l & 15);
+                float vf = 0.0f;
+                int vi = 0;
+#pragma unroll
+                for (int w = 0; w < KW; ++w) {
+                    if (GRP)
+                        vf += s_part[w][k][l];
+                    else
+                        vi += __float_as_int(s_part[w][k][l]);
+                }
+                if (R < ns && n < N && m < M) {
+                    if (GRP)
+                        y[static_cast<size_t>(m) * N + n] = ad[m] * vf;
+                    else if (ACC)
+                        reinterpret_cast<int32_t*>(y)[static_cast<size_t>(m) * N + n] = vi;
+                    else
+                        y[static_cast<size_t>(m) * N + n] = gamma * ad[m] * static_cast<float>(vi);
+                }
+            }
+            __syncthreads();
         }
-    };
+    }
+}
 
-    for (int c0 = bbeg; c0 < bend; c0 += CH) {
-        // the chunk's loads are issued together (surplus slots re-read the
-        // last block and are skipped below)
-        MfmaBlock<P, RS, TT, GRP, FOLD> L[CH];
-#pragma unroll
-        for (int i = 0; i < CH; ++i) load(L[i], min(c0 + i, bend - 1));
-#pragma unroll
-        for (int i = 0; i < CH; ++i)
-            if (c0 + i < bend) compute(L[i], c0 + i);
-    }
-    if constexpr (GRP && ACC) return;
+template <int FMT, int P, bool ACC, int TT, int KW, int C>
+static void launch_mfma_1(const bitq_wdesc& d, const BlobLayout& L, const MfmaShape& sh, const void* w,
+                          const void* act, int M, float* y, hipStream_t st) {
+    ActLayout A = act_layout(M, d.K, d.rank);
+    hipLaunchKernelGGL((gemm_mfma_kernel<FMT, P, ACC, TT, KW, C>), dim3(sh.grid), dim3(64 * KW), 0, st,
+                       static_cast<const uint8_t*>(w), L.off_c0, static_cast<const uint8_t*>(act), A.off_qm, A.off_d,
+                       M, d.N, static_cast<int>(L.Tb), static_cast<int>(L.Np / 16), y);
+}
 
-    // ---- the waves' partials, added in wave order
-    if (wave > 0) {
-#pragma unroll
-        for (int R = 0; R < RS; ++R)
-#pragma unroll
-            for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int v = (R * TT + tt) * 4 + i;
-                    s_part[wave - 1][v][lane] = GRP ? yacc[R][tt][i] : __int_as_float(acc[R][tt][i]);
-                }
+// The (KW, C) pairs built for each token-tile count; mfma_shape picks one.
+template <int FMT, int P, bool ACC, int TT>
+static void launch_mfma_kw(const bitq_wdesc& d, const BlobLayout& L, const MfmaShape& sh, const void* w,
+                           const void* act, int M, float* y, hipStream_t st) {
+#define BITQ_MFMA_CASE(KW_, C_) \
+    if (sh.KW == KW_ && sh.CH == C_) return launch_mfma_1<FMT, P, ACC, TT, KW_, C_>(d, L, sh, w, act, M, y, st)
+    if constexpr (TT == 1) {
+        BITQ_MFMA_CASE(8, 1);
+        BITQ_MFMA_CASE(8, 2);
+        BITQ_MFMA_CASE(8, 3);
+        BITQ_MFMA_CASE(8, 4);
+    } else {
+        BITQ_MFMA_CASE(8, 1);
+        BITQ_MFMA_CASE(8, 2);
     }
-    __syncthreads();
-    if (wave != 0) return;
-    const float gamma = (FMT == BITQ_TERNARY && !ACC) ? *reinterpret_cast<const float*>(blob + off_c0) : 1.0f;
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-        const int m = 16 * tt + li;
-        const float scale = ACC ? 1.0f : (FMT == BITQ_TERNARY ? gamma * ad[mrow[tt]] : ad[mrow[tt]]);
-#pragma unroll
-        for (int R = 0; R < RS; ++R)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int v = (R * TT + tt) * 4 + i;
-                const int n = 64 * t + r0 + 16 * R + 4 * g + i;
-                if (GRP) {
-                    float tot = yacc[R][tt][i];
-#pragma unroll
-                    for (int w = 0; w < KW - 1; ++w) tot += s_part[w][v][lane];
-                    if (n < N && m < M) y[static_cast<size_t>(m) * N + n] = scale * tot;
-                } else {
-                    int tot = acc[R][tt][i];
-#pragma unroll
-                    for (int w = 0; w < KW - 1; ++w) tot += __float_as_int(s_part[w][v][lane]);
-                    if (n < N && m < M) {
-                        if (ACC)
-                            reinterpret_cast<int32_t*>(y)[static_cast<size_t>(m) * N + n] = tot;
-                        else
-                            y[static_cast<size_t>(m) * N + n] = scale * static_cast<float>(tot);
-                    }
-                }
-            }
-    }
+#undef BITQ_MFMA_CASE
+    launch_mfma_1<FMT, P, ACC, TT, 8, 2>(d, L, sh, w, act, M, y, st);
 }
 
 template <int FMT, int P, bool ACC>
 static void launch_mfma(const bitq_wdesc& d, const BlobLayout& L, const void* w, const void* act, int M, float* y,
                         hipStream_t st) {
-    ActLayout A = act_layout(M, d.K, d.rank);
-    const auto* wb = static_cast<const uint8_t*>(w);
-    const auto* ab = static_cast<const uint8_t*>(act);
-    const int Tb = static_cast<int>(L.Tb);
     const MfmaShape sh = mfma_shape(d, M);
-#define BITQ_MFMA(TT_, RS, KW, CH)                                                                             \
-    hipLaunchKernelGGL((gemm_mfma_kernel<FMT, P, ACC, TT_, RS, KW, CH>), dim3(sh.grid), dim3(sh.block), 0, st, \
-                       wb, L.off_c0, ab, A.off_S, A.off_q, A.off_d, M, d.N, Tb, y)
-#define BITQ_MFMA_TT(TT_)                      \
-    do {                                       \
-        if (sh.RS == 4)                        \
-            BITQ_MFMA(TT_, 4, 8, 2);           \
-        else if (sh.KW == 16)                  \
-            BITQ_MFMA(TT_, 1, 16, 2);          \
-        else                                   \
-            BITQ_MFMA(TT_, 1, 8, 2);           \
-    } while (0)
     switch (sh.TT) {
-        case 1:
-            if (sh.RS == 4)
-                BITQ_MFMA(1, 4, 16, 1);
-            else
-                BITQ_MFMA_TT(1);
-            break;
-        case 2: BITQ_MFMA_TT(2); break;
-        case 3: BITQ_MFMA_TT(3); break;
-        default: BITQ_MFMA_TT(4); break;
+        case 1: launch_mfma_kw<FMT, P, ACC, 1>(d, L, sh, w, act, M, y, st); break;
+        case 2: launch_mfma_kw<FMT, P, ACC, 2>(d, L, sh, w, act, M, y, st); break;
+        case 3: launch_mfma_kw<FMT, P, ACC, 3>(d, L, sh, w, act, M, y, st); break;
+        default: launch_mfma_kw<FMT, P, ACC, 4>(d, L, sh, w, act, M, y, st); break;
     }
-#undef BITQ_MFMA_TT
-#undef BITQ_MFMA
 }
 
 template <bool ACC>

@@ -274,7 +274,13 @@ bitq_status bitq_quantize_weights_opts(const bitq_wdesc* desc, const float* W,
  *                          byte of q[m][32w + i] at bit i
  *   S      i32 [M][Kw]     sum of q over each run of 32 inputs
  *   q      i8  [M][Kp]     quantized activations (0 beyond K)
+ *   qm     i8  [M][Kp + 128]  the same codes, the bytes of each 32-input
+ *                          word in the order the matrix-core kernel reads them:
+ *                          input 8j + 2c + s of a word at byte 16s + 4c + j;
+ *                          rows Kp + 128 bytes apart (the last 128 bytes of a
+ *                          row are unused)
  *   d      f32 [M]         dequantization step amax/Qm (Qm = 127 for int8)
+ *   amax   f32 [M]         max_k |x[m][k]|
  * With m-bit activations (bitq_quantize_act_bits) q lies in [-Qm, Qm],
  * Qm = 2^(m-1) - 1; the byte's bits m-1..7 then all equal the sign, and the
  * GEMV uses planes 0..m-2 and plane 7 (weight -2^(m-1)).

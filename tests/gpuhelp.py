@@ -57,8 +57,23 @@ def parse_act(buf: np.ndarray, M: int, K: int) -> dict:
     planes = buf[L["off_planes"]:L["off_planes"] + M * Kw * 32].view(np.uint32).reshape(M, Kw, 8)
     S = buf[L["off_S"]:L["off_S"] + M * Kw * 4].view(np.int32).reshape(M, Kw)
     q = buf[L["off_q"]:L["off_q"] + M * Kp].view(np.int8).reshape(M, Kp)
+    qm = buf[L["off_qm"]:L["off_qm"] + M * L["qm_pitch"]].view(np.int8).reshape(M, L["qm_pitch"])[:, :Kp]
     d = buf[L["off_d"]:L["off_d"] + 4 * M].view(np.float32)
-    return dict(planes=planes, S=S, q=q, d=d, Kw=Kw, Kp=Kp)
+    amax = buf[L["off_amax"]:L["off_amax"] + 4 * M].view(np.float32)
+    return dict(planes=planes, S=S, q=q, qm=qm, d=d, amax=amax, Kw=Kw, Kp=Kp)
+
+
+# Byte position of input i of a 32-input word in the activation buffer's qm
+# section (include/bitq.h: input 8j + 2c + s at byte 16s + 4c + j)
+QM_POS = np.array([16 * (i & 1) + 4 * ((i >> 1) & 3) + (i >> 3) for i in range(32)])
+
+
+def qm_from_q(q: np.ndarray) -> np.ndarray:
+    """The qm section the header's layout gives for codes q [M, Kp]."""
+    M, Kp = q.shape
+    out = np.empty_like(q)
+    out.reshape(M, Kp // 32, 32)[:, :, QM_POS] = q.reshape(M, Kp // 32, 32)
+    return out
 
 
 def run_gemv(desc, blob_dev, x_dev, x_dtype, M=1, flags=0, out_elems=None, ws=None):

@@ -13,7 +13,7 @@ import pytest
 import bit_plane_gemv_amd as bq
 from oracle import act as oact, gemv as og, weights as ow, bitserial
 import synth
-from gpuhelp import (assert_within, dev_blob, parse_act, quantize_act_dev, run_gemv, say, to_dev, torch,
+from gpuhelp import (assert_within, dev_blob, parse_act, qm_from_q, quantize_act_dev, run_gemv, say, to_dev, torch,
                      workspace)
 
 pytestmark = pytest.mark.gpu
@@ -45,6 +45,9 @@ def _act_matches(got, x_f32, K, abits=8):
     assert np.all(got["planes"][:, Kw_real:, :] == 0), "planes padding"
     assert np.array_equal(got["S"][:, :Kw_real], oact.group_sums(q, 32)), "S"
     assert np.all(got["S"][:, Kw_real:] == 0)
+    assert np.array_equal(got["qm"], qm_from_q(got["q"])), "qm (the matrix-core order of q)"
+    amax = np.max(np.abs(np.asarray(x_f32, np.float32)), axis=1)
+    assert np.array_equal(got["amax"].view(np.uint32), amax.view(np.uint32)), "amax"
 
 
 @pytest.mark.parametrize("M,K", [(1, 4096), (1, 224), (16, 512), (64, 11008), (3, 32)])
@@ -54,6 +57,20 @@ def test_act_quant_bitexact_bf16(M, K):
     if M > 2:
         bits[1] = 0                                           # an all-zero token
         xf[1] = 0
+    _check_act(bits, xf, M, K)
+
+
+@pytest.mark.parametrize("M,K,f32", [(2, 16416, False), (3, 32768, True), (1, 1 << 20, False)])
+def test_act_quant_long_rows(M, K, f32):
+    # K above 16384: amax from a pass of its own, then every workgroup reads
+    # only its own inputs; the sections are the same bits
+    say("act_quant long rows", M, K, f32)
+    if f32:
+        xf = synth.gaussian_f32(np.random.default_rng(K + M), (M, K), 3.0)
+        bits = xf
+    else:
+        bits, xf = synth.random_bf16(np.random.default_rng(K + M), (M, K))
+    xf[0, K - 1] = bits[0, K - 1] = 0                         # amax elsewhere in the row
     _check_act(bits, xf, M, K)
 
 
@@ -195,7 +212,7 @@ def test_rabit_gemv_small(N, K, P):
     _rabit_case(N, K, P)
 
 
-@pytest.mark.parametrize("N,K,P", [(200, 32256, 2), (256, 32768, 1), (70, 64512, 1)])
+@pytest.mark.parametrize("N,K,P", [(200, 32256, 2), (256, 32768, 1), (70, 64512, 1), (136, 20096, 3)])
 def test_rabit_gemv_many_splits(N, K, P):
     # 63 splits (the most the split-k arrival count holds), 8 k blocks per
     # split, and the largest K of the float formats
@@ -229,6 +246,39 @@ def test_rabit_split_k_deterministic_and_workspace_reuse():
         assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
     y_ref, tol = og.gemv_rabit(B, g, h, x)
     assert_within(outs[0][None, :], y_ref, tol, "rabit determinism")
+
+
+@pytest.mark.parametrize("N,K,P", [(12352, 256, 2), (28672, 384, 1), (16, 4096, 2), (4160, 1024, 3)])
+def test_rabit_gemv_row_ranges(N, K, P):
+    # many row groups (the last one partial), a layer of one row tile, and
+    # three paths on a ragged N
+    say("rabit row ranges", N, K, P)
+    _rabit_case(N, K, P, seed=4)
+
+
+@pytest.mark.parametrize("fmt", ["rabit", "sign"])
+def test_float_gemv_nan_input_propagates(fmt):
+    """A NaN input makes every output row NaN (each row adds +-h x_k for every
+    k; the split-k bound is NaN too); the rows of a NaN-free call are finite."""
+    N, K = 300, 1056
+    say("nan propagation", fmt)
+    t = torch()
+    W = synth.gaussian_f32(np.random.default_rng(5), (N, K), 0.02)
+    x = synth.gaussian_f32(np.random.default_rng(6), (1, K), 1.0)[0].copy()
+    if fmt == "rabit":
+        B, g, h = ow.quantize_rabit(W, paths=2)
+        desc = bq.wdesc(bq.RABIT, N, K, planes=2)
+        blob = bq.pack_weights(desc, sign=B, g=g, h=h)
+    else:
+        B, alpha = ow.quantize_sign(W)
+        desc = bq.wdesc(bq.SIGN1, N, K)
+        blob = bq.pack_weights(desc, sign=B, alpha=alpha)
+    bd = dev_blob(blob)
+    y0 = run_gemv(desc, bd, to_dev(x), bq.DT_F32)
+    assert np.all(np.isfinite(y0))
+    x[777] = np.nan
+    y1 = run_gemv(desc, bd, to_dev(x), bq.DT_F32)
+    assert np.all(np.isnan(y1))
 
 
 def test_rabit_gemv_svid_refined_blob():
@@ -668,6 +718,17 @@ def test_mfma_ragged(fmt, N, K, M):
     say("mfma ragged", fmt, N, K, M)
     W = synth.gaussian_f32(np.random.default_rng(N * K + M), (N, K), 0.02)
     xs, xf = synth.random_bf16(np.random.default_rng(M + 3), (M, K))
+    _int_case(fmt, N, K, M, W, xs, xf)
+
+
+@pytest.mark.parametrize("fmt,N,K,M", [(bq.W2A8, 12352, 256, 40), (bq.TERNARY, 13000, 384, 64),
+                                       (bq.W2A8, 16, 4096, 16), (bq.W2A8, 4160, 1152, 4)])
+def test_mfma_row_ranges(fmt, N, K, M):
+    # more 16-row sub-tiles than one pass of the 256 workgroups holds (several
+    # passes, the last one partial), fewer sub-tiles than workgroups, ragged N
+    say("mfma row ranges", fmt, N, K, M)
+    W = synth.gaussian_f32(np.random.default_rng(N + K + M), (N, K), 0.02)
+    xs, xf = synth.random_bf16(np.random.default_rng(M + 11), (M, K))
     _int_case(fmt, N, K, M, W, xs, xf)
 
 
