@@ -64,7 +64,14 @@ METRIC = "packed-weight GB/s & % HBM peak, bit-plane GEMV 11008x4096 M=1; us/lay
 # kernel of known size; profiles/ holds the runs).  Each entry is valid only
 # for the kernel source it was measured on (first 16 hex digits of the
 # sha256 of that source file); otherwise traffic is reported as null.
-MEASURED_TRAFFIC: dict = {}
+MEASURED_TRAFFIC: dict = {
+    "rabit": {"source": "bitq_sign.hip", "sha16": "ba906aeaa6be2c6a", "bytes_per_launch": 13460480,
+              "profile": "profiles/gemv_sign_kernel_rabit_11008x4096.md"},
+    "w2a8": {"source": "bitq_bits.hip", "sha16": "acae8bcee832dc66", "bytes_per_launch": 12829696,
+             "profile": "profiles/gemv_bits_nr_kernel_w2a8_11008x4096.md"},
+    "w2a8+fuse": {"source": "bitq_bits.hip", "sha16": "acae8bcee832dc66", "bytes_per_launch": 12880896,
+                  "profile": "profiles/gemv_bits_nr_kernel_fused_w2a8_11008x4096.md"},
+}
 
 
 def source_sha(name: str) -> str:
