@@ -93,5 +93,34 @@ __device__ __forceinline__ int combine_planes(const int (&a)[8]) {
     return r;
 }
 
-}  // namespace bitq
+// Buffer loads: a 128-bit descriptor (base address in scalar registers and a
+// byte range), a per-lane 32-bit offset and a wave-uniform 32-bit offset.
+// The address arithmetic then stays out of the vector ALUs (no 64-bit
+// per-lane adds).  The last descriptor word is the raw-buffer format word of
+// the CDNA family.  Callers keep every access inside [base, base + bytes).
+// (base and range pass through readfirstlane: they are wave-uniform, and
+// the compiler then keeps the descriptor in scalar registers instead of
+// looping over the lanes' values at each load)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+    void* ub = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(ub, static_cast<short>(0),
+                                             static_cast<int>(__builtin_amdgcn_readfirstlane(bytes)), 0x00020000);
+}
+// A byte count as a descriptor range (at most 2^32 - 16), in integer
+// arithmetic (a min() over size_t here went through fp64 compares).
+__device__ __forceinline__ uint32_t range_u32(size_t bytes) {
+    return bytes < 0xFFFFFFF0u ? static_cast<uint32_t>(bytes) : 0xFFFFFFF0u;
+}
+__device__ __forceinline__ uint32_t buffer_load_u32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(voff), static_cast<int>(soff), 0);
+}
+__device__ __forceinline__ uint4 buffer_load_u128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), static_cast<int>(soff), 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 
+}  // namespace bitq

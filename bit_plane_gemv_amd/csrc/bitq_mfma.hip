@@ -120,13 +120,25 @@ __global__ __launch_bounds__(64 * KW) void gemm_mfma_kernel(const uint8_t* __res
     const uint32_t per = G / 8, rid = G % 8 == 0 ? (blockIdx.x % 8) * per + blockIdx.x / 8 : blockIdx.x;
     const int s_beg = static_cast<int>(ns_u * rid / G), s_end = static_cast<int>(ns_u * (rid + 1) / G);
     const int nbw = wave < Tb ? (Tb - wave + KW - 1) / KW : 0;  // k blocks of this wave
-    const int Kp = Tb * 128;
+    const int Kp = Tb * 128, Np = 16 * nsub;
     const int8_t* qm = reinterpret_cast<const int8_t*>(act + act_off_qm);
     const float* ad = reinterpret_cast<const float*>(act + act_off_d);
     const uint32_t* coef = reinterpret_cast<const uint32_t*>(blob + off_c0);
     int mrow[TT];  // this lane's token of each token tile (clamped for loads)
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) mrow[tt] = min(16 * tt + li, M - 1);
+    // Loads go through buffer descriptors: the per-lane part of each offset
+    // is computed once, the per-block part is a scalar offset, so the loads
+    // take no vector address arithmetic.  q: [M][Kp + 128] bytes.  (q of
+    // four token tiles through plain loads instead: measured on W2A8
+    // 11008x4096, the descriptor gains 7.42 -> 7.22 us at M = 4 and 8.33 ->
+    // 8.12 us at M = 16 but loses 16.30 -> 16.96 us at M = 64.)
+    constexpr bool kQDesc = TT <= 2;
+    const auto rq = buffer_rsrc(qm, static_cast<uint32_t>(M) * static_cast<uint32_t>(Kp + 128));
+    uint32_t qoff[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) qoff[tt] = static_cast<uint32_t>(mrow[tt]) * static_cast<uint32_t>(Kp + 128) + 32 * g;
+    const size_t coef_words = static_cast<size_t>(Np) * Tb, planes_bytes = static_cast<size_t>(Np / 64) * Tb * P * 1024;
 
     for (int sb = s_beg; sb < s_end; sb += S) {
         const int ns = min(S, s_end - sb);
@@ -139,6 +151,28 @@ __global__ __launch_bounds__(64 * KW) void gemm_mfma_kernel(const uint8_t* __res
             tl[R] = sg >> 2;
             r0[R] = 16 * (sg & 3);
         }
+        // descriptors over the coefficients and planes from this pass's first
+        // tile (offsets inside a pass span at most two tiles: 32 bits)
+        const size_t cw0 = static_cast<size_t>(sb >> 2) * Tb * 64, pb0 = static_cast<size_t>(sb >> 2) * Tb * P * 1024;
+        const auto rc = buffer_rsrc(coef + cw0, range_u32((coef_words - cw0) * 4));
+        const auto rw = buffer_rsrc(blob + kHeaderBytes + pb0, range_u32(planes_bytes - pb0));
+        uint32_t csub[S];  // scalar byte offset of sub-tile R's coefficient words in block 0
+#pragma unroll
+        for (int R = 0; R < S; ++R) csub[R] = static_cast<uint32_t>(((tl[R] - (sb >> 2)) * Tb) * 256 + r0[R] * 4);
+        // weight pieces of a round of CC blocks: lane part of slot t's offset
+        auto woff = [&](int CC, int t) __attribute__((always_inline)) {
+            const int m = min(4 * t + g, CC * S * P - 1);  // (surplus slots re-read the last piece)
+            const int i = m / (S * P), R = (m / P) % S, p = m % P;
+            const int sg = sb + min(R, ns - 1);
+            return static_cast<uint32_t>((((sg >> 2) - (sb >> 2)) * Tb + KW * i) * P + p) * 1024u +
+                   static_cast<uint32_t>(16 * (sg & 3) + li) * 16u;
+        };
+        constexpr int NIC = (C * S * P + 3) / 4, NI1 = (S * P + 3) / 4;
+        uint32_t woC[NIC], wo1[NI1];
+#pragma unroll
+        for (int t = 0; t < NIC; ++t) woC[t] = woff(C, t);
+#pragma unroll
+        for (int t = 0; t < NI1; ++t) wo1[t] = woff(1, t);
         v4i32_t acc[S][TT];
         float yacc[S][TT][4];
 #pragma unroll
@@ -155,15 +189,22 @@ __global__ __launch_bounds__(64 * KW) void gemm_mfma_kernel(const uint8_t* __res
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-                for (int tt = 0; tt < TT; ++tt)
-                    L.qv[s2][tt] = *reinterpret_cast<const v4i32_t*>(
-                        qm + static_cast<size_t>(mrow[tt]) * (Kp + 128) + 128 * b + 32 * g + 16 * s2);
+                for (int tt = 0; tt < TT; ++tt) {
+                    if constexpr (kQDesc) {
+                        const uint4 v = buffer_load_u128(rq, qoff[tt] + 16 * s2, 128u * static_cast<uint32_t>(b));
+                        L.qv[s2][tt] = v4i32_t{static_cast<int>(v.x), static_cast<int>(v.y), static_cast<int>(v.z),
+                                               static_cast<int>(v.w)};
+                    } else {
+                        L.qv[s2][tt] = *reinterpret_cast<const v4i32_t*>(
+                            qm + static_cast<size_t>(mrow[tt]) * (Kp + 128) + 128 * b + 32 * g + 16 * s2);
+                    }
+                }
             if constexpr (LOADC) {
 #pragma unroll
                 for (int R = 0; R < S; ++R) {
-                    const uint32_t* c = coef + (static_cast<size_t>(tl[R]) * Tb + b) * 64 + r0[R];
-                    L.zr[R] = c[li];
-                    L.cz[R] = *reinterpret_cast<const uint4*>(c + 4 * g);
+                    const uint32_t so = csub[R] + 256u * static_cast<uint32_t>(b);
+                    L.zr[R] = buffer_load_u32(rc, 4 * li, so);
+                    L.cz[R] = buffer_load_u128(rc, 16 * g, so);
                 }
             }
         };
@@ -265,14 +306,9 @@ __global__ __launch_bounds__(64 * KW) void gemm_mfma_kernel(const uint8_t* __res
 #pragma unroll
             for (int i = 0; i < CC; ++i) load(L[i], wave + KW * (i0 + i));
             uint4 wr[NI];
+            const uint32_t wso = static_cast<uint32_t>(wave + KW * i0) * P * 1024u;  // the round's first block
 #pragma unroll
-            for (int t = 0; t < NI; ++t) {
-                const int m = min(4 * t + g, NPC - 1);  // (surplus slots re-read the last piece)
-                const int i = m / (S * P), R = (m / P) % S, p = m % P;
-                const int sg = sb + min(R, ns - 1), b = wave + KW * (i0 + i);
-                const size_t off = ((static_cast<size_t>(sg >> 2) * Tb + b) * P + p) * 1024 + (16 * (sg & 3) + li) * 16;
-                wr[t] = *reinterpret_cast<const uint4*>(blob + kHeaderBytes + off);
-            }
+            for (int t = 0; t < NI; ++t) wr[t] = buffer_load_u128(rw, CC == C ? woC[t] : wo1[t], wso);
             __builtin_amdgcn_sched_barrier(0);
             uint32_t wt[NI][4];
 #pragma unroll
