@@ -22,8 +22,40 @@ namespace bitq {
 //           y = gamma d Y
 //   W2A8 ([ABQ] Eq. 3): per 128-group A = sum_j c_j (a0_j + 2 a1_j),
 //           y += delta (A - z S128)
-//   BVSR4 ([BVSR]): per 32-group P_k = sum_j c_j popc(beta_k & X_j),
-//           y += b S32 + sum_k c_k P_k with (c, b) = cache[idx]
+//   BVSR4 ([BVSR]): per 32-group P_k = sum_i beta_k[i] q_i (below: 4-bit
+//           dot products), y += b S32 + sum_k c_k P_k with (c, b) = cache[idx]
+
+// BVSR4 on the 4-bit dot products of gfx950 instead.  P_k = sum_i beta_k[i]
+// q_i is a masked sum of the group's activations; with q = 16 (q >> 4) +
+// (q & 15) split into a signed high and an unsigned low nibble, and the four
+// bitvectors stored nibble-interleaved (plane word s of a group: nibble e =
+// the 4 bits beta_0..3 of one of its inputs 8 s .. 8 s + 7), the mask
+// W & (0x11111111 << k) holds 2^k beta_k per nibble, and one v_dot8_u32_u4
+// (low nibbles) plus one v_dot8_i32_i4 (high nibbles) take 8 inputs of
+// bitvector k: 2^k P_k = lo + 16 hi (k = 3: lo - 16 hi, the signed nibble
+// 8 being -8).  Per group and bitvector 4 masks and 8 dot products replace
+// the 8 ANDs, 8 popcounts and plane combine of the AND+popcount form; the
+// same integer P_k comes out exactly.
+//
+// Low- and high-nibble words of 8 inputs from two words of 4 activation bytes
+// (inputs 0..3 in a, 4..7 in b): nibble e holds input (e >> 1) + 4 (e & 1).
+// v_dot8_i32_i4 in its three-operand form (the compiler's accumulate-in-place
+// form needs a register zeroed first for each chain)
+__device__ __forceinline__ int sdot8_acc(uint32_t a, uint32_t b, int c) {
+    int r;
+    asm("v_dot8_i32_i4 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ int sdot8_first(uint32_t a, uint32_t b) {
+    int r;
+    asm("v_dot8_i32_i4 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+__device__ __forceinline__ void nibble_words(uint32_t a, uint32_t b, uint32_t& lo, uint32_t& hi) {
+    lo = (a & 0x0F0F0F0Fu) | ((b & 0x0F0F0F0Fu) << 4);
+    hi = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
+}
 
 // ================================= AND+popcount GEMV, whole k per workgroup
 // No hand-off between workgroups: a workgroup (256 threads) owns RG rows
@@ -58,7 +90,8 @@ namespace bitq {
 template <int FMT, int P, bool ACC, int BPL, int RG, bool ONE, int XQ = 0>
 __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __restrict__ blob, size_t off_c0,
                                                            size_t off_c1, const uint8_t* __restrict__ act,
-                                                           size_t act_off_S, size_t act_off_d, int M, int N, int K,
+                                                           size_t act_off_S, size_t act_off_d, size_t act_off_q, int M,
+                                                           int N, int K,
                                                            int Tb, int abits, size_t off_c2, size_t act_off_h,
                                                            int rank, float* __restrict__ y) {
     constexpr bool TERN = FMT == BITQ_TERNARY || FMT == BITQ_HGF;  // ternary planes
@@ -113,6 +146,9 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
 
     uint4 wv[BPL][P];
     uint32_t coef[BPL];
+    constexpr bool NIBX = FMT == BITQ_BVSR4;
+    constexpr int XST = NIBX && !FQ ? (NBW * 8 + 255) / 256 : 1;  // q loads per lane and round
+    uint4 xs[XST];
     // uniform 64-bit bases of this tile; per-lane offsets fit in 32 bits
     const uint8_t* __restrict__ tile_planes = blob + kHeaderBytes + static_cast<size_t>(t) * Tb * P * 1024;
     const uint32_t* __restrict__ tile_coef = reinterpret_cast<const uint32_t*>(blob + off_c0) + static_cast<size_t>(t) * Tb * 64;
@@ -135,15 +171,31 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
     // other load), so they are issued ahead of the weight stream and land
     // while it is still in flight.  Slots past the last real block receive
     // copies of it (clamped addresses); the compute loop skips those blocks.
+    //
+    // BVSR4 stages nibble words instead of planes: q of the round goes into
+    // registers (16 inputs per lane and load) and, once it has landed,
+    // store_nibbles writes each 8 inputs' low-nibble word (unsigned q & 15)
+    // and high-nibble word (signed q >> 4) to the block's LDS words
+    // 8 w + s and 8 w + 4 + s (32-group w, sub-word s).
     auto stage = [&](int m, int b_base) __attribute__((always_inline)) {
-        const uint4* src = reinterpret_cast<const uint4*>(aplanes) + (static_cast<size_t>(m) * Kw + 4 * b_base) * 2;
         const int last = min(NBW, NB - b_base) - 1;  // last real block of the round
+        if constexpr (NIBX) {
+            const uint4* qsrc = reinterpret_cast<const uint4*>(act + act_off_q) +
+                                (static_cast<size_t>(m) * NB + b_base) * 8;  // q [M][Kp]
 #pragma unroll
-        for (int v = 0; v < SLOT_PASSES; ++v) {
-            const int slot = tid + 256 * v;
-            const int blk = slot / 9, part = slot - 9 * blk;
-            __builtin_amdgcn_global_load_lds(src + 8 * min(blk, last) + min(part, 7),
-                                             reinterpret_cast<uint4*>(s_act) + 256 * v + 64 * wave, 16, 0, 0);
+            for (int v = 0; v < XST; ++v) {
+                const int ch = tid + 256 * v;
+                xs[v] = qsrc[8 * min(ch >> 3, last) + (ch & 7)];
+            }
+        } else {
+            const uint4* src = reinterpret_cast<const uint4*>(aplanes) + (static_cast<size_t>(m) * Kw + 4 * b_base) * 2;
+#pragma unroll
+            for (int v = 0; v < SLOT_PASSES; ++v) {
+                const int slot = tid + 256 * v;
+                const int blk = slot / 9, part = slot - 9 * blk;
+                __builtin_amdgcn_global_load_lds(src + 8 * min(blk, last) + min(part, 7),
+                                                 reinterpret_cast<uint4*>(s_act) + 256 * v + 64 * wave, 16, 0, 0);
+            }
         }
         const int4* srcS = reinterpret_cast<const int4*>(aS + static_cast<size_t>(m) * Kw + 4 * b_base);
 #pragma unroll
@@ -155,6 +207,26 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
             // (wave_u is 0 here; a destination computed from it, rather than
             // the constant s_h, avoids a crash of this compiler's SGPR-copy pass)
             __builtin_amdgcn_global_load_lds(hsrc + min(tid, rank / 4 - 1), s_h + 64 * wave_u, 16, 0, 0);
+        }
+    };
+
+    // (the use of xs waits for its loads, and only for them: they are issued
+    // ahead of the weight stream)
+    auto store_nibbles = [&]() __attribute__((always_inline)) {
+        if constexpr (NIBX) {
+#pragma unroll
+            for (int v = 0; v < XST; ++v) {
+                const int ch = tid + 256 * v;
+                if (XST * 256 == NBW * 8 || ch < NBW * 8) {
+                    const int blk = ch >> 3, w = (ch & 7) >> 1, s0 = 2 * (ch & 1);
+                    uint32_t lo0, hi0, lo1, hi1;
+                    nibble_words(xs[v].x, xs[v].y, lo0, hi0);
+                    nibble_words(xs[v].z, xs[v].w, lo1, hi1);
+                    uint32_t* dst = &s_act[blk * BSTR + 8 * w + s0];
+                    *reinterpret_cast<uint2*>(dst) = make_uint2(lo0, lo1);
+                    *reinterpret_cast<uint2*>(dst + 4) = make_uint2(hi0, hi1);
+                }
+            }
         }
     };
 
@@ -271,6 +343,18 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
                                                 __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u), 0x05040100u);
             uint32_t hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[7], b[6], 0x0c0c0400u),
                                                 __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u), 0x05040100u);
+            S += static_cast<int>(quad_swap<0xB1>(static_cast<uint32_t>(S)));
+            S += static_cast<int>(quad_swap<0x4E>(static_cast<uint32_t>(S)));
+            const int word = c >> 2;  // 32-input word of the round: block word / 4, its word word % 4
+            uint32_t* dst = &s_act[(word >> 2) * BSTR + 8 * (word & 3)];
+            if ((tid & 3) == 0) s_S[word] = S;
+            if constexpr (NIBX) {  // chunk c = sub-word c % 4 of its word
+                uint32_t nlo, nhi;
+                nibble_words(lo, hi, nlo, nhi);
+                dst[c & 3] = nlo;
+                dst[4 + (c & 3)] = nhi;
+                continue;
+            }
             // 8x8 bit transpose of the 64-bit value hi:lo (bit 8e + j <-> 8j + e)
             uint32_t t;
             t = (lo ^ (lo >> 7)) & 0x00AA00AAu; lo = lo ^ t ^ (t << 7);
@@ -284,13 +368,8 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
             hi = __builtin_amdgcn_perm(quad_swap<0xB1>(hi), hi, sel1);
             lo = __builtin_amdgcn_perm(quad_swap<0x4E>(lo), lo, sel2);
             hi = __builtin_amdgcn_perm(quad_swap<0x4E>(hi), hi, sel2);
-            S += static_cast<int>(quad_swap<0xB1>(static_cast<uint32_t>(S)));
-            S += static_cast<int>(quad_swap<0x4E>(static_cast<uint32_t>(S)));
-            const int word = c >> 2;  // 32-input word of the round: block word / 4, its word word % 4
-            uint32_t* dst = &s_act[(word >> 2) * BSTR + 8 * (word & 3)];
             dst[pl] = lo;
             dst[pl + 4] = hi;
-            if ((tid & 3) == 0) s_S[word] = S;
         }
         barrier_after_loads<kWeightLoads>();
     }
@@ -303,6 +382,16 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
         const float scale = (TERN && !ACC ? *reinterpret_cast<const float*>(blob + off_c0) : 1.0f) *
                             (ACC ? 1.0f : (FQ ? dq_fused : ad[m]));
         const float gate = LORA ? *reinterpret_cast<const float*>(blob + kHdrGate) : 0.0f;
+        if constexpr (NIBX && ONE) {
+            // the weights stay in registers across the tokens: without this
+            // empty asm the compiler hoists every bitvector mask out of the
+            // token loop (256 registers) and spills
+#pragma unroll
+            for (int j = 0; j < BPL; ++j)
+#pragma unroll
+                for (int p = 0; p < P; ++p)
+                    asm volatile("" : "+v"(wv[j][p].x), "+v"(wv[j][p].y), "+v"(wv[j][p].z), "+v"(wv[j][p].w));
+        }
         float yacc = 0.0f;
         int tacc[2][8];
 #pragma unroll
@@ -318,11 +407,16 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
                 __builtin_amdgcn_sched_barrier(0);
                 load_weights(b_base);
                 __builtin_amdgcn_sched_barrier(0);
+                store_nibbles();
                 barrier_after_loads<kWeightLoads>();
             } else if (first) {
-                if (!FQ) barrier_after_loads<kWeightLoads>();  // copies issued in the prologue
+                if (!FQ) {  // copies issued in the prologue
+                    store_nibbles();
+                    barrier_after_loads<kWeightLoads>();
+                }
             } else {
                 stage(m, b_base);
+                store_nibbles();
                 barrier_after_loads<0>();
             }
 #pragma unroll
@@ -440,30 +534,40 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
                 } else {  // BVSR4
 #pragma unroll
                     for (int w = 0; w < 4; ++w) {
-                        const uint4 x0 = *reinterpret_cast<const uint4*>(xa + 8 * w);
-                        const uint4 x1 = *reinterpret_cast<const uint4*>(xa + 8 * w + 4);
-                        const uint32_t xj[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-                        int Pk[4];
+                        // nibble words of the group's sub-words sw = 0..3
+                        const uint4 x0 = *reinterpret_cast<const uint4*>(xa + 8 * w);      // q & 15
+                        const uint4 x1 = *reinterpret_cast<const uint4*>(xa + 8 * w + 4);  // q >> 4
+                        const uint32_t xl[4] = {x0.x, x0.y, x0.z, x0.w}, xh[4] = {x1.x, x1.y, x1.z, x1.w};
+                        uint32_t tl[4] = {0u, 0u, 0u, 0u};
+                        int th[4] = {0, 0, 0, 0};
 #pragma unroll
-                        for (int k = 0; k < 4; ++k) {
-                            const uint32_t bk = (&wv[j][k].x)[w];
-                            int a8[8];
+                        for (int sw = 0; sw < 4; ++sw) {
+                            const uint32_t ws = (&wv[j][sw].x)[w];
 #pragma unroll
-                            for (int jj = 0; jj < 8; ++jj) a8[jj] = bcnt_acc(bk & xj[jj], 0);
-                            Pk[k] = combine_planes(a8);
+                            for (int k = 0; k < 4; ++k) {
+                                const uint32_t mk = ws & (0x11111111u << k);  // nibbles 2^k beta_k
+                                tl[k] = __builtin_amdgcn_udot8(mk, xl[sw], tl[k], false);
+                                th[k] = sw == 0 ? sdot8_first(mk, xh[sw]) : sdot8_acc(mk, xh[sw], th[k]);
+                            }
                         }
+                        // T_k = 2^k P_k (as a signed nibble, 2^3 reads -8)
+                        int Tk[4];
+#pragma unroll
+                        for (int k = 0; k < 3; ++k) Tk[k] = static_cast<int>(tl[k]) + 16 * th[k];
+                        Tk[3] = static_cast<int>(tl[3]) - 16 * th[3];
                         const int gi = 4 * b + w;
                         if (ACC) {
                             const int G = K / 32;  // groups of the real (unpadded) K
                             int4* dst = reinterpret_cast<int4*>(y) + (static_cast<size_t>(m) * N + n) * G + gi;
-                            if (n < N && gi < G) *dst = make_int4(Pk[0], Pk[1], Pk[2], Pk[3]);
+                            if (n < N && gi < G) *dst = make_int4(Tk[0], Tk[1] >> 1, Tk[2] >> 2, Tk[3] >> 3);
                         } else {
+                            // the packed cache holds c_k 2^-k: c_k P_k exactly as (c_k 2^-k) T_k
                             const int id = (cw >> (8 * w)) & 0xFF;
                             const float4 c = s_cache[2 * id];
                             const float bo = s_cache[2 * id + 1].x;
                             const float S32 = static_cast<float>(s_S[4 * bl + w]);
-                            yacc += bo * S32 + c.x * static_cast<float>(Pk[0]) + c.y * static_cast<float>(Pk[1]) +
-                                    c.z * static_cast<float>(Pk[2]) + c.w * static_cast<float>(Pk[3]);
+                            yacc += bo * S32 + c.x * static_cast<float>(Tk[0]) + c.y * static_cast<float>(Tk[1]) +
+                                    c.z * static_cast<float>(Tk[2]) + c.w * static_cast<float>(Tk[3]);
                         }
                     }
                 }
@@ -539,7 +643,7 @@ static void launch_nr_bpl(const bitq_wdesc& d, const BlobLayout& L, const void* 
     auto kern = one ? gemv_bits_nr_kernel<FMT, P, ACC, BPL, RG, true> : gemv_bits_nr_kernel<FMT, P, ACC, BPL, RG, false>;
     const int abits = d.fmt == BITQ_WNAM ? d.abits : 8;
     hipLaunchKernelGGL(kern, dim3(groups), dim3(256), 0, st, static_cast<const uint8_t*>(w), L.off_c0, L.off_c1,
-                       static_cast<const uint8_t*>(act), A.off_S, A.off_d, M, d.N, d.K, static_cast<int>(L.Tb),
+                       static_cast<const uint8_t*>(act), A.off_S, A.off_d, A.off_q, M, d.N, d.K, static_cast<int>(L.Tb),
                        abits, L.off_c2, A.off_h, d.rank, y);
 }
 
@@ -601,7 +705,8 @@ static void launch_fq_bpl(const bitq_wdesc& d, const BlobLayout& L, const void* 
     const int abits = d.fmt == BITQ_WNAM ? d.abits : 8;
     hipLaunchKernelGGL((gemv_bits_nr_kernel<FMT, P, false, BPL, RG, true, XQ>), dim3(groups), dim3(256), 0, st,
                        static_cast<const uint8_t*>(w), L.off_c0, L.off_c1, static_cast<const uint8_t*>(x),
-                       static_cast<size_t>(0), static_cast<size_t>(0), 1, d.N, d.K, static_cast<int>(L.Tb), abits,
+                       static_cast<size_t>(0), static_cast<size_t>(0), static_cast<size_t>(0), 1, d.N, d.K,
+                       static_cast<int>(L.Tb), abits,
                        L.off_c2, static_cast<size_t>(0), 0, y);
 }
 

@@ -307,7 +307,13 @@ void pack_coefficients(const bitq_wdesc& d, const BlobLayout& L, const bitq_logi
                     size_t off = L.off_c0 + static_cast<size_t>((((n / 64) * L.Tb + g / 4) * 64 + n % 64) * 4 + g % 4);
                     dst[off] = s->idx[n * G + g];
                 }
-            std::memcpy(dst + L.off_c1, s->cache, 256 * 5 * 4);
+            // c_j 2^-j (exact), then b: the kernel's products of sub-word j
+            // carry the factor 2^j
+            float* cache = reinterpret_cast<float*>(dst + L.off_c1);
+            for (int e = 0; e < 256; ++e) {
+                for (int j = 0; j < 4; ++j) cache[5 * e + j] = std::ldexp(s->cache[5 * e + j], -j);
+                cache[5 * e + 4] = s->cache[5 * e + 4];
+            }
             break;
         }
     }
@@ -335,10 +341,17 @@ bitq_status pack_impl(const bitq_wdesc& d, const bitq_logical* s, void* dstv, si
             });
             break;
         case BITQ_W2A8:
-        case BITQ_BVSR4:
         case BITQ_WNAM:
             pack_planes(d, L, dst, nthreads,
                         [&](int64_t p, int64_t n, int64_t k) { return (s->code[n * K + k] >> p) & 1; });
+            break;
+        case BITQ_BVSR4:
+            // plane p of a 32-group holds its inputs 8p .. 8p + 7, one per
+            // nibble: bit 4e + j of the word = beta_j of input 8p + bvsr_nibble_input(e)
+            pack_planes(d, L, dst, nthreads, [&](int64_t p, int64_t n, int64_t k) {
+                const int64_t i = k & 31, in = (k & ~int64_t(31)) + 8 * p + bvsr_nibble_input(static_cast<int>(i >> 2));
+                return (s->code[n * K + in] >> (i & 3)) & 1;
+            });
             break;
     }
     pack_coefficients(d, L, s, dst);

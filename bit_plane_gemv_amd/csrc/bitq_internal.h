@@ -24,6 +24,11 @@ constexpr int kOneWgPerCuLds = 84 * 1024;
 constexpr int kHdrOffC2 = 88, kHdrRank = 96, kHdrAlpha = 100, kHdrGate = 104, kHdrAmaxA = 108;
 constexpr int kMaxHgfK = 63 * 256;  // HGF: <= 63 runs of 256 inputs meet in one fixed-point word
 
+// BVSR4 planes: nibble e (0..7) of a plane word holds the bitvector bits of
+// input (e >> 1) + 4 (e & 1) of the word's 8 inputs (the order in which two
+// words of 4 activation bytes split into nibble words most cheaply)
+constexpr int bvsr_nibble_input(int e) { return (e >> 1) + 4 * (e & 1); }
+
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 

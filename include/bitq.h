@@ -181,14 +181,19 @@ typedef struct {
  *     zero bits.
  *   plane meaning: SIGN1/RABIT bit 1 <-> +1, 0 <-> -1 (one plane per path);
  *     TERNARY and HGF plane 0 = [T == +1], plane 1 = [T == -1]; W2A8 plane i = bit i
- *     of q; BVSR4 plane k = beta_k.
+ *     of q; BVSR4 planes hold the four bitvectors nibble-interleaved: plane s
+ *     of a 32-input word carries its inputs 8s .. 8s+7, one per nibble, bits
+ *     4e .. 4e+3 for input 8s + (e >> 1) + 4 (e & 1) with bit 4e + j =
+ *     beta_j (the kernel masks one bitvector and takes 8 inputs per 4-bit
+ *     dot product).
  *   coefficient sections (zero-padded):
  *     SIGN1   c0 = alpha f32 [Np]
  *     RABIT   c0 = g f16 [P][Np];  c1 = h f16 [P][Kp]
  *     TERNARY c0 = gamma f32 [1]
  *     W2A8    c0 = u32 [Np/64][Kp/128][64]: low 16 bits delta, high 16 bits z
  *     BVSR4   c0 = idx u8 [Np/64][Kp/128][64][4] (byte j: group 4b + j);
- *             c1 = cache f32 [256][5]
+ *             c1 = cache f32 [256][5], entry (c_0, c_1/2, c_2/4, c_3/8, b)
+ *             (the dot products of bitvector j carry the factor 2^j)
  *     HGF     c0 = gamma f32 [1];  c1 = A transposed, f16 [r][Kp] (row j
  *             holds A[k][j] for every k);  c2 = B transposed, f16 [Np][r]
  *             (row n holds B[j][n] for every j)

@@ -24,7 +24,10 @@ Specification (all little-endian):
       4 w2a8    c0 = dz     u32 [Np/64][Kp/128][64], low half = delta (f16),
                 high half = zero point (f16)  (plane i = bit i of q)
       5 bvsr    c0 = idx    u8  [Np/64][Kp/128][64][4] (byte j = group 4b+j),
-                c1 = cache  f32 [256][5]      (plane k = bitvector beta_k)
+                c1 = cache  f32 [256][5], entry (c_0, c_1/2, c_2/4, c_3/8, b);
+                plane s of a 32-input word holds its inputs 8s .. 8s+7, one per
+                nibble: bits 4e .. 4e+3 belong to input 8s + (e >> 1) + 4 (e & 1),
+                bit 4e + j = beta_j of that input
       6 wnam    as w2a8 with P = n planes      (plane i = bit i of q)
       7 hgf     as ternary, plus c1 = A^T f16 [r][Kp] (row j = column j of
                 A) and c2 = B^T f16 [Np][r] (row n = column n of B)
@@ -121,14 +124,21 @@ def unpack(blob: np.ndarray) -> dict:
         out["delta"], out["zero"] = delta[:N, :G].copy(), zero[:N, :G].copy()
         pad_ok &= bool(np.all(dz[N:] == 0))
     elif fmt == 5:
-        code = np.zeros((N, K), dtype=np.uint8)
-        for k in range(P):
-            code |= (bits[k] << k).astype(np.uint8)
-        out["code"] = code
+        # natural bit position 32 g + 4 e + j of plane s -> bit j of the code
+        # of input 32 g + 8 s + (e >> 1) + 4 (e & 1)
+        G = K // 32
+        nib = bits.reshape(P, N, G, 8, 4).astype(np.uint8)
+        vals = sum(nib[..., j] << j for j in range(4))          # [s, n, g, e]
+        pos = np.array([(e >> 1) + 4 * (e & 1) for e in range(8)])
+        code = np.zeros((N, G, 32), dtype=np.uint8)
+        for sp in range(P):
+            code[:, :, 8 * sp + pos] = vals[sp]
+        out["code"] = code.reshape(N, K)
         idx = _section(b, h["off_c0"], Np * (Kp // 32), np.uint8)
         idx = idx.reshape(Tn, Tb, ROW_TILE, 4).transpose(0, 2, 1, 3).reshape(Np, Kp // 32)
         out["idx"] = idx[:N, :K // 32].copy()
-        out["cache"] = _section(b, h["off_c1"], 256 * 5 * 4, np.float32).reshape(256, 5).copy()
+        stored = _section(b, h["off_c1"], 256 * 5 * 4, np.float32).reshape(256, 5)
+        out["cache"] = np.ldexp(stored, np.array([0, 1, 2, 3, 0], dtype=np.int32)).astype(np.float32)
         pad_ok &= bool(np.all(idx[N:] == 0) and np.all(idx[:, K // 32:] == 0))
     else:
         raise ValueError(f"unknown format {fmt}")

@@ -25,6 +25,14 @@ def _set_bit(blob, Np, Kp, P, p, n, k):
     struct.pack_into("<I", blob, off, word)
 
 
+def _set_bvsr_bit(blob, Np, Kp, n, k, j):
+    """beta_j of weight (n, k) in the BVSR4 plane layout: plane s = (k % 32) // 8
+    of the 32-input word, nibble e with (e >> 1) + 4 (e & 1) = k % 8, bit j of it."""
+    pos = k % 8
+    e = 2 * pos if pos < 4 else 2 * (pos - 4) + 1
+    _set_bit(blob, Np, Kp, 4, (k % 32) // 8, n, (k // 32) * 32 + 4 * e + j)
+
+
 def test_hand_blob_sign():
     N, K = 70, 200                  # 2 row tiles, 2 k blocks, ragged both ways
     hdr, Np, Kp = _header(1, N, K, 1, 0, 0, 0, 0)
@@ -80,15 +88,18 @@ def test_hand_blob_w2a8_and_bvsr_coefficients():
     total = off_c1 + ((256 * 5 * 4 + 255) // 256) * 256
     hdr, Np, Kp = _header(5, N, K, 4, 32, off_c0, off_c1, total)
     blob = hdr + bytearray(total - 256)
-    _set_bit(blob, Np, Kp, 4, 0, 2, 40)
-    _set_bit(blob, Np, Kp, 4, 3, 2, 40)          # code[2,40] = 9
-    _set_bit(blob, Np, Kp, 4, 2, 63, 127)        # code[63,127] = 4
+    _set_bvsr_bit(blob, Np, Kp, 2, 40, 0)
+    _set_bvsr_bit(blob, Np, Kp, 2, 40, 3)        # code[2,40] = 9
+    _set_bvsr_bit(blob, Np, Kp, 63, 127, 2)      # code[63,127] = 4
+    _set_bvsr_bit(blob, Np, Kp, 7, 5, 1)         # code[7,5] = 2
     blob[off_c0 + 2 * 4 + 1] = 200               # idx[2, group 1]
     blob[off_c0 + 63 * 4 + 3] = 7                # idx[63, group 3]
     cache = np.arange(1280, dtype=np.float32).reshape(256, 5)
-    blob[off_c1:off_c1 + 5120] = cache.tobytes()
+    stored = cache * np.array([1, 0.5, 0.25, 0.125, 1], np.float32)   # c_j 2^-j, then b
+    blob[off_c1:off_c1 + 5120] = stored.tobytes()
     out = layout.unpack(np.frombuffer(bytes(blob), np.uint8))
-    assert out["code"][2, 40] == 9 and out["code"][63, 127] == 4 and out["code"].sum() == 13
+    assert out["code"][2, 40] == 9 and out["code"][63, 127] == 4 and out["code"][7, 5] == 2
+    assert out["code"].sum() == 15
     assert out["idx"][2, 1] == 200 and out["idx"][63, 3] == 7 and out["idx"].sum() == 207
     assert np.array_equal(out["cache"], cache)
 
