@@ -87,13 +87,16 @@ __device__ __forceinline__ void nibble_words(uint32_t a, uint32_t b, uint32_t& l
 // (byte j = plane j of the chunk), and the 4 lanes of a 32-input word
 // assemble its 8 plane words with two byte-permute exchanges.  No clamp is
 // needed: |x| <= amax gives |fl32(x s)| < Qm + 1/2.
+//
+// Arguments: what the prologue needs comes first (the first 56 bytes arrive
+// preloaded in scalar registers); activation-buffer offsets are 32-bit (the
+// host bounds that buffer far below 4 GB).
 template <int FMT, int P, bool ACC, int BPL, int RG, bool ONE, int XQ = 0>
 __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __restrict__ blob, size_t off_c0,
                                                            size_t off_c1, const uint8_t* __restrict__ act,
-                                                           size_t act_off_S, size_t act_off_d, size_t act_off_q, int M,
-                                                           int N, int K,
-                                                           int Tb, int abits, size_t off_c2, size_t act_off_h,
-                                                           int rank, float* __restrict__ y) {
+                                                           uint32_t act_off_S, uint32_t act_off_q, int N, int Tb, int M,
+                                                           int K, uint32_t act_off_d, int abits, size_t off_c2,
+                                                           uint32_t act_off_h, int rank, float* __restrict__ y) {
     constexpr bool TERN = FMT == BITQ_TERNARY || FMT == BITQ_HGF;  // ternary planes
     constexpr bool LORA = FMT == BITQ_HGF && !ACC;                 // the correction epilogue
     constexpr int G = 256 / RG;    // k-groups: lanes that share a row
@@ -643,8 +646,9 @@ static void launch_nr_bpl(const bitq_wdesc& d, const BlobLayout& L, const void* 
     auto kern = one ? gemv_bits_nr_kernel<FMT, P, ACC, BPL, RG, true> : gemv_bits_nr_kernel<FMT, P, ACC, BPL, RG, false>;
     const int abits = d.fmt == BITQ_WNAM ? d.abits : 8;
     hipLaunchKernelGGL(kern, dim3(groups), dim3(256), 0, st, static_cast<const uint8_t*>(w), L.off_c0, L.off_c1,
-                       static_cast<const uint8_t*>(act), A.off_S, A.off_d, A.off_q, M, d.N, d.K, static_cast<int>(L.Tb),
-                       abits, L.off_c2, A.off_h, d.rank, y);
+                       static_cast<const uint8_t*>(act), static_cast<uint32_t>(A.off_S), static_cast<uint32_t>(A.off_q),
+                       d.N, static_cast<int>(L.Tb), M, d.K, static_cast<uint32_t>(A.off_d), abits, L.off_c2,
+                       static_cast<uint32_t>(A.off_h), d.rank, y);
 }
 
 template <int FMT, int P, bool ACC, int RG>
@@ -704,10 +708,8 @@ static void launch_fq_bpl(const bitq_wdesc& d, const BlobLayout& L, const void* 
     const int groups = xcd_row_groups(tiles, RG);  // as launch_nr_bpl
     const int abits = d.fmt == BITQ_WNAM ? d.abits : 8;
     hipLaunchKernelGGL((gemv_bits_nr_kernel<FMT, P, false, BPL, RG, true, XQ>), dim3(groups), dim3(256), 0, st,
-                       static_cast<const uint8_t*>(w), L.off_c0, L.off_c1, static_cast<const uint8_t*>(x),
-                       static_cast<size_t>(0), static_cast<size_t>(0), static_cast<size_t>(0), 1, d.N, d.K,
-                       static_cast<int>(L.Tb), abits,
-                       L.off_c2, static_cast<size_t>(0), 0, y);
+                       static_cast<const uint8_t*>(w), L.off_c0, L.off_c1, static_cast<const uint8_t*>(x), 0u, 0u, d.N,
+                       static_cast<int>(L.Tb), 1, d.K, 0u, abits, L.off_c2, 0u, 0, y);
 }
 
 template <int FMT, int P, int RG, int XQ>
