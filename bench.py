@@ -62,16 +62,17 @@ METRIC = "packed-weight GB/s & % HBM peak, bit-plane GEMV 11008x4096 M=1; us/lay
 # HBM bytes moved per launch of a product kernel, from rocprofv3 counter runs
 # (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0; factors calibrated on a plain copy
 # kernel of known size; profiles/ holds the runs).  Each entry is valid only
-# for the kernel source it was measured on (first 16 hex digits of the
-# sha256 of that source file); otherwise traffic is reported as null.
+# for the kernel source and the build script it was measured with (first 16
+# hex digits of the sha256 of each file); otherwise traffic is reported as null.
 MEASURED_TRAFFIC: dict = {
-    "rabit": {"source": "bitq_sign.hip", "sha16": "ba906aeaa6be2c6a", "bytes_per_launch": 13460480,
-              "profile": "profiles/gemv_sign_kernel_rabit_11008x4096.md"},
-    "w2a8": {"source": "bitq_bits.hip", "sha16": "acae8bcee832dc66", "bytes_per_launch": 12829696,
-             "profile": "profiles/gemv_bits_nr_kernel_w2a8_11008x4096.md"},
-    "w2a8+fuse": {"source": "bitq_bits.hip", "sha16": "acae8bcee832dc66", "bytes_per_launch": 12880896,
-                  "profile": "profiles/gemv_bits_nr_kernel_fused_w2a8_11008x4096.md"},
+    "rabit": {"source": "bitq_sign.hip", "sha16": "ba906aeaa6be2c6a", "build_sha16": "75709457503c2a5c",
+              "bytes_per_launch": 13458432, "profile": "profiles/gemv_sign_kernel_rabit_11008x4096.md"},
+    "w2a8": {"source": "bitq_bits.hip", "sha16": "4e9c5a7e49562fb5", "build_sha16": "75709457503c2a5c",
+             "bytes_per_launch": 12826624, "profile": "profiles/gemv_bits_nr_kernel_w2a8_11008x4096.md"},
+    "w2a8+fuse": {"source": "bitq_bits.hip", "sha16": "4e9c5a7e49562fb5", "build_sha16": "75709457503c2a5c",
+                  "bytes_per_launch": 12869632, "profile": "profiles/gemv_bits_nr_kernel_fused_w2a8_11008x4096.md"},
 }
+BUILD_SCRIPT = os.path.join(ROOT, "bit_plane_gemv_amd", "build.py")
 
 
 def source_sha(name: str) -> str:
@@ -79,9 +80,14 @@ def source_sha(name: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def build_sha() -> str:
+    with open(BUILD_SCRIPT, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
 def measured_traffic(key: str):
     mt = MEASURED_TRAFFIC.get(key)
-    if mt is None or mt["sha16"] != source_sha(mt["source"]):
+    if mt is None or mt["sha16"] != source_sha(mt["source"]) or mt["build_sha16"] != build_sha():
         return None
     return mt
 
