@@ -54,7 +54,7 @@ INT8_MFMA_PEAK_TOPS = 5000.0      # MI355X dense int8 matrix-core peak
 # VALU lane-operations per second: 256 CUs x 4 SIMDs x 16 lanes per clock x
 # 2.4 GHz (one 64-lane instruction every 4 clocks per SIMD)
 VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
-MFMA_MIN_TOKENS = 4               # the library's switch to the matrix-core kernel
+MFMA_MIN_TOKENS = {"w2a8": 2, "wnam": 2, "ternary": 3}  # the library's switch to the matrix cores
 ROTATE_BYTES = 1 << 30
 CSRC = os.path.join(ROOT, "bit_plane_gemv_amd", "csrc")
 METRIC = "packed-weight GB/s & % HBM peak, bit-plane GEMV 11008x4096 M=1; us/layer"
@@ -532,7 +532,7 @@ def main():
     kernel_ms = ms_per_step
     if L.integer and not fuse:
         kernel_ms = timer.per_step_ms(L.product, K_steps, args.warmup)
-    mfma = M >= MFMA_MIN_TOKENS and fmt in ("ternary", "w2a8", "wnam")
+    mfma = fmt in MFMA_MIN_TOKENS and M >= MFMA_MIN_TOKENS[fmt]
     kname = product_kernel_name(L, mfma) + (" (fused quantizer)" if fuse else "")
     ctx = None if args.no_context else L.context_floor(timer, K_steps, args.warmup, L.gemv_bytes, fused=fuse)
     traffic_key = (args.workload + ("+fuse" if fuse else "")) if M == 1 else None

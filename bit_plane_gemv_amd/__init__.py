@@ -389,8 +389,8 @@ def act_layout(M: int, K: int, rank: int = 0) -> dict:
     off_S = a256(M * Kw * 32)
     off_q = a256(off_S + M * Kw * 4)
     off_qm = a256(off_q + M * Kp)
-    off_d = a256(off_qm + M * (Kp + 128))      # qm rows are Kp + 128 bytes apart
+    off_d = a256(off_qm + 16 * ((M + 15) // 16) * Kp)   # qm: whole tiles of 16 tokens
     off_amax = a256(off_d + 4 * M)
     off_h = a256(off_amax + 4 * M)
-    return dict(Kp=Kp, Kw=Kw, qm_pitch=Kp + 128, off_planes=0, off_S=off_S, off_q=off_q, off_qm=off_qm, off_d=off_d,
+    return dict(Kp=Kp, Kw=Kw, off_planes=0, off_S=off_S, off_q=off_q, off_qm=off_qm, off_d=off_d,
                 off_amax=off_amax, off_h=off_h, total=a256(off_h + 4 * M * rank))

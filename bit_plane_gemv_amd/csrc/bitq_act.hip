@@ -58,10 +58,18 @@ __device__ __forceinline__ void lora_arrive(unsigned long long* word, float part
     __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Where the matrix-core kernel reads input i of a 32-input word in the
-// permuted copy qm of q: input 8j + 2c + s sits at byte 16s + 4c + j, so
-// each 16 bytes of qm are one MFMA operand (see the matrix-core kernel).
-__device__ __forceinline__ int qm_pos(int i) { return 16 * (i & 1) + 4 * ((i >> 1) & 3) + (i >> 3); }
+// Where the matrix-core kernel reads input i of word w (inputs 32w ..
+// 32w + 31) of token m = 16t + j in the permuted copy qm of q, with T token
+// tiles of 16: in block b = w / 4, word g = w % 4 of the block, input
+// 8e + 2c + s of the word sits at byte
+//   ((b T + t) 2 + s) 1024 + (16 g + j) 16 + 4c + e,
+// so a wave's operand load for one block, token tile and k step (lane
+// 16 g + j taking 16 bytes) is 1 KB contiguous.
+__device__ __forceinline__ size_t qm_off(int m, int w, int i, int T) {
+    const int b = w >> 2, g = w & 3, t = m >> 4, j = m & 15;
+    return (static_cast<size_t>(b * T + t) * 2 + (i & 1)) * 1024 + static_cast<size_t>(16 * g + j) * 16 +
+           4 * ((i >> 1) & 3) + (i >> 3);
+}
 
 // amax of a long row (K > kAmaxOnePassK) in a launch of its own: one
 // workgroup of 1024 lanes per token, four 16-byte loads in flight per lane.
@@ -228,8 +236,7 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const void* __restrict__
         qi = static_cast<int>(fminf(fmaxf(r, -qmax), qmax));
     }
     out.q[static_cast<size_t>(m) * (Kw * 32) + k] = static_cast<int8_t>(qi);
-    out.qm[static_cast<size_t>(m) * (Kw * 32 + 128) + 32 * (w0 + (lane >> 5)) + qm_pos(lane & 31)] =
-        static_cast<int8_t>(qi);
+    out.qm[qm_off(m, w0 + (lane >> 5), lane & 31, (static_cast<int>(gridDim.y) + 15) >> 4)] = static_cast<int8_t>(qi);
     // planes: lane j (< 8) keeps plane j of word w0, lane 8 + j of word w0 + 1
     uint32_t mine = 0;
 #pragma unroll

@@ -761,9 +761,8 @@ ActLayout act_layout(int M, int K, int rank) {
     A.off_planes = 0;
     A.off_S = align256(static_cast<size_t>(M * A.Kw) * 32);
     A.off_q = align256(A.off_S + static_cast<size_t>(M * A.Kw) * 4);
-    A.qm_pitch = A.Kp + 128;
     A.off_qm = align256(A.off_q + static_cast<size_t>(M * A.Kp));
-    A.off_d = align256(A.off_qm + static_cast<size_t>(M * A.qm_pitch));
+    A.off_d = align256(A.off_qm + 16 * static_cast<size_t>((M + 15) / 16) * A.Kp);  // whole token tiles
     A.off_amax = align256(A.off_d + 4 * static_cast<size_t>(M));
     A.off_h = align256(A.off_amax + 4 * static_cast<size_t>(M));
     A.total = align256(A.off_h + 4 * static_cast<size_t>(M) * rank);
@@ -817,9 +816,9 @@ Plan make_plan(const bitq_wdesc& d, int M, bool fused) {
         p.off_partials = 0;
         p.ws_bytes = 0;
         // the contraction is compute-bound on the VALU from 2 tokens on; from
-        // kMfmaMinM tokens the int8 matrix-core kernel is faster and takes
-        // over (HGF and BVSR4 stay on the VALU)
-        p.mfma = M >= kMfmaMinM && (d.fmt == BITQ_TERNARY || d.fmt == BITQ_W2A8 || d.fmt == BITQ_WNAM);
+        // mfma_min_tokens(fmt) tokens the int8 matrix-core kernel is faster
+        // and takes over (HGF and BVSR4 stay on the VALU)
+        p.mfma = mfma_min_tokens(d.fmt) > 0 && M >= mfma_min_tokens(d.fmt);
         return p;
     }
     p.waves_per_wg = lut ? 4 : 1;
@@ -850,7 +849,7 @@ MfmaShape mfma_shape(const bitq_wdesc& d, int M) {
     s.RS = kMfmaSubs;
     const int64_t NB = round_up(d.K, kKBlock) / kKBlock;
     const int64_t nsub = round_up(d.N, kRowTile) / 16;
-    s.KW = 8;
+    s.KW = s.TT == 1 ? 16 : 8;
     const int64_t cmax = s.TT == 1 ? 4 : 2;
     const int64_t nbw = (NB + s.KW - 1) / s.KW, rounds = (nbw + cmax - 1) / cmax;
     s.CH = static_cast<int>((nbw + rounds - 1) / rounds);

@@ -47,7 +47,6 @@ BlobLayout blob_layout(const bitq_wdesc& d);
 // adds the HGF section h f32 [M][rank].
 struct ActLayout {
     int64_t M, K, Kp, Kw;
-    int64_t qm_pitch;  // bytes between token rows of the qm section (Kp + 128)
     size_t off_planes, off_S, off_q, off_qm, off_d, off_amax, off_h, total;
 };
 // Rows longer than this get their amax from a separate pass (act_amax_kernel)
@@ -72,7 +71,7 @@ struct Plan {
     int M;
     size_t off_partials;   // float formats: u64 [Np] split-k words (count + fixed-point sum)
     size_t ws_bytes;
-    bool mfma;             // integer formats, M >= kMfmaMinM: the int8 matrix-core kernel
+    bool mfma;             // TERNARY/W2A8/WNAM, M >= mfma_min_tokens: the int8 matrix-core kernel
 };
 Plan make_plan(const bitq_wdesc& d, int M, bool fused = false);  // fused: BITQ_F_FUSE_QUANT
 
@@ -96,7 +95,15 @@ LaunchShape launch_shape(const bitq_wdesc& d, int M, int x_dtype, uint32_t flags
 // Workgroups of the AND+popcount / XNOR kernels: 64/RG row groups per 64-row
 // tile, tiles dealt round-robin to the 8 XCDs (padded to whole rounds).
 inline int xcd_row_groups(int64_t tiles, int RG) { return static_cast<int>(8 * (64 / RG) * ((tiles + 7) / 8)); }
-constexpr int kMfmaMinM = 4;  // tokens from which TERNARY/W2A8/WNAM use the matrix cores
+// Tokens from which TERNARY, W2A8 and WNAM run on the int8 matrix cores
+// (measured on W2A8 11008x4096: 6.2 us at 2 and 3 tokens against 7.0 and
+// 9.0 us on the VALU; ternary 4096x4096: 4.8 us at 2 and 3 tokens against
+// 4.1 and 5.0 us).  0 for the formats that stay on the VALU.
+inline int mfma_min_tokens(int fmt) {
+    if (fmt == BITQ_W2A8 || fmt == BITQ_WNAM) return 2;
+    if (fmt == BITQ_TERNARY) return 3;
+    return 0;
+}
 constexpr int kMaxFusedK = 16384;    // BITQ_F_FUSE_QUANT: whole k range in one round of the kernel
 constexpr int kLaunchNotBuilt = -1;  // launcher: no kernel built for this combination
 

@@ -36,8 +36,9 @@ namespace bitq {
 // WNAM; the matrix cores then return A - z S128 itself, exactly), or the
 // ternary value (fields p + 2m: 0 -> 0, 1 -> +1, 2 -> -1).  So a code costs
 // about one VALU operation.  The activation buffer's qm section holds q in
-// the same order (input 8j + 2c + s at byte 16s + 4c + j of its word), so a
-// B operand is one 16-byte load.
+// the same order (input 8j + 2c + s of a word at byte 4c + j of its half s),
+// tiled so that the B operands of a wave's block, token tile and k step are
+// one contiguous 16-byte-per-lane load.
 //
 // Work decomposition.  One workgroup per CU (grid = 256) owns a contiguous
 // range of 16-row sub-tiles over the whole k range, up to kMfmaSubs of them
@@ -120,24 +121,23 @@ __global__ __launch_bounds__(64 * KW) void gemm_mfma_kernel(const uint8_t* __res
     const uint32_t per = G / 8, rid = G % 8 == 0 ? (blockIdx.x % 8) * per + blockIdx.x / 8 : blockIdx.x;
     const int s_beg = static_cast<int>(ns_u * rid / G), s_end = static_cast<int>(ns_u * (rid + 1) / G);
     const int nbw = wave < Tb ? (Tb - wave + KW - 1) / KW : 0;  // k blocks of this wave
-    const int Kp = Tb * 128, Np = 16 * nsub;
+    const int Np = 16 * nsub;
     const int8_t* qm = reinterpret_cast<const int8_t*>(act + act_off_qm);
     const float* ad = reinterpret_cast<const float*>(act + act_off_d);
     const uint32_t* coef = reinterpret_cast<const uint32_t*>(blob + off_c0);
-    int mrow[TT];  // this lane's token of each token tile (clamped for loads)
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) mrow[tt] = min(16 * tt + li, M - 1);
+    // q is tiled for these loads (include/bitq.h): the operand of block b,
+    // token tile tt and k step s2 is the 1 KB at ((b TT + tt) 2 + s2) 1024,
+    // lane l taking bytes 16 l .. 16 l + 15, so every q load of a wave is
+    // one contiguous KB.  (The earlier layout, token rows of Kp + 128 bytes,
+    // made each load touch 16 cache lines, half of each: W2A8 11008x4096
+    // took 15.9 us at M = 64, 9.6 us at M = 32, against 11.4 and 8.4 us.)
     // Loads go through buffer descriptors: the per-lane part of each offset
     // is computed once, the per-block part is a scalar offset, so the loads
-    // take no vector address arithmetic.  q: [M][Kp + 128] bytes.  (q of
-    // four token tiles through plain loads instead: measured on W2A8
-    // 11008x4096, the descriptor gains 7.42 -> 7.22 us at M = 4 and 8.33 ->
-    // 8.12 us at M = 16 but loses 16.30 -> 16.96 us at M = 64.)
+    // take no vector address arithmetic (four token tiles: plain loads,
+    // measured faster there).  Token slots past M hold no codes; their
+    // products land in outputs that are not stored.
     constexpr bool kQDesc = TT <= 2;
-    const auto rq = buffer_rsrc(qm, static_cast<uint32_t>(M) * static_cast<uint32_t>(Kp + 128));
-    uint32_t qoff[TT];
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) qoff[tt] = static_cast<uint32_t>(mrow[tt]) * static_cast<uint32_t>(Kp + 128) + 32 * g;
+    const auto rq = buffer_rsrc(qm, static_cast<uint32_t>(TT) * 2048u * static_cast<uint32_t>(Tb));
     const size_t coef_words = static_cast<size_t>(Np) * Tb, planes_bytes = static_cast<size_t>(Np / 64) * Tb * P * 1024;
 
     for (int sb = s_beg; sb < s_end; sb += S) {
@@ -190,13 +190,13 @@ __global__ __launch_bounds__(64 * KW) void gemm_mfma_kernel(const uint8_t* __res
             for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
                 for (int tt = 0; tt < TT; ++tt) {
+                    const uint32_t qo = static_cast<uint32_t>(lane) * 16u + static_cast<uint32_t>(tt * 2 + s2) * 1024u;
                     if constexpr (kQDesc) {
-                        const uint4 v = buffer_load_u128(rq, qoff[tt] + 16 * s2, 128u * static_cast<uint32_t>(b));
+                        const uint4 v = buffer_load_u128(rq, qo, static_cast<uint32_t>(b) * (TT * 2048u));
                         L.qv[s2][tt] = v4i32_t{static_cast<int>(v.x), static_cast<int>(v.y), static_cast<int>(v.z),
                                                static_cast<int>(v.w)};
                     } else {
-                        L.qv[s2][tt] = *reinterpret_cast<const v4i32_t*>(
-                            qm + static_cast<size_t>(mrow[tt]) * (Kp + 128) + 128 * b + 32 * g + 16 * s2);
+                        L.qv[s2][tt] = *reinterpret_cast<const v4i32_t*>(qm + static_cast<size_t>(b) * (TT * 2048) + qo);
                     }
                 }
             if constexpr (LOADC) {
@@ -400,7 +400,9 @@ static void launch_mfma_kw(const bitq_wdesc& d, const BlobLayout& L, const MfmaS
         BITQ_MFMA_CASE(8, 1);
         BITQ_MFMA_CASE(8, 2);
         BITQ_MFMA_CASE(8, 3);
-        BITQ_MFMA_CASE(8, 4);
+        BITQ_MFMA_CASE(16, 1);
+        BITQ_MFMA_CASE(16, 2);
+        BITQ_MFMA_CASE(16, 4);
     } else {
         BITQ_MFMA_CASE(8, 1);
         BITQ_MFMA_CASE(8, 2);

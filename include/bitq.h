@@ -279,11 +279,12 @@ bitq_status bitq_quantize_weights_opts(const bitq_wdesc* desc, const float* W,
  *                          byte of q[m][32w + i] at bit i
  *   S      i32 [M][Kw]     sum of q over each run of 32 inputs
  *   q      i8  [M][Kp]     quantized activations (0 beyond K)
- *   qm     i8  [M][Kp + 128]  the same codes, the bytes of each 32-input
- *                          word in the order the matrix-core kernel reads them:
- *                          input 8j + 2c + s of a word at byte 16s + 4c + j;
- *                          rows Kp + 128 bytes apart (the last 128 bytes of a
- *                          row are unused)
+ *   qm     i8  [Kp/128][T][2][64][16]  the same codes in the order the
+ *                          matrix-core kernel reads them, T = ceil(M/16) tiles
+ *                          of 16 tokens: input 8e + 2c + s of word g (inputs
+ *                          32g .. 32g + 31) of 128-input block b, token
+ *                          m = 16t + j, at byte ((b T + t) 2 + s) 1024 +
+ *                          (16 g + j) 16 + 4c + e (token slots past M unused)
  *   d      f32 [M]         dequantization step amax/Qm (Qm = 127 for int8)
  *   amax   f32 [M]         max_k |x[m][k]|
  * With m-bit activations (bitq_quantize_act_bits) q lies in [-Qm, Qm],
@@ -465,7 +466,7 @@ bitq_status bitq_gemv(const bitq_wdesc* desc, const void* w_dev, const void* x_d
  * and on the int8 matrix cores once the contraction is compute-bound.
  *   act_dev activation buffer from bitq_quantize_act(_bits) with this M
  *           (SIGN1: from bitq_binarize_act; HGF: from bitq_quantize_act_hgf).
- * From 4 tokens on, TERNARY, W2A8 and WNAM run on the int8 matrix cores
+ * W2A8 and WNAM (from 2 tokens) and TERNARY (from 3) run on the int8 matrix cores
  * (codes recombined from the planes, exact int32 sums): the integer partials
  * equal those of bitq_gemv, the fp32 outputs agree within the tolerance
  * (another summation order), and a token's output does not depend on the

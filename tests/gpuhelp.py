@@ -57,14 +57,18 @@ def parse_act(buf: np.ndarray, M: int, K: int) -> dict:
     planes = buf[L["off_planes"]:L["off_planes"] + M * Kw * 32].view(np.uint32).reshape(M, Kw, 8)
     S = buf[L["off_S"]:L["off_S"] + M * Kw * 4].view(np.int32).reshape(M, Kw)
     q = buf[L["off_q"]:L["off_q"] + M * Kp].view(np.int8).reshape(M, Kp)
-    qm = buf[L["off_qm"]:L["off_qm"] + M * L["qm_pitch"]].view(np.int8).reshape(M, L["qm_pitch"])[:, :Kp]
+    T = (M + 15) // 16
+    # [b][t][s][g][j][16] -> token m = 16 t + j, block b, word g, half s
+    tiles = buf[L["off_qm"]:L["off_qm"] + 16 * T * Kp].view(np.int8).reshape(Kp // 128, T, 2, 4, 16, 16)
+    qm = tiles.transpose(1, 4, 0, 3, 2, 5).reshape(16 * T, Kp)[:M]
     d = buf[L["off_d"]:L["off_d"] + 4 * M].view(np.float32)
     amax = buf[L["off_amax"]:L["off_amax"] + 4 * M].view(np.float32)
     return dict(planes=planes, S=S, q=q, qm=qm, d=d, amax=amax, Kw=Kw, Kp=Kp)
 
 
 # Byte position of input i of a 32-input word in the activation buffer's qm
-# section (include/bitq.h: input 8j + 2c + s at byte 16s + 4c + j)
+# section, with the word's two 16-byte halves side by side (include/bitq.h:
+# input 8e + 2c + s in half s at byte 4c + e)
 QM_POS = np.array([16 * (i & 1) + 4 * ((i >> 1) & 3) + (i >> 3) for i in range(32)])
 
 

@@ -379,7 +379,7 @@ def test_w2a8_workload(shape_idx, M):
 def test_w2a8_batch_invariance_and_determinism():
     """Run to run, and for a token whatever its place in a batch of the same
     size, the output bits are the same (same kernel, same launch shape).
-    Other batch sizes may run another kernel or launch shape (M = 2 the VALU
+    Other batch sizes may run another kernel or launch shape (M = 1 the VALU
     kernel, 16 and 40 different matrix-core shapes), which add the fp32 group
     terms in another order: there the outputs agree within the tolerance,
     and the exact integer partials agree bit for bit."""
