@@ -107,9 +107,12 @@ __global__ __launch_bounds__(64 * KW) void gemm_mfma_kernel(const uint8_t* __res
     constexpr int NV = S * TT * 4;             // partial outputs per lane
     // the waves' partials; at least kOneWgPerCuLds bytes, so that no CU
     // holds a second workgroup while another CU holds none
-    constexpr int PART = KW * NV * 64;
+    // (rows of 68 floats: the reads of the reduction below, 4 tokens x 16
+    // consecutive rows per wave instruction, then hit 64 distinct banks)
+    constexpr int KST = 68;
+    constexpr int PART = KW * NV * KST;
     __shared__ float s_part_mem[PART * 4 > kOneWgPerCuLds ? PART : kOneWgPerCuLds / 4];
-    float (*s_part)[NV][64] = reinterpret_cast<float (*)[NV][64]>(s_part_mem);
+    float (*s_part)[NV][KST] = reinterpret_cast<float (*)[NV][KST]>(s_part_mem);
 
     // (the wave index through readfirstlane: the compiler then knows it is
     // uniform and keeps the block and tile arithmetic in scalar registers)
@@ -124,6 +127,18 @@ __global__ __launch_bounds__(64 * KW) void gemm_mfma_kernel(const uint8_t* __res
     const int Np = 16 * nsub;
     const int8_t* qm = reinterpret_cast<const int8_t*>(act + act_off_qm);
     const float* ad = reinterpret_cast<const float*>(act + act_off_d);
+    // The step d of this thread's token of each tile in the final reduction
+    // (token 16 tt + (tid / 16) % 16), loaded once instead of once per output
+    // there (a dependent L2 round trip in every iteration).  With one token
+    // tile it is loaded just before the reduction: loaded here, its register
+    // made the first block's loads wait for it (1.05x slower at 4-16
+    // tokens); with more tiles, here (1.02x faster than there at 64 tokens).
+    float dtok[TT];
+    if constexpr (TT > 1) {
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) dtok[tt] = ad[min(16 * tt + ((tid >> 4) & 15), M - 1)];
+    }
+    const float gamma = (FMT == BITQ_TERNARY && !ACC) ? *reinterpret_cast<const float*>(blob + off_c0) : 1.0f;
     const uint32_t* coef = reinterpret_cast<const uint32_t*>(blob + off_c0);
     // q is tiled for these loads (include/bitq.h): the operand of block b,
     // token tile tt and k step s2 is the 1 KB at ((b TT + tt) 2 + s2) 1024,
@@ -343,6 +358,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_mfma_kernel(const uint8_t* __res
         for (; i0 < nbw; ++i0) round(std::integral_constant<int, 1>{}, i0);
 
         if constexpr (!(GRP && ACC)) {
+            if constexpr (TT == 1) dtok[0] = ad[min((tid >> 4) & 15, M - 1)];
             // ---- the waves' partials, added in wave order
 #pragma unroll
             for (int R = 0; R < S; ++R)
@@ -353,11 +369,17 @@ __global__ __launch_bounds__(64 * KW) void gemm_mfma_kernel(const uint8_t* __res
                         s_part[wave][(R * TT + tt) * 4 + i][lane] =
                             GRP ? yacc[R][tt][i] : __int_as_float(acc[R][tt][i]);
             __syncthreads();
-            const float gamma = (FMT == BITQ_TERNARY && !ACC) ? *reinterpret_cast<const float*>(blob + off_c0) : 1.0f;
+            // Output (row n, token m) of the pass is summed over the waves in
+            // wave order.  Thread idx takes n16 = idx % 16 (n = 16 (sb + R) +
+            // n16, held by lane 16 (n16 / 4) + li as element n16 % 4), token
+            // m = 16 tt + li with li = idx / 16 % 16, and the sub-tile and
+            // tile rt = idx / 256: a wave's stores are 4 tokens x 64
+            // contiguous bytes of y.
             for (int idx = tid; idx < NV * 64; idx += 64 * KW) {
-                const int k = idx >> 6, l = idx & 63;
-                const int R = k / (4 * TT), tt = (k / 4) % TT, i = k % 4;
-                const int n = 16 * (sb + R) + 4 * (l >> 4) + i, m = 16 * tt + (l & 15);
+                const int n16 = idx & 15, li2 = (idx >> 4) & 15, rt = idx >> 8;
+                const int R = rt / TT, tt = rt % TT;
+                const int k = 4 * rt + (n16 & 3), l = 16 * (n16 >> 2) + li2;
+                const int n = 16 * (sb + R) + n16, m = 16 * tt + li2;
                 float vf = 0.0f;
                 int vi = 0;
 #pragma unroll
@@ -368,12 +390,16 @@ __global__ __launch_bounds__(64 * KW) void gemm_mfma_kernel(const uint8_t* __res
                         vi += __float_as_int(s_part[w][k][l]);
                 }
                 if (R < ns && n < N && m < M) {
+                    float dm = dtok[0];
+#pragma unroll
+                    for (int t2 = 1; t2 < TT; ++t2)
+                        if (tt == t2) dm = dtok[t2];
                     if (GRP)
-                        y[static_cast<size_t>(m) * N + n] = ad[m] * vf;
+                        y[static_cast<size_t>(m) * N + n] = dm * vf;
                     else if (ACC)
                         reinterpret_cast<int32_t*>(y)[static_cast<size_t>(m) * N + n] = vi;
                     else
-                        y[static_cast<size_t>(m) * N + n] = gamma * ad[m] * static_cast<float>(vi);
+                        y[static_cast<size_t>(m) * N + n] = gamma * dm * static_cast<float>(vi);
                 }
             }
             __syncthreads();
@@ -397,18 +423,13 @@ static void launch_mfma_kw(const bitq_wdesc& d, const BlobLayout& L, const MfmaS
 #define BITQ_MFMA_CASE(KW_, C_) \
     if (sh.KW == KW_ && sh.CH == C_) return launch_mfma_1<FMT, P, ACC, TT, KW_, C_>(d, L, sh, w, act, M, y, st)
     if constexpr (TT == 1) {
-        BITQ_MFMA_CASE(8, 1);
-        BITQ_MFMA_CASE(8, 2);
-        BITQ_MFMA_CASE(8, 3);
         BITQ_MFMA_CASE(16, 1);
-        BITQ_MFMA_CASE(16, 2);
-        BITQ_MFMA_CASE(16, 4);
+        launch_mfma_1<FMT, P, ACC, TT, 16, 2>(d, L, sh, w, act, M, y, st);
     } else {
         BITQ_MFMA_CASE(8, 1);
-        BITQ_MFMA_CASE(8, 2);
+        launch_mfma_1<FMT, P, ACC, TT, 8, 2>(d, L, sh, w, act, M, y, st);
     }
 #undef BITQ_MFMA_CASE
-    launch_mfma_1<FMT, P, ACC, TT, 8, 2>(d, L, sh, w, act, M, y, st);
 }
 
 template <int FMT, int P, bool ACC>
