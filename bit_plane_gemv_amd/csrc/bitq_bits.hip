@@ -57,10 +57,20 @@ __device__ __forceinline__ void nibble_words(uint32_t a, uint32_t b, uint32_t& l
     hi = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
 }
 
+// The waves' partials of row r added in a fixed order (pairs, then pairs of
+// pairs, then the two halves of eight waves).
+template <typename T, int W>
+__device__ __forceinline__ T wave_sum(const T (&s)[W][16], int r) {
+    T v = (s[0][r] + s[1][r]) + (s[2][r] + s[3][r]);
+    if constexpr (W == 8) v += (s[4][r] + s[5][r]) + (s[6][r] + s[7][r]);
+    return v;
+}
+
 // ================================= AND+popcount GEMV, whole k per workgroup
-// No hand-off between workgroups: a workgroup (256 threads) owns RG rows
+// No hand-off between workgroups: a workgroup (NT = 256 threads; 512 for the
+// fused quantizer with 16 rows and a long k range) owns RG rows
 // (16 or 8) and the whole k range.  Thread (g, r) = (tid / RG, tid % RG)
-// takes row r of the group and the k blocks b = g + G j (j < BPL, G = 256/RG
+// takes row r of the group and the k blocks b = g + G j (j < BPL, G = NT/RG
 // k-groups) of each round of G BPL blocks; the RG lanes of a k-group read RG
 // adjacent rows of a tile (16 RG contiguous bytes per load).  Activation
 // planes and group sums of the round are staged once in LDS; the G k-groups'
@@ -91,15 +101,17 @@ __device__ __forceinline__ void nibble_words(uint32_t a, uint32_t b, uint32_t& l
 // Arguments: what the prologue needs comes first (the first 56 bytes arrive
 // preloaded in scalar registers); activation-buffer offsets are 32-bit (the
 // host bounds that buffer far below 4 GB).
-template <int FMT, int P, bool ACC, int BPL, int RG, bool ONE, int XQ = 0>
-__global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __restrict__ blob, size_t off_c0,
+template <int FMT, int P, bool ACC, int BPL, int RG, bool ONE, int XQ = 0, int NT = 256>
+__global__ __launch_bounds__(NT) void gemv_bits_nr_kernel(const uint8_t* __restrict__ blob, size_t off_c0,
                                                            size_t off_c1, const uint8_t* __restrict__ act,
                                                            uint32_t act_off_S, uint32_t act_off_q, int N, int Tb, int M,
                                                            int K, uint32_t act_off_d, int abits, size_t off_c2,
                                                            uint32_t act_off_h, int rank, float* __restrict__ y) {
     constexpr bool TERN = FMT == BITQ_TERNARY || FMT == BITQ_HGF;  // ternary planes
     constexpr bool LORA = FMT == BITQ_HGF && !ACC;                 // the correction epilogue
-    constexpr int G = 256 / RG;    // k-groups: lanes that share a row
+    constexpr int G = NT / RG;     // k-groups: lanes that share a row
+    constexpr int NWV = NT / 64;   // waves
+    static_assert(NT == 256 || (NT == 512 && XQ != 0 && RG == 16), "512 lanes: fused quantizer, 16 rows");
     constexpr int Q = 64 / RG;     // row groups per 64-row tile
     constexpr int NBW = G * BPL;   // k blocks per round
     constexpr int BSTR = 36;       // LDS words per block: 32 + 4 padding, so up to
@@ -108,10 +120,10 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
     // (global_load_lds_dwordx4: lane l of a wave fills the 16-byte slot l of
     // the wave's destination), in whole passes of 256 lanes.  A block takes 9
     // slots: its 8 plane uint4 and one slot of padding.
-    constexpr int SLOT_PASSES = (NBW * 9 + 255) / 256;
-    constexpr int S_PASSES = (NBW + 255) / 256;
-    __shared__ __attribute__((aligned(16))) uint32_t s_act[SLOT_PASSES * 256 * 4];
-    __shared__ __attribute__((aligned(16))) int32_t s_S[S_PASSES * 256 * 4];
+    constexpr int SLOT_PASSES = (NBW * 9 + NT - 1) / NT;
+    constexpr int S_PASSES = (NBW + NT - 1) / NT;
+    __shared__ __attribute__((aligned(16))) uint32_t s_act[SLOT_PASSES * NT * 4];
+    __shared__ __attribute__((aligned(16))) int32_t s_S[S_PASSES * NT * 4];
     __shared__ float4 s_cache[FMT == BITQ_BVSR4 ? 512 : 1];
     // HGF: B^T rows of the group (RG x rank fp16, rank <= 64: RG 8 slots of
     // 16 bytes) and h of the current token (rank floats; the copy fills one
@@ -121,8 +133,8 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
     __shared__ __attribute__((aligned(16))) uint32_t s_lora[FMT == BITQ_HGF ? (RG * 8 + 64) * 4 : 4];
     uint4* const s_bt = reinterpret_cast<uint4*>(s_lora);
     float4* const s_h = reinterpret_cast<float4*>(s_lora + RG * 8 * 4);
-    __shared__ float s_red[4][16];
-    __shared__ int32_t s_redi[4][16];
+    __shared__ float s_red[NWV][16];
+    __shared__ int32_t s_redi[NWV][16];
     constexpr bool FQ = XQ != 0;   // fused activation quantizer
     static_assert(!FQ || (ONE && !ACC && FMT != BITQ_HGF), "fused quantizer: whole k in one round, y output");
 
@@ -150,7 +162,7 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
     uint4 wv[BPL][P];
     uint32_t coef[BPL];
     constexpr bool NIBX = FMT == BITQ_BVSR4;
-    constexpr int XST = NIBX && !FQ ? (NBW * 8 + 255) / 256 : 1;  // q loads per lane and round
+    constexpr int XST = NIBX && !FQ ? (NBW * 8 + NT - 1) / NT : 1;  // q loads per lane and round
     uint4 xs[XST];
     // uniform 64-bit bases of this tile; per-lane offsets fit in 32 bits
     const uint8_t* __restrict__ tile_planes = blob + kHeaderBytes + static_cast<size_t>(t) * Tb * P * 1024;
@@ -187,24 +199,24 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
                                 (static_cast<size_t>(m) * NB + b_base) * 8;  // q [M][Kp]
 #pragma unroll
             for (int v = 0; v < XST; ++v) {
-                const int ch = tid + 256 * v;
+                const int ch = tid + NT * v;
                 xs[v] = qsrc[8 * min(ch >> 3, last) + (ch & 7)];
             }
         } else {
             const uint4* src = reinterpret_cast<const uint4*>(aplanes) + (static_cast<size_t>(m) * Kw + 4 * b_base) * 2;
 #pragma unroll
             for (int v = 0; v < SLOT_PASSES; ++v) {
-                const int slot = tid + 256 * v;
+                const int slot = tid + NT * v;
                 const int blk = slot / 9, part = slot - 9 * blk;
                 __builtin_amdgcn_global_load_lds(src + 8 * min(blk, last) + min(part, 7),
-                                                 reinterpret_cast<uint4*>(s_act) + 256 * v + 64 * wave, 16, 0, 0);
+                                                 reinterpret_cast<uint4*>(s_act) + NT * v + 64 * wave, 16, 0, 0);
             }
         }
         const int4* srcS = reinterpret_cast<const int4*>(aS + static_cast<size_t>(m) * Kw + 4 * b_base);
 #pragma unroll
         for (int v = 0; v < S_PASSES; ++v)
-            __builtin_amdgcn_global_load_lds(srcS + min(tid + 256 * v, last),
-                                             reinterpret_cast<int4*>(s_S) + 256 * v + 64 * wave, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(srcS + min(tid + NT * v, last),
+                                             reinterpret_cast<int4*>(s_S) + NT * v + 64 * wave, 16, 0, 0);
         if (LORA && b_base == 0 && wave_u == 0) {  // h[m]: rank / 4 16-byte slots
             const float4* hsrc = reinterpret_cast<const float4*>(act + act_off_h) + static_cast<size_t>(m) * (rank / 4);
             // (wave_u is 0 here; a destination computed from it, rather than
@@ -219,8 +231,8 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
         if constexpr (NIBX) {
 #pragma unroll
             for (int v = 0; v < XST; ++v) {
-                const int ch = tid + 256 * v;
-                if (XST * 256 == NBW * 8 || ch < NBW * 8) {
+                const int ch = tid + NT * v;
+                if (XST * NT == NBW * 8 || ch < NBW * 8) {
                     const int blk = ch >> 3, w = (ch & 7) >> 1, s0 = 2 * (ch & 1);
                     uint32_t lo0, hi0, lo1, hi1;
                     nibble_words(xs[v].x, xs[v].y, lo0, hi0);
@@ -244,8 +256,9 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
 #pragma unroll
         for (int v = 0; v < 8; ++v) {
             const int slot = tid + 256 * v, e = slot >> 3, f = slot & 7;
-            __builtin_amdgcn_global_load_lds(cache + 5 * e + min(f, 4),
-                                             reinterpret_cast<float*>(s_cache) + 256 * v + 64 * wave, 4, 0, 0);
+            if (NT == 256 || wave_u < 4)  // 2048 4-byte slots: the first four waves
+                __builtin_amdgcn_global_load_lds(cache + 5 * e + min(f, 4),
+                                                 reinterpret_cast<float*>(s_cache) + 256 * v + 64 * wave_u, 4, 0, 0);
         }
     }
     if (LORA && wave_u < RG / 8) {
@@ -257,9 +270,9 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
     }
     // fused quantizer: chunks c = tid + 256 i of 8 inputs (word c / 4, byte
     // c % 4 of its plane words); XLPC 16-byte loads each
-    constexpr int XCPT = FQ ? NBW * 16 / 256 : 1;
+    constexpr int XCPT = FQ ? NBW * 16 / NT : 1;
     constexpr int XLPC = XQ == 2 ? 2 : 1;
-    static_assert(!FQ || (NBW * 16) % 256 == 0, "whole chunks per thread");
+    static_assert(!FQ || (NBW * 16) % NT == 0, "whole chunks per thread");
     uint4 xr[XCPT][XLPC];
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (FQ) {
@@ -271,7 +284,7 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
         const int nch = K / 8;
 #pragma unroll
         for (int i = 0; i < XCPT; ++i) {
-            const int c = min(tid + 256 * i, nch - 1);
+            const int c = min(tid + NT * i, nch - 1);
 #pragma unroll
             for (int l = 0; l < XLPC; ++l) xr[i][l] = global_load16(xaddr, XLPC * c + l);
         }
@@ -285,7 +298,7 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
 
     float dq_fused = 0.0f;  // the token's d (fused quantizer)
     if constexpr (FQ) {
-        __shared__ float s_amax[4];
+        __shared__ float s_amax[NWV];
         // 8 inputs of chunk i as floats (fp32: two 16-byte loads; the index
         // XLPC - 1 keeps the bf16 instantiation, which never takes that
         // branch, inside the array)
@@ -317,6 +330,7 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
         if ((tid & 63) == 0) s_amax[wave] = am;
         barrier_after_loads<kWeightLoads>();
         am = fmaxf(fmaxf(s_amax[0], s_amax[1]), fmaxf(s_amax[2], s_amax[3]));
+        if constexpr (NWV == 8) am = fmaxf(am, fmaxf(fmaxf(s_amax[4], s_amax[5]), fmaxf(s_amax[6], s_amax[7])));
         const float qmax = FMT == BITQ_WNAM ? static_cast<float>((1 << (abits - 1)) - 1) : 127.0f;
         const float sx = am > 0.0f ? __fdiv_rn(qmax, am) : 0.0f;
         dq_fused = am > 0.0f ? __fdiv_rn(am, qmax) : 0.0f;
@@ -332,7 +346,7 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
         const int nch = K / 8;
 #pragma unroll
         for (int i = 0; i < XCPT; ++i) {
-            const int c = tid + 256 * i;
+            const int c = tid + NT * i;
             const float sc = c < nch ? sx : 0.0f;  // chunks past K quantize to 0
             float v[8];
             chunk(i, v);
@@ -590,7 +604,7 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
             __syncthreads();
             if (tid < RG && n < N)
                 reinterpret_cast<int32_t*>(y)[static_cast<size_t>(m) * N + n] =
-                    (s_redi[0][r] + s_redi[1][r]) + (s_redi[2][r] + s_redi[3][r]);
+                    wave_sum(s_redi, r);
         } else {
             float v;
             if (TERN) {
@@ -606,7 +620,7 @@ __global__ __launch_bounds__(256) void gemv_bits_nr_kernel(const uint8_t* __rest
             if ((tid & 63) < RG) s_red[wave][r] = v;
             __syncthreads();
             if (tid < RG && n < N) {
-                float tot = (s_red[0][r] + s_red[1][r]) + (s_red[2][r] + s_red[3][r]);
+                float tot = wave_sum(s_red, r);
                 tot = scale * tot;
                 if (LORA) {  // gate sum_j h_j B[j][n], fp32 in j order
                     float l = 0.0f;
@@ -701,13 +715,13 @@ static void launch_wnam(const bitq_wdesc& d, const Plan& pl, const BlobLayout& L
 // admits K <= kMaxFusedK, so the plan's blocks per lane (at most 4 with 8 rows
 // per workgroup, 8 with 16) keep the whole k range in one round; other
 // combinations are not built and return false.
-template <int FMT, int P, int BPL, int RG, int XQ>
+template <int FMT, int P, int BPL, int RG, int XQ, int NT = 256>
 static void launch_fq_bpl(const bitq_wdesc& d, const BlobLayout& L, const void* w, const void* x, float* y,
                           hipStream_t st) {
     const int tiles = static_cast<int>(L.Tn);
     const int groups = xcd_row_groups(tiles, RG);  // as launch_nr_bpl
     const int abits = d.fmt == BITQ_WNAM ? d.abits : 8;
-    hipLaunchKernelGGL((gemv_bits_nr_kernel<FMT, P, false, BPL, RG, true, XQ>), dim3(groups), dim3(256), 0, st,
+    hipLaunchKernelGGL((gemv_bits_nr_kernel<FMT, P, false, BPL, RG, true, XQ, NT>), dim3(groups), dim3(NT), 0, st,
                        static_cast<const uint8_t*>(w), L.off_c0, L.off_c1, static_cast<const uint8_t*>(x), 0u, 0u, d.N,
                        static_cast<int>(L.Tb), 1, d.K, 0u, abits, L.off_c2, 0u, 0, y);
 }
@@ -715,8 +729,24 @@ static void launch_fq_bpl(const bitq_wdesc& d, const BlobLayout& L, const void* 
 template <int FMT, int P, int RG, int XQ>
 static bool launch_fq_rg(const bitq_wdesc& d, const Plan& pl, const BlobLayout& L, const void* w, const void* x,
                          float* y, hipStream_t st) {
-    if (L.Tb > static_cast<size_t>(256 / RG) * pl.blocks_per_split) return false;  // not one round
     constexpr bool wnam = FMT == BITQ_WNAM;
+    if constexpr (RG == 16) {
+        if (pl.waves_per_wg == 8) {  // 512 lanes, 2 to 4 blocks per lane
+            if (L.Tb > static_cast<size_t>(512 / RG) * pl.blocks_per_split) return false;
+            switch (pl.blocks_per_split) {
+                case 2: launch_fq_bpl<FMT, P, 2, RG, XQ, 512>(d, L, w, x, y, st); return true;
+                case 3:
+                    if constexpr (!wnam) {
+                        launch_fq_bpl<FMT, P, 3, RG, XQ, 512>(d, L, w, x, y, st);
+                        return true;
+                    }
+                    return false;
+                case 4: launch_fq_bpl<FMT, P, 4, RG, XQ, 512>(d, L, w, x, y, st); return true;
+                default: return false;
+            }
+        }
+    }
+    if (L.Tb > static_cast<size_t>(256 / RG) * pl.blocks_per_split) return false;  // not one round
     switch (pl.blocks_per_split) {
         case 1: launch_fq_bpl<FMT, P, 1, RG, XQ>(d, L, w, x, y, st); return true;
         case 2: launch_fq_bpl<FMT, P, 2, RG, XQ>(d, L, w, x, y, st); return true;

@@ -800,7 +800,8 @@ Plan make_plan(const bitq_wdesc& d, int M, bool fused) {
         // 6.5 us at 11008x4096).
         const bool wnam = d.fmt == BITQ_WNAM;
         const int rg = fused ? (d.N >= 4096 ? 16 : 8) : (d.N >= 16384 && !wnam ? 16 : 8);
-        const int64_t kgroups = 256 / rg;
+        p.waves_per_wg = fused && rg == 16 && NB > kFusedWideMinBlocks ? 8 : 4;
+        const int64_t kgroups = 64 * p.waves_per_wg / rg;
         const int64_t need = (NB + kgroups - 1) / kgroups;
         const int sizes[6] = {1, 2, 3, 4, 6, 8};
         p.blocks_per_split = 8;
@@ -809,7 +810,6 @@ Plan make_plan(const bitq_wdesc& d, int M, bool fused) {
                 p.blocks_per_split = sz;
                 break;
             }
-        p.waves_per_wg = 4;
         p.rows_per_wg = rg;
         p.row_groups = static_cast<int>((d.N + rg - 1) / rg);
         p.splits = 1;
@@ -877,6 +877,7 @@ LaunchShape launch_shape(const bitq_wdesc& d, int M, int x_dtype, uint32_t flags
         ls.block = m.block;
     } else {
         ls.grid = xcd_row_groups(tiles, p.rows_per_wg);
+        ls.block = 64 * p.waves_per_wg;
     }
     return ls;
 }

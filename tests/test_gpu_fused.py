@@ -85,13 +85,17 @@ def _x(K, seed, dt):
 
 
 def _same_order(desc):
-    """Both kernels use the same rows per workgroup (so the same fp32
-    summation order), or the sums are exact integers (ternary)."""
+    """Both kernels use the same workgroup shape (so the same fp32 summation
+    order), or the sums are exact integers (ternary).  The fused kernel takes
+    16 rows per workgroup from 4096 rows on, with 8 waves (32 k-groups) when
+    K > 6144; the plain kernel has 4 waves and 8 rows below 16384 rows."""
     if desc.fmt == bq.TERNARY:
         return True
     fused_rg = 16 if desc.N >= 4096 else 8
     plain_rg = 16 if desc.N >= 16384 and desc.fmt != bq.WNAM else 8
-    return fused_rg == plain_rg
+    if fused_rg != plain_rg:
+        return False
+    return fused_rg == 8 or (desc.K + 127) // 128 <= 48
 
 
 def _check(desc, bd, ref, xs, xf, rows=None):
