@@ -111,7 +111,8 @@ __global__ __launch_bounds__(NT) void gemv_bits_nr_kernel(const uint8_t* __restr
     constexpr bool LORA = FMT == BITQ_HGF && !ACC;                 // the correction epilogue
     constexpr int G = NT / RG;     // k-groups: lanes that share a row
     constexpr int NWV = NT / 64;   // waves
-    static_assert(NT == 256 || (NT == 512 && XQ != 0 && RG == 16), "512 lanes: fused quantizer, 16 rows");
+    static_assert(NT == 256 || (NT == 512 && RG == 16 && (XQ != 0 || FMT == BITQ_BVSR4)),
+                  "512 lanes: 16 rows, fused quantizer or BVSR4");
     constexpr int Q = 64 / RG;     // row groups per 64-row tile
     constexpr int NBW = G * BPL;   // k blocks per round
     constexpr int BSTR = 36;       // LDS words per block: 32 + 4 padding, so up to
@@ -648,7 +649,7 @@ __global__ __launch_bounds__(NT) void gemv_bits_nr_kernel(const uint8_t* __restr
         for (int m = 1; m < M; ++m) pass(m, false);
 }
 
-template <int FMT, int P, bool ACC, int BPL, int RG>
+template <int FMT, int P, bool ACC, int BPL, int RG, int NT = 256>
 static void launch_nr_bpl(const bitq_wdesc& d, const BlobLayout& L, const void* w, const void* act, int M,
                           float* y, hipStream_t st) {
     ActLayout A = act_layout(M, d.K, d.rank);
@@ -656,10 +657,11 @@ static void launch_nr_bpl(const bitq_wdesc& d, const BlobLayout& L, const void* 
     // the grid is padded to whole rounds of 8 tiles (extra workgroups exit)
     const int tiles = static_cast<int>(L.Tn);
     const int groups = xcd_row_groups(tiles, RG);
-    const bool one = L.Tb <= (256 / RG) * BPL;  // the whole k range in one round
-    auto kern = one ? gemv_bits_nr_kernel<FMT, P, ACC, BPL, RG, true> : gemv_bits_nr_kernel<FMT, P, ACC, BPL, RG, false>;
+    const bool one = L.Tb <= (NT / RG) * BPL;  // the whole k range in one round
+    auto kern = one ? gemv_bits_nr_kernel<FMT, P, ACC, BPL, RG, true, 0, NT>
+                    : gemv_bits_nr_kernel<FMT, P, ACC, BPL, RG, false, 0, NT>;
     const int abits = d.fmt == BITQ_WNAM ? d.abits : 8;
-    hipLaunchKernelGGL(kern, dim3(groups), dim3(256), 0, st, static_cast<const uint8_t*>(w), L.off_c0, L.off_c1,
+    hipLaunchKernelGGL(kern, dim3(groups), dim3(NT), 0, st, static_cast<const uint8_t*>(w), L.off_c0, L.off_c1,
                        static_cast<const uint8_t*>(act), static_cast<uint32_t>(A.off_S), static_cast<uint32_t>(A.off_q),
                        d.N, static_cast<int>(L.Tb), M, d.K, static_cast<uint32_t>(A.off_d), abits, L.off_c2,
                        static_cast<uint32_t>(A.off_h), d.rank, y);
@@ -676,6 +678,16 @@ static void launch_nr_rg(const bitq_wdesc& d, const Plan& pl, const BlobLayout& 
             default: launch_nr_bpl<FMT, P, ACC, 8, RG>(d, L, w, act, M, y, st); break;
         }
     } else {
+        if constexpr (FMT == BITQ_BVSR4 && RG == 16) {
+            if (pl.waves_per_wg == 8) {  // 512 lanes, one round: 2 to 4 blocks per lane
+                switch (pl.blocks_per_split) {
+                    case 2: launch_nr_bpl<FMT, P, ACC, 2, RG, 512>(d, L, w, act, M, y, st); return;
+                    case 3: launch_nr_bpl<FMT, P, ACC, 3, RG, 512>(d, L, w, act, M, y, st); return;
+                    case 4: launch_nr_bpl<FMT, P, ACC, 4, RG, 512>(d, L, w, act, M, y, st); return;
+                    default: break;
+                }
+            }
+        }
         switch (pl.blocks_per_split) {  // blocks per lane
             case 1: launch_nr_bpl<FMT, P, ACC, 1, RG>(d, L, w, act, M, y, st); break;
             case 2: launch_nr_bpl<FMT, P, ACC, 2, RG>(d, L, w, act, M, y, st); break;

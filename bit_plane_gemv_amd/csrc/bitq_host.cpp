@@ -800,7 +800,9 @@ Plan make_plan(const bitq_wdesc& d, int M, bool fused) {
         // 6.5 us at 11008x4096).
         const bool wnam = d.fmt == BITQ_WNAM;
         const int rg = fused ? (d.N >= 4096 ? 16 : 8) : (d.N >= 16384 && !wnam ? 16 : 8);
-        p.waves_per_wg = fused && rg == 16 && NB > kFusedWideMinBlocks ? 8 : 4;
+        const bool wide = rg == 16 && NB > kWideMinBlocks &&
+                          (fused || (d.fmt == BITQ_BVSR4 && M == 1 && NB <= 4 * 32));  // BVSR4: one round
+        p.waves_per_wg = wide ? 8 : 4;
         const int64_t kgroups = 64 * p.waves_per_wg / rg;
         const int64_t need = (NB + kgroups - 1) / kgroups;
         const int sizes[6] = {1, 2, 3, 4, 6, 8};

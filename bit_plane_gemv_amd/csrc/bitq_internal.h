@@ -74,13 +74,15 @@ struct Plan {
     bool mfma;             // TERNARY/W2A8/WNAM, M >= mfma_min_tokens: the int8 matrix-core kernel
 };
 Plan make_plan(const bitq_wdesc& d, int M, bool fused = false);  // fused: BITQ_F_FUSE_QUANT
-// The fused-quantizer GEMV with 16 rows per workgroup takes 8 waves (32
-// k-groups) instead of 4 when the k range has more than this many 128-input
-// blocks: then 4 waves would leave 4 or more blocks per lane.  Measured
-// (one launch per step): W2A8 4096x11008 6.96 -> 6.57 us, BVSR 28672x8192
-// 27.95 -> 27.58 us; with 4096 inputs 8 waves are slower (W2A8 11008x4096
-// 5.67 -> 5.95 us, ternary 4096x4096 3.65 -> 3.92 us).
-constexpr int kFusedWideMinBlocks = 48;
+// The fused-quantizer GEMV with 16 rows per workgroup, and the BVSR4 GEMV
+// of one token with 16 rows, take 8 waves (32 k-groups) instead of 4 when
+// the k range has more than this many 128-input blocks: then 4 waves would
+// leave 4 or more blocks per lane.  Measured: fused W2A8 4096x11008 6.96 ->
+// 6.57 us, fused BVSR 28672x8192 27.95 -> 27.58 us, BVSR 28672x8192
+// 26.33 -> 25.75 us; slower with 4096 inputs (fused W2A8 11008x4096 5.67 ->
+// 5.95 us, fused ternary 4096x4096 3.65 -> 3.92 us) and for the other
+// formats' two-launch GEMVs (W2A8 4096x11008 5.02 -> 5.43 us).
+constexpr int kWideMinBlocks = 48;
 
 // Launch shape of the matrix-core kernel for M tokens: TT token tiles of 16,
 // RS = kMfmaSubs sub-tiles of 16 rows per pass of a workgroup, KW waves over
