@@ -67,9 +67,9 @@ METRIC = "packed-weight GB/s & % HBM peak, bit-plane GEMV 11008x4096 M=1; us/lay
 MEASURED_TRAFFIC: dict = {
     "rabit": {"source": "bitq_sign.hip", "sha16": "ba906aeaa6be2c6a", "build_sha16": "75709457503c2a5c",
               "bytes_per_launch": 13458432, "profile": "profiles/gemv_sign_kernel_rabit_11008x4096.md"},
-    "w2a8": {"source": "bitq_bits.hip", "sha16": "c9e8c116f6633db6", "build_sha16": "75709457503c2a5c",
+    "w2a8": {"source": "bitq_bits.hip", "sha16": "241574416dea4db5", "build_sha16": "75709457503c2a5c",
              "bytes_per_launch": 12822528, "profile": "profiles/gemv_bits_nr_kernel_w2a8_11008x4096.md"},
-    "w2a8+fuse": {"source": "bitq_bits.hip", "sha16": "c9e8c116f6633db6", "build_sha16": "75709457503c2a5c",
+    "w2a8+fuse": {"source": "bitq_bits.hip", "sha16": "241574416dea4db5", "build_sha16": "75709457503c2a5c",
                   "bytes_per_launch": 12880896, "profile": "profiles/gemv_bits_nr_kernel_fused_w2a8_11008x4096.md"},
 }
 BUILD_SCRIPT = os.path.join(ROOT, "bit_plane_gemv_amd", "build.py")
