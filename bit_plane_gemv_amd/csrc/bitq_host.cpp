@@ -850,7 +850,9 @@ MfmaShape mfma_shape(const bitq_wdesc& d, int M) {
     // 2 blocks as possible, evenly filled.
     MfmaShape s{};
     s.TT = std::min(4, (M + 15) / 16);
-    s.RS = kMfmaSubs;
+    // sub-tiles per pass: one when every workgroup owns at most one (up to
+    // 4096 rows), so that no surplus slot repeats the products of the last
+    s.RS = round_up(d.N, kRowTile) / 16 <= kWholeRowGrid ? 1 : kMfmaSubs;
     const int64_t NB = round_up(d.K, kKBlock) / kKBlock;
     const int64_t nsub = round_up(d.N, kRowTile) / 16;
     s.KW = s.TT == 1 ? 16 : 8;

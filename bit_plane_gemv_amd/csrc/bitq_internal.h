@@ -85,7 +85,8 @@ Plan make_plan(const bitq_wdesc& d, int M, bool fused = false);  // fused: BITQ_
 constexpr int kWideMinBlocks = 48;
 
 // Launch shape of the matrix-core kernel for M tokens: TT token tiles of 16,
-// RS = kMfmaSubs sub-tiles of 16 rows per pass of a workgroup, KW waves over
+// RS = kMfmaSubs (or 1, when the sub-tiles do not outnumber the workgroups)
+// sub-tiles of 16 rows per pass of a workgroup, KW waves over
 // k, CH k blocks whose loads a wave issues together; grid = one workgroup
 // per CU (at most one per sub-tile), of 64 KW lanes.
 constexpr int kMfmaSubs = 3;

@@ -95,12 +95,12 @@ struct MfmaBlock {
     uint4 cz[LOADC ? S : 1];    // coefficient words of rows 4 g .. 4 g + 3 (their delta)
 };
 
-template <int FMT, int P, bool ACC, int TT, int KW, int C>
+template <int FMT, int P, bool ACC, int TT, int KW, int C, int S>
 __global__ __launch_bounds__(64 * KW) void gemm_mfma_kernel(const uint8_t* __restrict__ blob, size_t off_c0,
                                                             const uint8_t* __restrict__ act, size_t act_off_qm,
                                                             size_t act_off_d, int M, int N, int Tb, int nsub,
                                                             float* __restrict__ y) {
-    constexpr int S = kMfmaSubs;
+    static_assert(S == 1 || S == kMfmaSubs, "sub-tiles per pass");
     constexpr bool GRP = FMT != BITQ_TERNARY;  // per-128-group epilogue (W2A8, WNAM)
     constexpr bool LOADC = GRP && !ACC;        // coefficients needed (fold + delta)
     constexpr bool PERM = FMT == BITQ_TERNARY || (LOADC && P <= 3);  // codes through a byte table
@@ -411,7 +411,10 @@ template <int FMT, int P, bool ACC, int TT, int KW, int C>
 static void launch_mfma_1(const bitq_wdesc& d, const BlobLayout& L, const MfmaShape& sh, const void* w,
                           const void* act, int M, float* y, hipStream_t st) {
     ActLayout A = act_layout(M, d.K, d.rank);
-    hipLaunchKernelGGL((gemm_mfma_kernel<FMT, P, ACC, TT, KW, C>), dim3(sh.grid), dim3(64 * KW), 0, st,
+    // one sub-tile per workgroup when the sub-tiles do not outnumber the CUs
+    // (up to 4096 rows): no surplus slots
+    auto kern = sh.RS == 1 ? gemm_mfma_kernel<FMT, P, ACC, TT, KW, C, 1> : gemm_mfma_kernel<FMT, P, ACC, TT, KW, C, kMfmaSubs>;
+    hipLaunchKernelGGL(kern, dim3(sh.grid), dim3(64 * KW), 0, st,
                        static_cast<const uint8_t*>(w), L.off_c0, static_cast<const uint8_t*>(act), A.off_qm, A.off_d,
                        M, d.N, static_cast<int>(L.Tb), static_cast<int>(L.Np / 16), y);
 }
