@@ -125,13 +125,15 @@ struct ActOut {
 
 // PRE: amax comes from act_amax_kernel (out.amax, written by the previous
 // launch on the stream) and the workgroup reads only its own 256 inputs.
-template <int DT, int RANK, bool PRE>
+template <int DT, int RANK, bool PRE, int HOLD = 4>
 __global__ __launch_bounds__(256) void quant_act_kernel(const void* __restrict__ x, int K, int Kw, float qmax,
                                                         ActOut out, const uint8_t* __restrict__ blob, size_t off_at,
                                                         int Kp, unsigned long long* __restrict__ ws) {
     static_assert(!(PRE && RANK > 0), "the HGF activation step has K <= 16128: one pass");
     constexpr int VEC = (DT == BITQ_DT_F32) ? 4 : 8;  // inputs per 16-byte load
-    constexpr int HOLD = 4;                            // 16-byte loads kept per thread
+    // HOLD: 16-byte loads per thread in flight together in the one-pass amax
+    // (8 for rows of more than 1024 of them: the whole row in one batch
+    // instead of a batch of 4 and a loop of dependent loads)
     __shared__ float s_red[4];
     __shared__ float s_slice[256];                     // this workgroup's 256 inputs
     const int m = blockIdx.y;
@@ -341,12 +343,23 @@ static ActOut act_out(void* act, const ActLayout& A) {
     return o;
 }
 
+// Workgroups from which the amax of each token is taken by a launch of its
+// own (one read of the row) rather than by every workgroup of the token:
+// 64 tokens x 11008 inputs (2752 workgroups) 25.8 -> 23.9 us per W2A8
+// 4096x11008 step; with 64 x 4096 (1024 workgroups) the extra launch costs
+// more than the repeated reads save (14.7 -> 16.9 us).
+constexpr int64_t kAmaxPassMinWorkgroups = 2048;
+
 template <int DT>
 static void launch_quant_plain(const void* x, int M, int K, int Kw, float qmax, const ActOut& o, hipStream_t st) {
     const dim3 grid((Kw + 7) / 8, M);
-    if (K > kAmaxOnePassK) {
+    if (K > kAmaxOnePassK || static_cast<int64_t>(grid.x) * M >= kAmaxPassMinWorkgroups) {
         hipLaunchKernelGGL((act_amax_kernel<DT>), dim3(M), dim3(1024), 0, st, x, K, o.amax);
         hipLaunchKernelGGL((quant_act_kernel<DT, 0, true>), grid, dim3(256), 0, st, x, K, Kw, qmax, o,
+                           static_cast<const uint8_t*>(nullptr), static_cast<size_t>(0), 0,
+                           static_cast<unsigned long long*>(nullptr));
+    } else if (K / (DT == BITQ_DT_F32 ? 4 : 8) > 1024) {
+        hipLaunchKernelGGL((quant_act_kernel<DT, 0, false, 8>), grid, dim3(256), 0, st, x, K, Kw, qmax, o,
                            static_cast<const uint8_t*>(nullptr), static_cast<size_t>(0), 0,
                            static_cast<unsigned long long*>(nullptr));
     } else {
